@@ -1,0 +1,190 @@
+"""Throughput of the draft-tree verification step on one MI355X.
+
+A step is one pass of the whole path over one batch: gdntree_build -> gdntree_verify ->
+gdntree_accept_commit.  The default workload is the large ragged batch: 32 requests x one
+GDN layer (32 heads, d = 128), 16-position x top-16 lattices, N = 64 draft nodes per
+request, bf16 rows, fp32 state.  The synthetic target argmax (the stand-in for the target
+model's LM head) is resolved once per input set, untimed, from the deterministic tree.
+
+Honest HBM numbers: the timed steps rotate through several independent input sets (more
+than the 256 MB last-level cache), so each step reads its rows and states from HBM.
+
+Prints ONE JSON line.  value = verified (node, layer) pairs per second over whole steps.
+roofline: the verify kernel (the dominant one), algorithmic bytes per launch / the mean of
+its HIP-event durations over the timed steps.  cpu_baseline: the fp64 oracle on a bounded
+sample of the same workload, on the host.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload ragged]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def verify_bytes(cfg, n_nodes_total: int, out_elem: int) -> int:
+    """Algorithmic HBM bytes of one verify launch: the fp32 state of every (layer, request,
+    head) once, plus q, k, v, alpha, beta read and o written once per used row."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    per_row = 3 * cfg.D * e + 2 * e + cfg.D * out_elem
+    return cfg.L * cfg.H * (cfg.B * 4 * cfg.D * cfg.D + n_nodes_total * per_row)
+
+
+def commit_bytes(cfg, tau_total: int) -> int:
+    e = 2 if cfg.dtype == "bf16" else 4
+    return cfg.L * cfg.H * (cfg.B * 8 * cfg.D * cfg.D + tau_total * (2 * cfg.D * e + 2 * e))
+
+
+def cpu_baseline(name: str, reqs: int) -> dict:
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import generate, resolve_target
+    w = generate(name, seed=0, B=reqs)
+    cfg = w.cfg
+
+    def target_fn(tree):
+        return resolve_target(tree["depth"], tree["n_nodes"], w.lat_tok, w.tgt_choice, w.tgt_uniform)
+
+    args = (w.lat_logp, w.lat_tok, w.root_tok, cfg.N, w.f64("q"), w.f64("k"), w.f64("v"),
+            w.f64("alpha"), w.f64("beta"), w.h0.double().numpy())
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        r = oracle.pipeline(*args, target_fn)
+        dt = time.perf_counter() - t0
+    nodes = int(np.asarray(r["tree"]["n_nodes"]).sum()) * cfg.L
+    return {"value": nodes / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
+            "sample": f"{name} workload (seed 0), its first {reqs} requests: the full "
+                      f"build+verify+accept+commit pipeline in fp64 numpy, {dt:.1f} s, "
+                      f"BLAS limited to 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ragged")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated through (0: auto)")
+    ap.add_argument("--cpu-reqs", type=int, default=12)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
+              "multi-GPU mode (the verify step shards by request or head with no exchange).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gdn_draft_tree_amd as g
+    from workloads import CONFIGS, generate, resolve_target
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    e = 2 if cfg.dtype == "bf16" else 4
+    set_bytes = (5 * cfg.L * cfg.B * cfg.rows * cfg.H * cfg.D * e + cfg.L * cfg.B * cfg.H * cfg.D * cfg.D * 4)
+    nsets = args.sets or max(2, int(np.ceil(600e6 / set_bytes)))
+
+    sets = []
+    for s in range(nsets):
+        w = generate(cfg, seed=s)
+        d = dict(lat_logp=torch.from_numpy(w.lat_logp).to(dev), lat_tok=torch.from_numpy(w.lat_tok).to(dev),
+                 root_tok=torch.from_numpy(w.root_tok).to(dev), q=w.q.to(dev), k=w.k.to(dev), v=w.v.to(dev),
+                 alpha=w.alpha.to(dev), beta=w.beta.to(dev), state=g.state_from_math(w.h0).to(dev))
+        d["tree"] = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N)
+        torch.cuda.synchronize()
+        tgt = resolve_target(d["tree"].depth.cpu().numpy(), d["tree"].n_nodes.cpu().numpy(), w.lat_tok,
+                             w.tgt_choice, w.tgt_uniform)
+        d["target"] = torch.from_numpy(tgt).to(dev)
+        d["o"] = torch.empty(cfg.L, cfg.B, cfg.rows, cfg.H, cfg.D, dtype=w.q.dtype, device=dev)
+        d["acc"] = (torch.empty(cfg.B, dtype=torch.int32, device=dev),
+                    torch.empty(cfg.B, cfg.P + 1, dtype=torch.int32, device=dev),
+                    torch.empty(cfg.B, cfg.P + 1, dtype=torch.int32, device=dev))
+        sets.append(d)
+        del w
+    print(f"# {nsets} input sets of {set_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i, events=None):
+        d = sets[i % nsets]
+        if events:
+            events[0].record(stream)
+        g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N, out=d["tree"], stream=stream)
+        if events:
+            events[1].record(stream)
+        g.gdntree_verify(d["tree"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o=d["o"],
+                         stream=stream)
+        if events:
+            events[2].record(stream)
+        g.gdntree_accept_commit(d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"],
+                                cfg.P, acc=d["acc"], stream=stream)
+        if events:
+            events[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # whole-step throughput (no events inside the timed region)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-kernel durations with HIP events on the launch stream
+    for i in range(args.steps):
+        step(args.warmup + i, ev[i])
+    torch.cuda.synchronize()
+    t_build = float(np.mean([a.elapsed_time(b) for a, b, _, _ in ev])) * 1e3
+    t_verify = float(np.mean([b.elapsed_time(c) for _, b, c, _ in ev])) * 1e3
+    t_commit = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in ev])) * 1e3
+
+    n_nodes = [int(d["tree"].n_nodes.sum()) for d in sets]
+    taus = [int(d["acc"][0].sum()) for d in sets]
+    nodes_per_step = float(np.mean(n_nodes)) * cfg.L
+    ms = elapsed / args.steps * 1e3
+    vbytes = float(np.mean([verify_bytes(cfg, n, e) for n in n_nodes]))
+    cbytes = float(np.mean([commit_bytes(cfg, t) for t in taus]))
+    achieved = vbytes / (t_verify * 1e-6) / 1e9
+
+    out = {
+        "metric": "GDN tree-verify nodes/s per layer", "value": nodes_per_step / (ms * 1e-3),
+        "unit": "nodes/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.notes}", "B": cfg.B, "L": cfg.L, "H": cfg.H, "d": cfg.D,
+                   "P": cfg.P, "K": cfg.K, "N": cfg.N, "io_dtype": cfg.dtype, "input_sets": nsets},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "verify_kernel",
+                     "algorithmic_bytes": vbytes, "mean_us": t_verify},
+        "kernels_us": {"build": t_build, "verify": t_verify, "accept_commit": t_commit},
+        "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
+        "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),
+        "tau_mean": float(np.mean(taus)) / cfg.B,
+        "precision": "bf16 rows and outputs; fp32 state, gates and accumulation (S0 and the "
+                     "effective queries split hi+lo bf16 on MFMA); fp64 tree scores",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_reqs, cfg.B))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""Thin ctypes binding over libgdntree.so, with the C ABI's names.
+
+Only argument marshalling happens here: shape/dtype/device checks and pointer extraction
+from torch tensors (torch provides device memory and the current stream).  Every step of
+the verified path runs in the library's HIP kernels; there is no fallback.  If the shared
+library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdntree.so")
+
+GDNTREE_OK, GDNTREE_ERR_ARG, GDNTREE_ERR_UNSUPPORTED, GDNTREE_ERR_DEVICE = 0, 1, 2, 3
+GDNTREE_F32, GDNTREE_BF16 = 0, 1
+EXPORTED = ("gdntree_build", "gdntree_verify", "gdntree_accept_commit", "gdntree_status_str")
+
+
+class GdnTreeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"gdntree status {status}: {message}")
+        self.status = status
+
+
+class CTree(ctypes.Structure):
+    _fields_ = [("parent", ctypes.c_void_p), ("depth", ctypes.c_void_p), ("rank", ctypes.c_void_p),
+                ("token", ctypes.c_void_p), ("score", ctypes.c_void_p), ("anc", ctypes.c_void_p),
+                ("n_nodes", ctypes.c_void_p)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gdn_draft_tree_amd.build_lib`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.gdntree_build.argtypes = [vp, vp, vp, i, i, i, i, CTree, vp]
+    lib.gdntree_build.restype = i
+    lib.gdntree_verify.argtypes = [CTree, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, i, vp, vp]
+    lib.gdntree_verify.restype = i
+    lib.gdntree_accept_commit.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp,
+                                          vp, vp, vp, vp]
+    lib.gdntree_accept_commit.restype = i
+    lib.gdntree_status_str.argtypes = [i]
+    lib.gdntree_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def gdntree_status_str(status: int) -> str:
+    return LIB.gdntree_status_str(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != GDNTREE_OK:
+        raise GdnTreeError(status, gdntree_status_str(status))
+
+
+@dataclass
+class Tree:
+    """Device tensors of a batch of best-first trees ([B][N+1] each, n_nodes [B])."""
+    parent: torch.Tensor
+    depth: torch.Tensor
+    rank: torch.Tensor
+    token: torch.Tensor
+    score: torch.Tensor
+    anc: torch.Tensor
+    n_nodes: torch.Tensor
+
+    @staticmethod
+    def empty(B: int, N: int, device) -> "Tree":
+        i32 = dict(dtype=torch.int32, device=device)
+        return Tree(parent=torch.empty(B, N + 1, **i32), depth=torch.empty(B, N + 1, **i32),
+                    rank=torch.empty(B, N + 1, **i32), token=torch.empty(B, N + 1, **i32),
+                    score=torch.empty(B, N + 1, dtype=torch.float64, device=device),
+                    anc=torch.empty(B, N + 1, dtype=torch.int64, device=device),
+                    n_nodes=torch.empty(B, **i32))
+
+    @property
+    def B(self) -> int:
+        return self.parent.shape[0]
+
+    @property
+    def N(self) -> int:
+        return self.parent.shape[1] - 1
+
+    def c(self) -> CTree:
+        for name in ("parent", "depth", "rank", "token", "score", "anc", "n_nodes"):
+            t = getattr(self, name)
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"tree.{name} must be a contiguous device tensor")
+        return CTree(self.parent.data_ptr(), self.depth.data_ptr(), self.rank.data_ptr(),
+                     self.token.data_ptr(), self.score.data_ptr(), self.anc.data_ptr(),
+                     self.n_nodes.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return GDNTREE_BF16
+    if dtype == torch.float32:
+        return GDNTREE_F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def gdntree_build(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch.Tensor, N: int,
+                  out: Tree | None = None, stream=None) -> Tree:
+    """Best-first tree from a [B][P][K] lattice (sorted along K); see gdntree.h."""
+    B, P, K = lat_logp.shape
+    out = out if out is not None else Tree.empty(B, N, lat_logp.device)
+    args = (_dev(lat_logp, "lat_logp", torch.float32, (B, P, K)),
+            _dev(lat_tok, "lat_tok", torch.int32, (B, P, K)),
+            _dev(root_tok, "root_tok", torch.int32, (B,)))
+    if out.B != B or out.N != N:
+        raise ValueError("output tree has the wrong shape")
+    _check(LIB.gdntree_build(*args, B, P, K, N, out.c(), _stream(stream)))
+    return out
+
+
+def gdntree_verify(tree: Tree, q, k, v, alpha, beta, state, o=None, out_dtype=None, stream=None):
+    """Per-node GDN outputs o [L][B][N+1][H][d_v] for every tree slot < n_nodes.
+
+    q, k, v: [L][B][N+1][H][d]; alpha, beta: [L][B][N+1][H] (bf16 or fp32, all the same);
+    state: fp32 [L][B][H][d_v][d_k] (the transpose of the d_k x d_v state), read only.
+    """
+    L, B, R, H, D = q.shape
+    dt = q.dtype
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty(L, B, R, H, D, dtype=out_dtype, device=q.device)
+    ptrs = [_dev(x, nm, dt, (L, B, R, H, D)) for x, nm in ((q, "q"), (k, "k"), (v, "v"))]
+    ptrs += [_dev(x, nm, dt, (L, B, R, H)) for x, nm in ((alpha, "alpha"), (beta, "beta"))]
+    sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
+    op = _dev(o, "o", out_dtype, (L, B, R, H, D))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match the rows")
+    _check(LIB.gdntree_verify(tree.c(), B, R - 1, L, H, D, D, _code(dt), *ptrs, sp,
+                              _code(out_dtype), op, _stream(stream)))
+    return o
+
+
+def gdntree_accept_commit(tree: Tree, target_argmax, k, v, alpha, beta, state, P: int,
+                          acc=None, stream=None):
+    """Greedy acceptance + bonus and in-place commit of the accepted-path state.
+
+    Returns (acc_len [B], acc_tok [B][P+1], acc_node [B][P+1]) int32 device tensors.
+    """
+    L, B, R, H, D = k.shape
+    dt = k.dtype
+    if acc is None:
+        acc = (torch.empty(B, dtype=torch.int32, device=k.device),
+               torch.empty(B, P + 1, dtype=torch.int32, device=k.device),
+               torch.empty(B, P + 1, dtype=torch.int32, device=k.device))
+    acc_len, acc_tok, acc_node = acc
+    tp = _dev(target_argmax, "target_argmax", torch.int32, (B, R))
+    ptrs = [_dev(x, nm, dt, (L, B, R, H, D)) for x, nm in ((k, "k"), (v, "v"))]
+    ptrs += [_dev(x, nm, dt, (L, B, R, H)) for x, nm in ((alpha, "alpha"), (beta, "beta"))]
+    sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
+    ap = (_dev(acc_len, "acc_len", torch.int32, (B,)),
+          _dev(acc_tok, "acc_tok", torch.int32, (B, P + 1)),
+          _dev(acc_node, "acc_node", torch.int32, (B, P + 1)))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match the rows")
+    _check(LIB.gdntree_accept_commit(tree.c(), B, R - 1, P, tp, L, H, D, D, _code(dt), *ptrs, sp,
+                                     *ap, _stream(stream)))
+    return acc_len, acc_tok, acc_node

@@ -1,0 +1,109 @@
+// C-ABI entry points: host-side argument validation, then the kernel launches.
+// No allocation, no synchronisation, no exceptions across the boundary.
+
+#include <hip/hip_runtime.h>
+
+#include "gdntree_internal.h"
+
+#define GDNTREE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace gdntree;
+
+bool dtype_ok(int d) { return d == GDNTREE_F32 || d == GDNTREE_BF16; }
+
+gdntree_status device_ok() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return GDNTREE_ERR_DEVICE;
+  }
+  return GDNTREE_OK;
+}
+
+gdntree_status head_dims(int dk, int dv) {
+  if (dk <= 0 || dv <= 0) return GDNTREE_ERR_ARG;
+  if (dk != dv || (dk != 64 && dk != 128)) return GDNTREE_ERR_UNSUPPORTED;
+  return GDNTREE_OK;
+}
+
+// Grid dimensions must fit in 32 bits: (layers * requests * heads) workgroup units.
+bool grid_fits(long long units) { return units > 0 && units * 4 < 0x7fffffffLL; }
+
+}  // namespace
+
+GDNTREE_EXPORT gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
+                                            const int32_t *root_tok, int B, int P, int K, int N,
+                                            gdntree_tree out, void *stream) {
+  if (!lat_logp || !lat_tok || !root_tok || !out.parent || !out.depth || !out.rank ||
+      !out.token || !out.score || !out.anc || !out.n_nodes)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || P <= 0 || K <= 0 || N <= 0) return GDNTREE_ERR_ARG;
+  if (P > kMaxP || K > kMaxK || N > kMaxN || !grid_fits(B)) return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  if (launch_build(lat_logp, lat_tok, root_tok, B, P, K, N, out, (hipStream_t)stream) != hipSuccess)
+    return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
+GDNTREE_EXPORT gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, int L, int H, int dk,
+                                             int dv, gdntree_dtype in_dtype, const void *q,
+                                             const void *k, const void *v, const void *alpha,
+                                             const void *beta, const float *state,
+                                             gdntree_dtype out_dtype, void *o, void *stream) {
+  if (!tree.parent || !tree.n_nodes || !q || !k || !v || !alpha || !beta || !state || !o)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || N <= 0 || L <= 0 || H <= 0) return GDNTREE_ERR_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDNTREE_ERR_ARG;
+  if (gdntree_status st = head_dims(dk, dv); st != GDNTREE_OK) return st;
+  if (N > kMaxN || !grid_fits((long long)L * B * H)) return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  VerifyParams p;
+  p.parent = tree.parent;
+  p.n_nodes = tree.n_nodes;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state = state;
+  p.o = o;
+  p.B = B; p.R = N + 1; p.L = L; p.H = H; p.D = dk;
+  p.in_bf16 = in_dtype == GDNTREE_BF16;
+  p.out_bf16 = out_dtype == GDNTREE_BF16;
+  if (launch_verify(p, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
+GDNTREE_EXPORT gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, int N, int P,
+                                                    const int32_t *target_argmax, int L, int H,
+                                                    int dk, int dv, gdntree_dtype in_dtype,
+                                                    const void *k, const void *v, const void *alpha,
+                                                    const void *beta, float *state, int32_t *acc_len,
+                                                    int32_t *acc_tok, int32_t *acc_node,
+                                                    void *stream) {
+  if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !k || !v || !alpha ||
+      !beta || !state || !acc_len || !acc_tok || !acc_node)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || N <= 0 || P <= 0 || L <= 0 || H <= 0) return GDNTREE_ERR_ARG;
+  if (!dtype_ok(in_dtype)) return GDNTREE_ERR_ARG;
+  if (gdntree_status st = head_dims(dk, dv); st != GDNTREE_OK) return st;
+  if (N > kMaxN || P > kMaxP || !grid_fits((long long)L * B * H)) return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  CommitParams p;
+  p.parent = tree.parent; p.token = tree.token; p.n_nodes = tree.n_nodes; p.target = target_argmax;
+  p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state = state;
+  p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
+  p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
+  p.in_bf16 = in_dtype == GDNTREE_BF16;
+  if (launch_accept_commit(p, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
+GDNTREE_EXPORT const char *gdntree_status_str(int status) {
+  switch (status) {
+    case GDNTREE_OK: return "ok";
+    case GDNTREE_ERR_ARG: return "invalid argument (null pointer, non-positive size or unknown dtype)";
+    case GDNTREE_ERR_UNSUPPORTED: return "unsupported size (N<=64, P<=16, K<=64, d_k=d_v in {64,128})";
+    case GDNTREE_ERR_DEVICE: return "no usable HIP device or kernel launch failed";
+    default: return "unknown status";
+  }
+}

@@ -1,0 +1,61 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gdntree.h"
+
+namespace gdntree {
+
+constexpr int kMaxN = 64;          // draft nodes
+constexpr int kMaxSlots = kMaxN + 1;
+constexpr int kMaxP = 16;          // positions, hence tree depth
+constexpr int kMaxK = 64;          // candidates per position
+constexpr int kMaxAnc = kMaxP + 1; // ancestors-or-self of a node (depth 0..16)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// Element loads for the two input dtypes.
+__device__ __forceinline__ float load_elem(const uint16_t *p, size_t i) { return bf16_bits_to_f32(p[i]); }
+__device__ __forceinline__ float load_elem(const float *p, size_t i) { return p[i]; }
+
+// Launchers (defined next to their kernels).  They assume validated arguments.
+hipError_t launch_build(const float *lat_logp, const int32_t *lat_tok, const int32_t *root_tok,
+                        int B, int P, int K, int N, gdntree_tree out, hipStream_t stream);
+
+struct VerifyParams {
+  const int32_t *parent;
+  const int32_t *n_nodes;
+  const void *q, *k, *v, *alpha, *beta;
+  const float *state;
+  void *o;
+  int B, R, L, H, D;   // R = N + 1 slots
+  int in_bf16, out_bf16;
+};
+hipError_t launch_verify(const VerifyParams &p, hipStream_t stream);
+
+struct CommitParams {
+  const int32_t *parent, *token, *n_nodes, *target;
+  const void *k, *v, *alpha, *beta;
+  float *state;
+  int32_t *acc_len, *acc_tok, *acc_node;
+  int B, R, P, L, H, D;
+  int in_bf16;
+};
+hipError_t launch_accept_commit(const CommitParams &p, hipStream_t stream);
+
+}  // namespace gdntree

@@ -1,0 +1,146 @@
+/*
+ * gdntree.h - C ABI of the gfx950 library for lossless draft-tree verification of
+ * speculative decoding against a hybrid Gated-DeltaNet (GDN) target.
+ *
+ * One decode step is three calls on one stream:
+ *   gdntree_build          best-first draft tree from the drafter's top-K lattice
+ *   gdntree_verify         gated-delta-rule outputs of every tree node, per GDN layer
+ *   gdntree_accept_commit  greedy acceptance of the longest matching root path plus a
+ *                          bonus token, then the accepted-path state commit
+ *
+ * Sources: the SpecPilot paper summary (paper.rainbus.top, "SpecPilot: Autonomous
+ * Algorithm Discovery and Systems Optimization for Speculative Decoding"), sections
+ * Prerequisites > speculative decoding, > parallel drafter, > draft-tree verification,
+ * > hybrid recurrent architecture, and Technical novelty.
+ *
+ * Conventions shared by every call
+ *  - Every array argument is a DEVICE pointer to memory the caller owns.  The library never
+ *    allocates, frees or synchronises; it validates arguments on the host, enqueues its
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *  - Layouts are dense row-major with the shapes given; no strides.
+ *  - On any error nothing is enqueued and no output is touched (except ERR_DEVICE after a
+ *    failed launch, when the stream state is the runtime's).  No C++ exception crosses the
+ *    ABI.  The library holds no global state and is safe to call from several threads;
+ *    calls are ordered only through their streams.
+ *  - Slot t of a request's tree holds node t; slot 0 is the root (the pending last token,
+ *    processed first from the committed state), draft slots 1..N follow in insertion order
+ *    and every parent index is smaller than its child's.  Slots >= n_nodes[b] are never
+ *    read and never written.
+ *  - Limits: 1 <= N <= 64 draft nodes, 1 <= P <= 16 positions (so tree depth <= 16),
+ *    1 <= K <= 64 candidates, d_k = d_v in {64, 128}.
+ */
+#ifndef GDNTREE_H
+#define GDNTREE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDNTREE_OK = 0,
+  GDNTREE_ERR_ARG = 1,          /* null pointer, non-positive size, unknown dtype          */
+  GDNTREE_ERR_UNSUPPORTED = 2,  /* a size beyond the limits above, or d_k != d_v            */
+  GDNTREE_ERR_DEVICE = 3        /* no usable HIP device, or a kernel launch failed          */
+} gdntree_status;
+
+typedef enum { GDNTREE_F32 = 0, GDNTREE_BF16 = 1 } gdntree_dtype;
+
+/* One best-first tree per request, N+1 slots each ([B][N+1] arrays). */
+typedef struct {
+  int32_t *parent;   /* parent slot; -1 for the root                                       */
+  int32_t *depth;    /* root 0; a draft at lattice position p has depth p+1                */
+  int32_t *rank;     /* candidate rank at position depth-1; -1 for the root                */
+  int32_t *token;    /* token id; the root holds root_tok[b]                               */
+  double *score;     /* cumulative path log-prob, summed root to leaf in fp64; root 0.0   */
+  uint64_t *anc;     /* bit j-1 set iff draft slot j is an ancestor-or-self; root 0        */
+                     /* (the attention tree mask of the target's attention layers)         */
+  int32_t *n_nodes;  /* [B] slots in use, root included (N+1 unless the trie ran out)      */
+} gdntree_tree;
+
+/*
+ * gdntree_build - best-first (DDTree-style) tree over the drafter lattice.
+ *
+ * Starting from the root, repeatedly inserts the not-yet-inserted lattice child with the
+ * largest cumulative path log-prob score(parent) + lat_logp[b][depth(parent)][rank] until
+ * N draft nodes exist or the trie (positions 0..P-1) is exhausted.  Ties go to the smaller
+ * parent slot, then the smaller rank.  Scores are fp64 sums of the fp32 log-probs, added
+ * root to leaf, so topology and scores are bit-reproducible.  (SpecPilot summary,
+ * Prerequisites > draft-tree verification: nodes added greedily by path log-prob up to N;
+ * Technical novelty: edges scored by log p(child | parent), trees wider than the block.)
+ *
+ *   lat_logp  f32 [B][P][K]  candidate log-probs per position, NON-INCREASING along K
+ *                            (a sorted top-K); an unsorted row yields a valid tree that
+ *                            may differ from the best-first one.  Must not hold NaN.
+ *   lat_tok   i32 [B][P][K]  candidate token ids (distinct within a position)
+ *   root_tok  i32 [B]        the pending last token of each request
+ *   out                      every field written for slots < n_nodes[b]
+ */
+gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
+                             const int32_t *root_tok, int B, int P, int K, int N,
+                             gdntree_tree out, void *stream);
+
+/*
+ * gdntree_verify - per-node gated delta rule over the tree, one or more layers.
+ *
+ * For every layer l, request b, head h and slot t < n_nodes[b], with S_p the state of
+ * t's parent (the committed state h0 = state[l][b][h] for the root):
+ *     S_t = alpha_t (I - beta_t k_t k_t^T) S_p + beta_t k_t v_t^T,    o_t = S_t^T q_t
+ * (SpecPilot summary, Prerequisites > hybrid recurrent architecture).  Node states are
+ * derived along root paths from h0 and never written to memory (no per-node snapshots);
+ * only o is written.  No 1/sqrt(d_k) scale is applied.  The result is exact up to fp32
+ * rounding and reduction order.
+ *
+ * Reads tree.parent and tree.n_nodes only.  A tree whose parent links are not
+ * parent[t] < t for t >= 1, or whose depth exceeds 16, gets NaN outputs for that request.
+ *
+ *   q, k      in_dtype [L][B][N+1][H][d_k]
+ *   v         in_dtype [L][B][N+1][H][d_v]
+ *   alpha     in_dtype [L][B][N+1][H]   decay gate in (0, 1]
+ *   beta      in_dtype [L][B][N+1][H]   write strength
+ *   state     f32 [L][B][H][d_v][d_k]   committed state, read only.  NOTE the layout: the
+ *             d_v x d_k transpose of the d_k x d_v matrix S, i.e. column j of S (the key-
+ *             space vector of value channel j) is contiguous.
+ *   o         out_dtype [L][B][N+1][H][d_v]  written for slots < n_nodes[b]
+ */
+gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, int L, int H, int dk, int dv,
+                              gdntree_dtype in_dtype, const void *q, const void *k,
+                              const void *v, const void *alpha, const void *beta,
+                              const float *state, gdntree_dtype out_dtype, void *o,
+                              void *stream);
+
+/*
+ * gdntree_accept_commit - greedy acceptance plus bonus, then the accepted-path commit.
+ *
+ * Acceptance (SpecPilot summary, Prerequisites > speculative decoding and > draft-tree
+ * verification): u <- root; while some child c of u has token[c] == target_argmax[u]
+ * (the smallest such slot), u <- c.  tau = accepted drafts + 1, at most P+1.  The emitted
+ * tokens are the accepted drafts' tokens followed by the bonus target_argmax[u].
+ * Commit: for every layer and head, state[l][b][h] <- the state of node u, recomputed in
+ * fp32 from the committed state along root -> u with the gated delta rule and written in
+ * place (same layout as gdntree_verify).
+ *
+ *   target_argmax  i32 [B][N+1]  the target's argmax after each slot's node
+ *   k, v, alpha, beta            as for gdntree_verify (rows of the accepted slots are read)
+ *   state          f32 [L][B][H][d_v][d_k], updated in place
+ *   acc_len        i32 [B]       tau
+ *   acc_tok        i32 [B][P+1]  accepted draft tokens then the bonus; padded with -1
+ *   acc_node       i32 [B][P+1]  root slot 0 then the accepted slots; padded with -1
+ * Reads tree.parent, tree.token and tree.n_nodes.
+ */
+gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, int N, int P,
+                                     const int32_t *target_argmax, int L, int H, int dk,
+                                     int dv, gdntree_dtype in_dtype, const void *k,
+                                     const void *v, const void *alpha, const void *beta,
+                                     float *state, int32_t *acc_len, int32_t *acc_tok,
+                                     int32_t *acc_node, void *stream);
+
+/* Human-readable name of a status code ("unknown status" for other values). */
+const char *gdntree_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDNTREE_H */

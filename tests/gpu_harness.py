@@ -1,0 +1,116 @@
+"""Helpers for GPU parity tests: run the HIP path and the oracle on the same inputs and
+compare them to the stated bars (bit-exact trees / acceptance; states and outputs within
+2e-3 of the fp64 state's Frobenius norm)."""
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import CONFIGS, generate, resolve_target
+
+TOL = 2e-3
+
+
+def slice_workload(w, H=None, B=None, L=None):
+    """A sub-workload with the first H heads / B requests / L layers (heads, requests and
+    layers are independent, so this is plumbing, not arithmetic)."""
+    H = H or w.cfg.H
+    B = B or w.cfg.B
+    L = L or w.cfg.L
+    sl5 = (slice(0, L), slice(0, B), slice(None), slice(0, H))
+    w2 = replace(w, cfg=replace(w.cfg, H=H, B=B, L=L),
+                 lat_logp=w.lat_logp[:B].copy(), lat_tok=w.lat_tok[:B].copy(), root_tok=w.root_tok[:B].copy(),
+                 p_top1=w.p_top1[:B].copy(), tgt_choice=w.tgt_choice[:B].copy(),
+                 tgt_uniform=w.tgt_uniform[:B].copy(),
+                 q=w.q[sl5].contiguous(), k=w.k[sl5].contiguous(), v=w.v[sl5].contiguous(),
+                 alpha=w.alpha[sl5].contiguous(), beta=w.beta[sl5].contiguous(),
+                 h0=w.h0[:L, :B, :H].contiguous())
+    return w2
+
+
+def device_inputs(w, dev="cuda"):
+    import gdn_draft_tree_amd as g
+    return dict(
+        lat_logp=torch.from_numpy(w.lat_logp).to(dev), lat_tok=torch.from_numpy(w.lat_tok).to(dev),
+        root_tok=torch.from_numpy(w.root_tok).to(dev),
+        q=w.q.to(dev), k=w.k.to(dev), v=w.v.to(dev), alpha=w.alpha.to(dev), beta=w.beta.to(dev),
+        state=g.state_from_math(w.h0).to(dev))
+
+
+def run_gpu(w, out_dtype=None, d=None):
+    """build -> verify -> (host: synthetic target from the built tree) -> accept_commit."""
+    import gdn_draft_tree_amd as g
+    d = d or device_inputs(w)
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    o = g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    depth = tree.depth.cpu().numpy()
+    n_nodes = tree.n_nodes.cpu().numpy()
+    target = resolve_target(depth, n_nodes, w.lat_tok, w.tgt_choice, w.tgt_uniform)
+    acc = g.gdntree_accept_commit(tree, torch.from_numpy(target).cuda(), d["k"], d["v"], d["alpha"],
+                                  d["beta"], d["state"], w.cfg.P)
+    torch.cuda.synchronize()
+    return dict(tree={f: getattr(tree, f).cpu().numpy() for f in
+                      ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")},
+                o=o.float().cpu().numpy().astype(np.float64), target=target,
+                acc_len=acc[0].cpu().numpy(), acc_tok=acc[1].cpu().numpy(), acc_node=acc[2].cpu().numpy(),
+                state=g.state_to_math(d["state"]).cpu().numpy().astype(np.float64))
+
+
+def run_oracle(w):
+    def target_fn(tree):
+        return resolve_target(tree["depth"], tree["n_nodes"], w.lat_tok, w.tgt_choice, w.tgt_uniform)
+    return oracle.pipeline(w.lat_logp, w.lat_tok, w.root_tok, w.cfg.N, w.f64("q"), w.f64("k"), w.f64("v"),
+                           w.f64("alpha"), w.f64("beta"), w.h0.double().numpy(), target_fn)
+
+
+def assert_tree_equal(gt, ot):
+    np.testing.assert_array_equal(gt["n_nodes"], ot["n_nodes"])
+    for b in range(len(ot["n_nodes"])):
+        n = int(ot["n_nodes"][b])
+        for f in ("parent", "depth", "rank", "token"):
+            np.testing.assert_array_equal(gt[f][b, :n], ot[f][b, :n], err_msg=f"{f} b={b}")
+        assert gt["score"][b, :n].tobytes() == ot["score"][b, :n].tobytes(), f"score bits b={b}"
+        np.testing.assert_array_equal(gt["anc"][b, :n].view(np.uint64), ot["anc"][b, :n], err_msg=f"anc b={b}")
+
+
+def output_errors(g_o, o_ref, hnorm, n_nodes):
+    """max over channels of |o_gpu - o_ref| / ||S_ref(t)||_F for every used (l, b, t, h)."""
+    errs = []
+    for b, n in enumerate(n_nodes):
+        n = int(n)
+        e = np.abs(g_o[:, b, :n] - o_ref[:, b, :n]).max(-1) / hnorm[:, b, :n]
+        errs.append(e.max())
+    return float(max(errs))
+
+
+def state_errors(g_s, s_ref):
+    num = np.abs(g_s - s_ref).max(axis=(-2, -1))
+    den = np.sqrt((s_ref ** 2).sum(axis=(-2, -1)))
+    return float((num / den).max())
+
+
+def check_all(w, out_dtype=None, gpu=None, ref=None):
+    gpu = gpu or run_gpu(w, out_dtype=out_dtype)
+    ref = ref or run_oracle(w)
+    assert_tree_equal(gpu["tree"], ref["tree"])
+    np.testing.assert_array_equal(gpu["target"], ref["target"])
+    oe = output_errors(gpu["o"], ref["o"], ref["hnorm"], ref["tree"]["n_nodes"])
+    assert oe <= TOL, f"output error {oe:.3e} > {TOL}"
+    np.testing.assert_array_equal(gpu["acc_len"], ref["acc_len"])
+    np.testing.assert_array_equal(gpu["acc_tok"], ref["acc_tok"])
+    np.testing.assert_array_equal(gpu["acc_node"], ref["acc_node"])
+    se = state_errors(gpu["state"], ref["state"])
+    assert se <= TOL, f"committed state error {se:.3e} > {TOL}"
+    return dict(out_err=oe, state_err=se, gpu=gpu, ref=ref)
+
+
+def config(name):
+    return CONFIGS[name]
+
+
+def make(name, seed=0, **kw):
+    return generate(name, seed=seed, **kw)

@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad arguments on
+the host before touching a device (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdntree.h")
+
+
+def _lib():
+    import gdn_draft_tree_amd as g
+    return g
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdntree_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == ["gdntree_accept_commit", "gdntree_build", "gdntree_status_str", "gdntree_verify"]
+
+
+def test_library_exports_every_declared_symbol():
+    g = _lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (gdntree_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(g.LIB, name)
+    # nothing else leaks out of the library under the gdntree_ prefix
+    assert exported == set(_declared())
+
+
+def test_status_strings():
+    g = _lib()
+    seen = set()
+    for code in (g.GDNTREE_OK, g.GDNTREE_ERR_ARG, g.GDNTREE_ERR_UNSUPPORTED, g.GDNTREE_ERR_DEVICE):
+        s = g.gdntree_status_str(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 4
+    assert g.gdntree_status_str(99) == "unknown status"
+    assert g.gdntree_status_str(-1) == "unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: every case below fails validation first
+
+
+def _tree(g, **null):
+    fields = {f: FAKE for f, _ in g.CTree._fields_}
+    fields.update({k: None for k in null})
+    return g.CTree(**fields)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_logp", 1), ("null_tree_field", 1), ("B0", 1), ("P0", 1), ("K0", 1), ("N0", 1),
+    ("P17", 2), ("K65", 2), ("N65", 2),
+])
+def test_build_rejects(case, expect):
+    g = _lib()
+    args = dict(logp=FAKE, tok=FAKE, root=FAKE, B=2, P=8, K=16, N=24, tree=_tree(g))
+    if case == "null_logp": args["logp"] = None
+    if case == "null_tree_field": args["tree"] = _tree(g, anc=1)
+    if case == "B0": args["B"] = 0
+    if case == "P0": args["P"] = 0
+    if case == "K0": args["K"] = 0
+    if case == "N0": args["N"] = 0
+    if case == "P17": args["P"] = 17
+    if case == "K65": args["K"] = 65
+    if case == "N65": args["N"] = 65
+    st = g.LIB.gdntree_build(args["logp"], args["tok"], args["root"], args["B"], args["P"], args["K"],
+                             args["N"], args["tree"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_q", 1), ("null_state", 1), ("null_parent", 1), ("H0", 1), ("L0", 1), ("dtype9", 1),
+    ("out_dtype9", 1), ("dk_ne_dv", 2), ("d96", 2), ("d256", 2), ("N65", 2), ("dneg", 1),
+])
+def test_verify_rejects(case, expect):
+    g = _lib()
+    a = dict(tree=_tree(g), B=2, N=24, L=1, H=4, dk=128, dv=128, idt=1, q=FAKE, k=FAKE, v=FAKE,
+             al=FAKE, be=FAKE, st=FAKE, odt=1, o=FAKE)
+    if case == "null_q": a["q"] = None
+    if case == "null_state": a["st"] = None
+    if case == "null_parent": a["tree"] = _tree(g, parent=1)
+    if case == "H0": a["H"] = 0
+    if case == "L0": a["L"] = 0
+    if case == "dtype9": a["idt"] = 9
+    if case == "out_dtype9": a["odt"] = 9
+    if case == "dk_ne_dv": a["dv"] = 64
+    if case == "d96": a["dk"] = a["dv"] = 96
+    if case == "d256": a["dk"] = a["dv"] = 256
+    if case == "N65": a["N"] = 65
+    if case == "dneg": a["dk"] = -128
+    st = g.LIB.gdntree_verify(a["tree"], a["B"], a["N"], a["L"], a["H"], a["dk"], a["dv"], a["idt"], a["q"],
+                              a["k"], a["v"], a["al"], a["be"], a["st"], a["odt"], a["o"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_target", 1), ("null_acc", 1), ("null_token", 1), ("P0", 1), ("P17", 2), ("N65", 2),
+    ("d32", 2), ("dtype7", 1),
+])
+def test_accept_commit_rejects(case, expect):
+    g = _lib()
+    a = dict(tree=_tree(g), B=2, N=24, P=8, tgt=FAKE, L=1, H=4, dk=128, dv=128, idt=1, k=FAKE, v=FAKE,
+             al=FAKE, be=FAKE, st=FAKE, al_=FAKE, at=FAKE, an=FAKE)
+    if case == "null_target": a["tgt"] = None
+    if case == "null_acc": a["an"] = None
+    if case == "null_token": a["tree"] = _tree(g, token=1)
+    if case == "P0": a["P"] = 0
+    if case == "P17": a["P"] = 17
+    if case == "N65": a["N"] = 65
+    if case == "d32": a["dk"] = a["dv"] = 32
+    if case == "dtype7": a["idt"] = 7
+    st = g.LIB.gdntree_accept_commit(a["tree"], a["B"], a["N"], a["P"], a["tgt"], a["L"], a["H"], a["dk"],
+                                     a["dv"], a["idt"], a["k"], a["v"], a["al"], a["be"], a["st"], a["al_"],
+                                     a["at"], a["an"], None)
+    assert st == expect
+
+
+def test_no_device_reports_err_device():
+    """Valid arguments on a machine without a GPU stop at the device check (no launch)."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this case only runs where no device exists")
+    g = _lib()
+    st = g.LIB.gdntree_verify(_tree(g), 2, 24, 1, 4, 128, 128, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1,
+                              FAKE, None)
+    assert st == g.GDNTREE_ERR_DEVICE
+
+
+def test_binding_checks_devices_and_dtypes():
+    """The Python binding refuses host tensors before calling the library."""
+    import torch
+    g = _lib()
+    with pytest.raises(ValueError):
+        g.gdntree_build(torch.zeros(1, 4, 4), torch.zeros(1, 4, 4, dtype=torch.int32),
+                        torch.zeros(1, dtype=torch.int32), 8,
+                        out=g.Tree(*[torch.zeros(1, 9)] * 6, torch.zeros(1)))

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs.  Trees, targets and acceptance must be bit-exact; outputs and committed states
+within 2e-3 of the fp64 state's Frobenius norm (max-abs error over value channels)."""
+import math
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import CONFIGS, Config, generate
+
+from . import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def test_tiny_full():
+    w = generate("tiny", seed=0)
+    r = H.check_all(w)
+    _say(f"tiny: out_err={r['out_err']:.2e} state_err={r['state_err']:.2e} tau={r['gpu']['acc_len']}")
+
+
+@pytest.mark.parametrize("name,seed,heads,reqs,layers", [
+    ("one_layer", 0, None, None, None),     # 32 heads -> 1-wave workgroups, 4 slices per head
+    ("one_layer", 1, None, None, None),
+    ("batched", 0, 8, None, None),          # 192 heads -> 2-wave workgroups
+    ("batched", 1, 16, None, None),         # 384 heads -> 4-wave workgroups
+    ("ragged", 0, 4, None, None),           # N = 64: 65 rows, a ragged last node tile
+    ("ragged", 2, 8, 16, None),
+    ("deep", 0, 2, None, 48),               # 48 layers share one tree
+])
+def test_configs(name, seed, heads, reqs, layers):
+    w = generate(name, seed=seed, B=reqs)
+    w = H.slice_workload(w, H=heads, L=layers)
+    r = H.check_all(w)
+    _say(f"{name} seed={seed} H={w.cfg.H} B={w.cfg.B} L={w.cfg.L}: out_err={r['out_err']:.2e} "
+         f"state_err={r['state_err']:.2e} tau={r['gpu']['acc_len'].tolist()}")
+
+
+@pytest.mark.parametrize("name", ["one_layer", "batched", "ragged", "deep"])
+def test_full_size_sampled(name):
+    """Full configuration on the GPU (the bench's launch shape); the oracle checks a sample
+    of heads and requests, the tree and acceptance of every request."""
+    w = generate(name, seed=0)
+    gpu = H.run_gpu(w)
+    cfg = w.cfg
+    heads = sorted({0, cfg.H // 2, cfg.H - 1})
+    reqs = sorted({0, cfg.B - 1})
+    layers = sorted({0, cfg.L - 1})
+    import oracle
+    tree = oracle.build_tree(w.lat_logp, w.lat_tok, w.root_tok, cfg.N)
+    H.assert_tree_equal(gpu["tree"], tree)
+    from workloads import resolve_target
+    target = resolve_target(tree["depth"], tree["n_nodes"], w.lat_tok, w.tgt_choice, w.tgt_uniform)
+    acc_len, acc_tok, acc_node = oracle.accept(tree, target, cfg.P)
+    np.testing.assert_array_equal(gpu["acc_len"], acc_len)
+    np.testing.assert_array_equal(gpu["acc_tok"], acc_tok)
+    np.testing.assert_array_equal(gpu["acc_node"], acc_node)
+    worst_o = worst_s = 0.0
+    for l in layers:
+        for b in reqs:
+            n = int(tree["n_nodes"][b])
+            for h in heads:
+                q, k, v = (w.f64(x)[l, b, :, h] for x in ("q", "k", "v"))
+                a, bb = w.f64("alpha")[l, b, :, h], w.f64("beta")[l, b, :, h]
+                h0 = w.h0[l, b, h].double().numpy()
+                st, ou = oracle.verify_request(tree["parent"][b], n, q[:, None], k[:, None], v[:, None],
+                                               a[:, None], bb[:, None], h0[None])
+                hn = np.sqrt((st[:, 0] ** 2).sum(axis=(-2, -1)))
+                err = np.abs(gpu["o"][l, b, :n, h] - ou[:, 0]).max(-1) / hn
+                worst_o = max(worst_o, float(err.max()))
+                u = int(acc_node[b, int(acc_len[b]) - 1])
+                se = np.abs(gpu["state"][l, b, h] - st[u, 0]).max() / np.linalg.norm(st[u, 0])
+                worst_s = max(worst_s, float(se))
+    _say(f"{name} full size: sampled out_err={worst_o:.2e} state_err={worst_s:.2e}")
+    assert worst_o <= H.TOL and worst_s <= H.TOL
+
+
+def _custom(P, K, N, B=2, H_=2, D=128, dtype="bf16", L=1, seed=0, V=1000):
+    cfg = Config("custom", B=B, L=L, H=H_, D=D, dtype=dtype, P=P, K=K, V=V, N=N)
+    return generate(cfg, seed=seed)
+
+
+def test_uniform_lattice_ties():
+    """Every candidate tied: the tie-break (parent slot, then rank) decides the whole tree."""
+    w = _custom(P=4, K=4, N=64)
+    w.lat_logp[:] = np.float32(-math.log(4))
+    H.check_all(w)
+
+
+def test_k1_chain_and_exhausted_trie():
+    H.check_all(_custom(P=16, K=1, N=24))          # chain of 16, n = 17 < N + 1
+    H.check_all(_custom(P=2, K=3, N=64, B=3))       # 12-node trie, n = 13
+
+
+def test_deep_chain_tau_17():
+    """A peaked lattice and a target that always agrees with rank 0: depth 16, tau = 17."""
+    w = _custom(P=16, K=16, N=64, B=2, H_=4)
+    logp = w.lat_logp.astype(np.float64)
+    logp[..., 0] = -1e-4
+    logp[..., 1:] -= 20.0
+    w.lat_logp[:] = np.sort(logp, axis=-1)[..., ::-1].astype(np.float32)
+    w.tgt_choice[:] = 0
+    r = H.check_all(w)
+    assert (r["gpu"]["acc_len"] == 17).all()
+
+
+def test_poisoned_unused_slots():
+    """Slots at or beyond n_nodes hold NaN inputs and a sentinel output; neither may leak."""
+    import gdn_draft_tree_amd as g
+    w = _custom(P=2, K=3, N=40, B=2, H_=3)           # n = 13 of 41 slots
+    n = 13
+    for name in ("q", "k", "v", "alpha", "beta"):
+        getattr(w, name)[:, :, n:] = float("nan")
+    d = H.device_inputs(w)
+    o = torch.full((1, 2, 41, 3, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o=o)
+    torch.cuda.synchronize()
+    assert int(tree.n_nodes.cpu()[0]) == n
+    oc = o.float().cpu()
+    assert torch.isfinite(oc[:, :, :n]).all()
+    assert (oc[:, :, n:] == 7.0).all()
+    H.check_all(w)
+
+
+@pytest.mark.parametrize("D,dtype,out", [(64, "bf16", None), (128, "f32", None), (64, "f32", None),
+                                         (128, "bf16", torch.float32)])
+def test_dtypes_and_head_dims(D, dtype, out):
+    w = _custom(P=8, K=16, N=64, B=3, H_=4, D=D, dtype=dtype)
+    H.check_all(w, out_dtype=out)
+
+
+def test_layers_and_requests():
+    H.check_all(_custom(P=8, K=8, N=24, B=5, H_=3, L=4, seed=3))
+
+
+def test_determinism_and_launch_shape_independence():
+    """Same inputs give bitwise-identical outputs run to run, and a request's outputs do not
+    depend on the launch shape (1-wave vs 4-wave workgroups, chosen by the head count)."""
+    import gdn_draft_tree_amd as g
+    w1 = _custom(P=8, K=16, N=64, B=1, H_=8, seed=5)
+    d1 = H.device_inputs(w1)
+    t1 = g.gdntree_build(d1["lat_logp"], d1["lat_tok"], d1["root_tok"], 64)
+    o1 = g.gdntree_verify(t1, d1["q"], d1["k"], d1["v"], d1["alpha"], d1["beta"], d1["state"])
+    o1b = g.gdntree_verify(t1, d1["q"], d1["k"], d1["v"], d1["alpha"], d1["beta"], d1["state"])
+    # 32 copies of the request: 256 heads -> 4-wave workgroups
+    rep = lambda x: x.repeat_interleave(32, dim=1) if x.dim() >= 2 else x
+    d32 = {k_: (rep(v_) if k_ in ("q", "k", "v", "alpha", "beta", "state") else v_) for k_, v_ in d1.items()}
+    d32["lat_logp"] = d1["lat_logp"].repeat(32, 1, 1)
+    d32["lat_tok"] = d1["lat_tok"].repeat(32, 1, 1)
+    d32["root_tok"] = d1["root_tok"].repeat(32)
+    t32 = g.gdntree_build(d32["lat_logp"], d32["lat_tok"], d32["root_tok"], 64)
+    o32 = g.gdntree_verify(t32, d32["q"].contiguous(), d32["k"].contiguous(), d32["v"].contiguous(),
+                           d32["alpha"].contiguous(), d32["beta"].contiguous(), d32["state"].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o1b.view(torch.int16))
+    for b in (0, 17, 31):
+        assert torch.equal(o32[:, b].view(torch.int16), o1[:, 0].view(torch.int16))
+
+
+def test_malformed_tree_is_contained():
+    """A parent link that is not smaller than its child gives NaN outputs for that request
+    only; an out-of-range node count leaves that request's outputs untouched."""
+    import gdn_draft_tree_amd as g
+    w = _custom(P=4, K=4, N=8, B=3, H_=2)
+    d = H.device_inputs(w)
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], 8)
+    torch.cuda.synchronize()
+    tree.parent[1, 5] = 7
+    tree.n_nodes[2] = 99
+    o = torch.full((1, 3, 9, 2, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o=o)
+    torch.cuda.synchronize()
+    oc = o.float().cpu()
+    assert torch.isfinite(oc[:, 0]).all()
+    assert torch.isnan(oc[:, 1]).all()
+    assert (oc[:, 2] == 3.0).all()
