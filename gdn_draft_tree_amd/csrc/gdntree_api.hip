@@ -52,7 +52,7 @@ GDNTREE_EXPORT gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, in
                                              const void *k, const void *v, const void *alpha,
                                              const void *beta, const float *state,
                                              gdntree_dtype out_dtype, void *o, void *stream) {
-  if (!tree.parent || !tree.n_nodes || !q || !k || !v || !alpha || !beta || !state || !o)
+  if (!tree.parent || !tree.anc || !tree.n_nodes || !q || !k || !v || !alpha || !beta || !state || !o)
     return GDNTREE_ERR_ARG;
   if (B <= 0 || N <= 0 || L <= 0 || H <= 0) return GDNTREE_ERR_ARG;
   if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDNTREE_ERR_ARG;
@@ -61,6 +61,7 @@ GDNTREE_EXPORT gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, in
   if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
   VerifyParams p;
   p.parent = tree.parent;
+  p.anc = reinterpret_cast<const unsigned long long *>(tree.anc);
   p.n_nodes = tree.n_nodes;
   p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
   p.state = state;

@@ -17,6 +17,7 @@ constexpr int kMaxAnc = kMaxP + 1; // ancestors-or-self of a node (depth 0..16)
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
@@ -39,6 +40,7 @@ hipError_t launch_build(const float *lat_logp, const int32_t *lat_tok, const int
 
 struct VerifyParams {
   const int32_t *parent;
+  const unsigned long long *anc;
   const int32_t *n_nodes;
   const void *q, *k, *v, *alpha, *beta;
   const float *state;

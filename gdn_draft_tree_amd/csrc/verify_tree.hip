@@ -16,7 +16,7 @@
 // and o_t = g_t S0^T q_t + sum_{s in anc(t)+t} Mm[t,s] u_s with Mm[t,s] = r(t,s)(q_t . k_s).
 // With Wm = Mm (I + Lm)^-1 (same ancestor sparsity) this collapses to
 //     o_t = S0^T qe_t + sum_s W1[t,s] v_s,
-//     qe_t = g_t q_t - sum_s W2[t,s] k_s,   W1[t,s] = Wm[t,s] b_s,   W2 = W1[t,s] g_s,
+//     qe_t = g_t q_t - sum_s W2[t,s] k_s,   W1[t,s] = Wm[t,s] b_s,   W2[t,s] = W1[t,s] g_s,
 // so S0 (the only large operand, d_k x d_v fp32) is touched by ONE dense product
 // [qe_t]^T S0 over all nodes.  That product runs on bf16 MFMA with S0 and qe split into
 // hi + lo bf16 parts (hi*hi + lo*hi + hi*lo; the dropped lo*lo term is ~2^-16 relative),
@@ -26,14 +26,18 @@
 // Work decomposition: one workgroup per (layer, request, head) and slice of d_v rows; each
 // wave owns 32 value channels j (two 16-row MFMA tiles of S0^T) for all nodes.  S0^T rows
 // are contiguous in the [d_v][d_k] state layout, so each lane loads its MFMA A-operand
-// fragments straight from HBM, at kernel entry, while the tree prologue runs.
+// fragments straight from HBM at kernel entry, while the tree prologue runs.  Ancestor
+// sets come from the tree's ancestor bitmasks (depth = popcount), so no thread walks
+// parent links.  LDS holds only the n used rows, which lets two workgroups share a CU at
+// N = 64 and overlap one's prologue with the other's HBM traffic.
 
 #include "gdntree_internal.h"
 
 namespace gdntree {
 namespace {
 
-constexpr int kA = kMaxAnc;  // 17 ancestor slots (depth 0..16)
+constexpr int kA = kMaxAnc;  // 17 ancestor depths (0..16)
+constexpr int kAR = 20;      // padded compact row (five 16-byte vectors)
 
 template <bool BF16IN>
 struct InT;
@@ -45,50 +49,64 @@ struct InT<false> { typedef float T; static constexpr int kPad = 4; };
 template <int D, bool BF16IN, int NT>
 struct VerifySmem {
   typedef typename InT<BF16IN>::T T;
-  static constexpr int NP = 16 * NT;                  // padded node rows
-  static constexpr int RS = D + InT<BF16IN>::kPad;    // K/Q/V row stride (16 B pad)
-  static constexpr int QS = D + 8;                    // qe hi/lo row stride (bf16)
-  alignas(16) T k[NP * RS];
-  alignas(16) T q[NP * RS];                           // bf16 input: reused as qe_hi
-  alignas(16) T v[BF16IN ? NP * D : 4];               // fp32 input reads v from memory
-  alignas(16) uint16_t qhi[BF16IN ? 8 : NP * QS];
-  alignas(16) uint16_t qlo[NP * QS];
-  alignas(16) float lc[NP * kA];                      // k.k Gram -> Lm
-  alignas(16) float mc[NP * kA];                      // q.k Gram -> Mm
-  alignas(16) float wc[NP * kA];                      // Wm
-  float alpha[NP], beta[NP], gamma[NP];
-  int parent[NP];
-  int8_t depth[NP];
-  int8_t anc[NP * kA];                                // ancestor slot at each depth
+  static constexpr int RM = (16 * NT < kMaxSlots) ? 16 * NT : kMaxSlots;  // rows held
+  static constexpr int RS = D + InT<BF16IN>::kPad;  // K/Q/V row stride (16 B pad)
+  static constexpr int QS = D + 8;                  // qe hi/lo row stride (bf16)
+  alignas(16) T kv[RM * RS];                        // k rows, later v rows
+  alignas(16) T q[RM * RS];                         // q rows; bf16 input: then qe_hi
+  alignas(16) uint16_t qhi[BF16IN ? 8 : RM * QS];
+  alignas(16) uint16_t qlo[RM * QS];
+  alignas(16) float lc[RM * kAR];                   // k.k Gram -> Lm rows
+  alignas(16) float mc[RM * kAR];                   // q.k Gram -> W2 rows
+  alignas(16) float wc[RM * kAR];                   // W1 rows
+  alignas(16) int8_t anc[RM * kAR];                 // ancestor slot at each depth
+  alignas(16) unsigned long long mask[RM];
+  float alpha[RM], beta[RM], gamma[RM];
+  int parent[RM];
+  int8_t depth[RM];
   int bad;
 };
 
-// 8 consecutive elements of an LDS row as one MFMA operand (bf16 input: exact).
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t *row) {
   const uint4 u = *reinterpret_cast<const uint4 *>(row);
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// x = hi + lo with hi, lo bf16 (round to nearest even); x - hi is exact in fp32.
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
-  u16x8 h, l;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint16_t hb = f32_to_bf16_bits(x[i]);
-    h[i] = hb;
-    l[i] = f32_to_bf16_bits(x[i] - bf16_bits_to_f32(hb));
+    const __bf16 h = (__bf16)x[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(x[i] - (float)h);
   }
-  hi = __builtin_bit_cast(bf16x8, h);
-  lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Gram tile product for rows ra (of A) and rb (of B), 8 columns per lane per k-step.
+// 8 consecutive elements from an LDS row (bf16 or fp32) widened to fp32.
+__device__ __forceinline__ void lds_row8(const uint16_t *p, float *x) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void lds_row8(const float *p, float *x) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// One 16x16 Gram tile (k-steps over d_k) from LDS rows ra (A) and rb (B).
 template <int D, bool BF16IN>
-__device__ __forceinline__ f32x4 gram_tile(const typename InT<BF16IN>::T *A, const typename InT<BF16IN>::T *Bm,
-                                           int rs, int ra, int rb, int kofs) {
+__device__ __forceinline__ f32x4 gram_tile(const typename InT<BF16IN>::T *A,
+                                           const typename InT<BF16IN>::T *Bm, int rs, int ra,
+                                           int rb, int kofs) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
@@ -97,8 +115,8 @@ __device__ __forceinline__ f32x4 gram_tile(const typename InT<BF16IN>::T *A, con
       acc = mfma(lds_frag(A + ra * rs + col), lds_frag(Bm + rb * rs + col), acc);
     } else {
       float xa[8], xb[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { xa[i] = A[ra * rs + col + i]; xb[i] = Bm[rb * rs + col + i]; }
+      lds_row8(A + ra * rs + col, xa);
+      lds_row8(Bm + rb * rs + col, xb);
       bf16x8 ah, al, bh, bl;
       split8(xa, ah, al);
       split8(xb, bh, bl);
@@ -110,18 +128,41 @@ __device__ __forceinline__ f32x4 gram_tile(const typename InT<BF16IN>::T *A, con
   return acc;
 }
 
-template <int D, bool BF16IN, int NT>
-__global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
+// Load a padded compact row (20 floats) into registers.
+__device__ __forceinline__ void load_row20(const float *p, float *r) {
+#pragma unroll
+  for (int v = 0; v < 5; ++v) {
+    const float4 x = reinterpret_cast<const float4 *>(p)[v];
+    r[4 * v] = x.x; r[4 * v + 1] = x.y; r[4 * v + 2] = x.z; r[4 * v + 3] = x.w;
+  }
+}
+__device__ __forceinline__ void store_row20(float *p, const float *r) {
+#pragma unroll
+  for (int v = 0; v < 5; ++v)
+    reinterpret_cast<float4 *>(p)[v] = make_float4(r[4 * v], r[4 * v + 1], r[4 * v + 2], r[4 * v + 3]);
+}
+__device__ __forceinline__ void load_anc20(const int8_t *p, int *a) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t t4 = *reinterpret_cast<const uint32_t *>(p + 16);
+  const uint32_t w[5] = {u.x, u.y, u.z, u.w, t4};
+#pragma unroll
+  for (int e = 0; e < 20; ++e) a[e] = (int)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
+}
+
+template <int D, bool BF16IN, int NT, int W>
+__global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
   typedef VerifySmem<D, BF16IN, NT> SM;
   typedef typename SM::T T;
-  constexpr int NP = SM::NP, RS = SM::RS, QS = SM::QS;
-  constexpr int KS = D / 32;        // MFMA k-steps over d_k
+  constexpr int RS = SM::RS, QS = SM::QS;
+  constexpr int KS = D / 32;          // MFMA k-steps over d_k
   constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / CH;         // 16-byte chunks per row
+  constexpr int nthr = 64 * W;
+  constexpr int VPT = BF16IN ? (SM::RM * CPR + nthr - 1) / nthr : 0;  // v chunks per thread
+  constexpr int S = D / (32 * W);  // d_v slices per head
   __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nthr = blockDim.x, W = nthr >> 6;
-  const int S = D / (32 * W);  // d_v slices per head
   int hh, js;
   if (S == 1) {
     hh = blockIdx.x;
@@ -145,80 +186,82 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
   const T *gb = static_cast<const T *>(p.beta);
   auto row_off = [&](int t) -> size_t { return ((rowbase + t) * p.H + h) * (size_t)D; };
 
-  // ---- 0. this wave's S0^T operand fragments (rows j, 8 consecutive i per lane) --------
+  // ---- 0. loads: S0^T fragments -> registers; k, q rows -> LDS; v rows -> registers ----
   const int j0 = js * 32 * W + wave * 32;
   const float *sbase = p.state + (size_t)hh * D * D;
-  float4 sraw[2][KS][2];
+  f32x4 sraw[2][KS][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float4 *ptr = reinterpret_cast<const float4 *>(
+      const f32x4 *ptr = reinterpret_cast<const f32x4 *>(
           sbase + (size_t)(j0 + 16 * mt + (lane & 15)) * D + 32 * ks + 8 * (lane >> 4));
       sraw[mt][ks][0] = ptr[0];
       sraw[mt][ks][1] = ptr[1];
     }
-
-  // ---- 1. tree metadata, gates and the K / Q (/ V) rows of the n used slots -----------
+  for (int c = tid; c < 2 * n * CPR; c += nthr) {
+    const int m = c / (n * CPR), rem = c % (n * CPR), t = rem / CPR, cc = rem % CPR;
+    const uint4 val = *reinterpret_cast<const uint4 *>((m ? gq : gk) + row_off(t) + cc * CH);
+    *reinterpret_cast<uint4 *>((m ? s.q : s.kv) + t * RS + cc * CH) = val;
+  }
+  u32x4 vpre[VPT > 0 ? VPT : 1];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int c = min(tid + i * nthr, n * CPR - 1);
+    vpre[i] = *reinterpret_cast<const u32x4 *>(gv + row_off(c / CPR) + (c % CPR) * CH);
+  }
   if (tid == 0) s.bad = 0;
   for (int t = tid; t < n; t += nthr) {
     s.parent[t] = p.parent[(size_t)b * p.R + t];
+    s.mask[t] = p.anc[(size_t)b * p.R + t];
     const size_t gi = (rowbase + t) * p.H + h;
     s.alpha[t] = load_elem(ga, gi);
     s.beta[t] = load_elem(gb, gi);
   }
-  {
-    constexpr int CPR = D / CH;  // chunks per row
-    const int nmat = BF16IN ? 3 : 2;
-    const int total = nmat * n * CPR;
-    for (int c = tid; c < total; c += nthr) {
-      const int m = c / (n * CPR), rem = c % (n * CPR), t = rem / CPR, cc = rem % CPR;
-      const T *src = (m == 0 ? gk : m == 1 ? gq : gv) + row_off(t) + cc * CH;
-      const uint4 val = *reinterpret_cast<const uint4 *>(src);
-      T *dst = (m == 0) ? s.k + t * RS + cc * CH : (m == 1) ? s.q + t * RS + cc * CH : s.v + t * D + cc * CH;
-      *reinterpret_cast<uint4 *>(dst) = val;
-    }
-  }
   __syncthreads();
 
-  // depth, ancestor table and path gate of each node (walks parent links; checks them)
+  // ---- 1a. per node: validate links, ancestors from the bitmask, path gate ------------
   for (int t = tid; t < n; t += nthr) {
-    int x = t, dep = 0;
-    bool ok = true;
-    while (x > 0) {
-      const int px = s.parent[x];
-      if (px < 0 || px >= x || ++dep > kMaxP) { ok = false; break; }
-      x = px;
+    const unsigned long long m = s.mask[t];
+    const int dt = __popcll(m);
+    bool ok = dt <= kMaxP;
+    if (t == 0) {
+      ok = ok && m == 0ull;
+    } else {
+      const int pt = s.parent[t];
+      ok = ok && pt >= 0 && pt < t && m == (s.mask[pt] | (1ull << (t - 1)));
     }
     if (!ok) {
       s.bad = 1;
-    } else {
-      s.depth[t] = (int8_t)dep;
-      x = t;
-      for (int e = dep; e >= 0; --e) {
-        s.anc[t * kA + e] = (int8_t)x;
-        if (e > 0) x = s.parent[x];
+      continue;
+    }
+    int a[kAR];
+    a[0] = 0;
+    unsigned long long mm = m;
+#pragma unroll
+    for (int e = 1; e < kAR; ++e) {
+      a[e] = 0;
+      if (e <= dt) {
+        a[e] = __ffsll((long long)mm);  // slot = bit index + 1
+        mm &= mm - 1;
       }
-      float g = 1.f;
-      for (int e = 0; e <= dep; ++e) g *= s.alpha[s.anc[t * kA + e]];
-      s.gamma[t] = g;
     }
-  }
-  __syncthreads();
-
-  const int jw0 = js * 32 * W;  // this workgroup's first value channel
-  if (s.bad) {
-    const int span = 32 * W;
-    for (int c = tid; c < n * span; c += nthr) {
-      const int t = c / span, j = jw0 + c % span;
-      const size_t oi = row_off(t) + j;
-      if (p.out_bf16) static_cast<uint16_t *>(p.o)[oi] = 0x7fc0;
-      else static_cast<float *>(p.o)[oi] = __builtin_nanf("");
-    }
-    return;
+    uint32_t w[5];
+#pragma unroll
+    for (int v = 0; v < 5; ++v)
+      w[v] = (uint32_t)a[4 * v] | ((uint32_t)a[4 * v + 1] << 8) | ((uint32_t)a[4 * v + 2] << 16) |
+             ((uint32_t)a[4 * v + 3] << 24);
+    *reinterpret_cast<uint4 *>(&s.anc[t * kAR]) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint32_t *>(&s.anc[t * kAR + 16]) = w[4];
+    s.depth[t] = (int8_t)dt;
+    float g = 1.f;
+#pragma unroll
+    for (int e = 0; e < kA; ++e)
+      if (e <= dt) g *= s.alpha[a[e]];
+    s.gamma[t] = g;
   }
 
-  // ---- 2. Gram entries k_t.k_s and q_t.k_s for s ancestor-or-self of t (MFMA) ---------
+  // ---- 1b. Gram entries k_t.k_s and q_t.k_s for s ancestor-or-self of t (MFMA) --------
   {
     constexpr int NPAIR = NT * (NT + 1) / 2;
     for (int pi = wave; pi < 2 * NPAIR; pi += W) {
@@ -228,76 +271,114 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
       while ((mt + 1) * (mt + 2) / 2 <= qi) ++mt;
       const int nt = qi - mt * (mt + 1) / 2;
       if (16 * mt >= n) continue;
-      const f32x4 g = gram_tile<D, BF16IN>(part ? s.q : s.k, s.k, RS, 16 * mt + (lane & 15),
-                                           16 * nt + (lane & 15), 8 * (lane >> 4));
+      const int ra = min(16 * mt + (lane & 15), n - 1), rb = min(16 * nt + (lane & 15), n - 1);
+      const f32x4 g = gram_tile<D, BF16IN>(part ? s.q : s.kv, s.kv, RS, ra, rb, 8 * (lane >> 4));
       const int sn = 16 * nt + (lane & 15);
+      if (sn >= n) continue;
+      const unsigned long long ms = s.mask[sn];
+      const int es = __popcll(ms);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = 16 * mt + 4 * (lane >> 4) + r;
-        if (t < n && sn <= t) {
-          const int e = s.depth[sn];
-          if (e <= s.depth[t] && s.anc[t * kA + e] == sn) (part ? s.mc : s.lc)[t * kA + e] = g[r];
+        if (t < n && sn <= t && es <= kMaxP) {
+          const unsigned long long mtt = s.mask[t];
+          const bool is_anc = (sn == 0) || ((mtt >> (sn - 1)) & 1ull);
+          if (is_anc) (part ? s.mc : s.lc)[t * kAR + es] = g[r];
         }
       }
     }
   }
   __syncthreads();
+  if (s.bad) {
+    const int jw0 = js * 32 * W, span = 32 * W;
+    for (int c = tid; c < n * span; c += nthr) {
+      const size_t oi = row_off(c / span) + jw0 + c % span;
+      if (p.out_bf16) static_cast<uint16_t *>(p.o)[oi] = 0x7fc0;
+      else static_cast<float *>(p.o)[oi] = __builtin_nanf("");
+    }
+    return;
+  }
 
-  // ---- 3. gate ratios: Lm and Mm rows --------------------------------------------------
+  // ---- 2. per node: Lm, Mm rows; then Wm solve; W1, W2 rows ---------------------------
   for (int t = tid; t < n; t += nthr) {
     const int dt = s.depth[t];
+    int arow[kAR];
+    load_anc20(&s.anc[t * kAR], arow);
+    float gk[kAR], gqk[kAR];
+    load_row20(&s.lc[t * kAR], gk);
+    load_row20(&s.mc[t * kAR], gqk);
+    float al[kAR];
+#pragma unroll
+    for (int e = 0; e < kAR; ++e) al[e] = (e < kA && e <= dt) ? s.alpha[arow[e]] : 1.f;
     const float bt = s.beta[t];
     float rho = 1.f;  // g_t / g_{anc at depth e}
-    for (int e = dt; e >= 0; --e) {
-      s.mc[t * kA + e] *= rho;
-      if (e < dt) s.lc[t * kA + e] *= bt * rho;
-      rho *= s.alpha[s.anc[t * kA + e]];
+    float lrow[kAR], mrow[kAR];
+#pragma unroll
+    for (int e = kAR - 1; e >= 0; --e) {
+      const bool on = e < kA && e <= dt;
+      mrow[e] = on ? rho * gqk[e] : 0.f;
+      lrow[e] = (e < dt) ? bt * rho * gk[e] : 0.f;
+      if (on) rho *= al[e];
     }
+    store_row20(&s.lc[t * kAR], lrow);
+    store_row20(&s.mc[t * kAR], mrow);
   }
   __syncthreads();
-
-  // Wm row t solves Wm (I + Lm) = Mm over t's path, deepest ancestor first.
   for (int t = tid; t < n; t += nthr) {
     const int dt = s.depth[t];
-    float w[kA];
+    int arow[kAR];
+    load_anc20(&s.anc[t * kAR], arow);
+    float w[kAR];
+    load_row20(&s.mc[t * kAR], w);
+    // right-looking solve of w (I + Lm) = Mm over the path, deepest ancestor first
 #pragma unroll
-    for (int e = kA - 1; e >= 0; --e) {
-      float acc = 0.f;
-      if (e <= dt) {
-        acc = s.mc[t * kA + e];
+    for (int e2 = kA - 1; e2 >= 1; --e2) {
+      if (e2 <= dt) {
+        float lr[kAR];
+        load_row20(&s.lc[arow[e2] * kAR], lr);
 #pragma unroll
-        for (int e2 = e + 1; e2 < kA; ++e2)
-          if (e2 <= dt) acc -= w[e2] * s.lc[s.anc[t * kA + e2] * kA + e];
+        for (int e = 0; e < e2; ++e) w[e] -= w[e2] * lr[e];
       }
-      w[e] = acc;
     }
+    float w1[kAR], w2[kAR];
 #pragma unroll
-    for (int e = 0; e < kA; ++e)
-      if (e <= dt) s.wc[t * kA + e] = w[e];
+    for (int e = 0; e < kAR; ++e) {
+      w1[e] = 0.f;
+      w2[e] = 0.f;
+      if (e < kA && e <= dt) {
+        const int sn = arow[e];
+        w1[e] = w[e] * s.beta[sn];
+        w2[e] = w1[e] * s.gamma[sn];
+      }
+    }
+    store_row20(&s.wc[t * kAR], w1);
+    store_row20(&s.mc[t * kAR], w2);
   }
   __syncthreads();
 
-  // ---- 4. effective queries qe_t = g_t q_t - sum_s W2[t,s] k_s, split hi/lo (bf16) ------
+  // ---- 3. effective queries qe_t = g_t q_t - sum_s W2[t,s] k_s, split hi/lo (bf16) ------
   {
     uint16_t *qhi = BF16IN ? reinterpret_cast<uint16_t *>(s.q) : s.qhi;
     constexpr int C8 = D / 8;
-    for (int it = tid; it < NP * C8; it += nthr) {
+    for (int it = tid; it < n * C8; it += nthr) {
       const int t = it / C8, c = it % C8;
-      float x[8];
-      if (t < n) {
-        const float g = s.gamma[t];
+      int a[kAR];
+      load_anc20(&s.anc[t * kAR], a);
+      float w2[kAR];
+      load_row20(&s.mc[t * kAR], w2);
+      const int dt = s.depth[t];
+      float x[8], y[8];
+      lds_row8(s.q + t * RS + 8 * c, x);
+      const float g = s.gamma[t];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = g * load_elem(s.q, (size_t)t * RS + 8 * c + i);
-        const int dt = s.depth[t];
-        for (int e = 0; e <= dt; ++e) {
-          const int sn = s.anc[t * kA + e];
-          const float w2 = s.wc[t * kA + e] * s.beta[sn] * s.gamma[sn];
+      for (int i = 0; i < 8; ++i) x[i] *= g;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] -= w2 * load_elem(s.k, (size_t)sn * RS + 8 * c + i);
+      for (int e = 0; e < kA; ++e) {
+        if (e <= dt) {
+          lds_row8(s.kv + a[e] * RS + 8 * c, y);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] -= w2[e] * y[i];
         }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = 0.f;
       }
       bf16x8 hi, lo;
       split8(x, hi, lo);
@@ -306,24 +387,33 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
     }
   }
   __syncthreads();
+  if constexpr (BF16IN) {  // k rows are dead: the v rows take their place
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * nthr;
+      if (c < n * CPR) *reinterpret_cast<u32x4 *>(s.kv + (c / CPR) * RS + (c % CPR) * CH) = vpre[i];
+    }
+    __syncthreads();
+  }
 
-  // ---- 5-7. o^T = S0^T [qe] + V^T W1^T, node tile by node tile -------------------------
+  // ---- 4. o^T = S0^T [qe] + V^T W1^T, node tile by node tile --------------------------
   bf16x8 ahi[2][KS], alo[2][KS];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const float x[8] = {sraw[mt][ks][0].x, sraw[mt][ks][0].y, sraw[mt][ks][0].z, sraw[mt][ks][0].w,
-                          sraw[mt][ks][1].x, sraw[mt][ks][1].y, sraw[mt][ks][1].z, sraw[mt][ks][1].w};
+      const float x[8] = {sraw[mt][ks][0][0], sraw[mt][ks][0][1], sraw[mt][ks][0][2], sraw[mt][ks][0][3],
+                          sraw[mt][ks][1][0], sraw[mt][ks][1][1], sraw[mt][ks][1][2], sraw[mt][ks][1][3]};
       split8(x, ahi[mt][ks], alo[mt][ks]);
     }
   const uint16_t *qhi = BF16IN ? reinterpret_cast<const uint16_t *>(s.q) : s.qhi;
   const int ntiles = (n + 15) / 16;
+  const int jl = j0 + 4 * (lane >> 4);  // + 16*mt + r
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (nt >= ntiles) break;
     const int t = 16 * nt + (lane & 15);
-    const int jl = j0 + 4 * (lane >> 4);  // + 16*mt + r
+    const int tb = min(t, n - 1);
     f32x4 acc0[2], acc1[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -331,24 +421,29 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
       acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // V^T W1^T on the vector ALUs (ancestor-sparse)
-    if (t < n) {
-      const int dt = s.depth[t];
-      for (int e = 0; e <= dt; ++e) {
-        const int sn = s.anc[t * kA + e];
-        const float w1 = s.wc[t * kA + e] * s.beta[sn];
+    {
+      int a[kAR];
+      load_anc20(&s.anc[tb * kAR], a);
+      float w1[kAR];
+      load_row20(&s.wc[tb * kAR], w1);
+      const int dt = s.depth[tb];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          float vv[4];
-          if constexpr (BF16IN) {
-            const uint2 u = *reinterpret_cast<const uint2 *>(s.v + sn * D + jl + 16 * mt);
-            vv[0] = bf16_bits_to_f32(u.x & 0xffff); vv[1] = bf16_bits_to_f32(u.x >> 16);
-            vv[2] = bf16_bits_to_f32(u.y & 0xffff); vv[3] = bf16_bits_to_f32(u.y >> 16);
-          } else {
-            const float4 u = *reinterpret_cast<const float4 *>(gv + row_off(sn) + jl + 16 * mt);
-            vv[0] = u.x; vv[1] = u.y; vv[2] = u.z; vv[3] = u.w;
+      for (int e = 0; e < kA; ++e) {
+        if (e <= dt) {
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) {
+            float vv[4];
+            if constexpr (BF16IN) {
+              const uint2 u = *reinterpret_cast<const uint2 *>(s.kv + a[e] * RS + jl + 16 * mt);
+              vv[0] = __uint_as_float(u.x << 16); vv[1] = __uint_as_float(u.x & 0xffff0000u);
+              vv[2] = __uint_as_float(u.y << 16); vv[3] = __uint_as_float(u.y & 0xffff0000u);
+            } else {
+              const float4 u = *reinterpret_cast<const float4 *>(gv + row_off(a[e]) + jl + 16 * mt);
+              vv[0] = u.x; vv[1] = u.y; vv[2] = u.z; vv[3] = u.w;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc0[mt][r] += w1[e] * vv[r];
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc0[mt][r] += w1 * vv[r];
         }
       }
     }
@@ -356,8 +451,8 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int col = 32 * ks + 8 * (lane >> 4);
-      const bf16x8 bhi = lds_frag(qhi + t * QS + col);
-      const bf16x8 blo = lds_frag(s.qlo + t * QS + col);
+      const bf16x8 bhi = lds_frag(qhi + tb * QS + col);
+      const bf16x8 blo = lds_frag(s.qlo + tb * QS + col);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         acc0[mt] = mfma(ahi[mt][ks], bhi, acc0[mt]);
@@ -385,16 +480,24 @@ __global__ __launch_bounds__(256) void verify_kernel(VerifyParams p) {
   }
 }
 
+template <int D, bool BF16IN, int NT, int W>
+hipError_t launch_w(const VerifyParams &p, hipStream_t stream) {
+  const int HT = p.L * p.B * p.H;
+  constexpr int S = D / (32 * W);
+  const long long blocks = (S == 1) ? HT : (long long)((HT + 7) / 8) * 8 * S;
+  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, W>), dim3((unsigned)blocks), dim3(64 * W), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+// Waves per workgroup (one per 32 value channels): a whole head per workgroup when there
+// are enough heads to fill the chip, otherwise slices of a head across workgroups.
 template <int D, bool BF16IN, int NT>
 hipError_t launch_one(const VerifyParams &p, hipStream_t stream) {
   const int HT = p.L * p.B * p.H;
-  int W = D / 32;  // waves per workgroup (one per 32 value channels)
-  if (HT < 256) W = (HT >= 128 && D / 64 >= 1) ? D / 64 : 1;
-  const int S = D / (32 * W);
-  const long long blocks = (S == 1) ? HT : (long long)((HT + 7) / 8) * 8 * S;
-  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT>), dim3((unsigned)blocks), dim3(64 * W), 0,
-                     stream, p);
-  return hipGetLastError();
+  if (HT >= 256) return launch_w<D, BF16IN, NT, D / 32>(p, stream);
+  if (D == 128 && HT >= 128) return launch_w<D, BF16IN, NT, 2>(p, stream);
+  return launch_w<D, BF16IN, NT, 1>(p, stream);
 }
 
 template <int D, bool BF16IN>

@@ -92,8 +92,10 @@ gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
  * only o is written.  No 1/sqrt(d_k) scale is applied.  The result is exact up to fp32
  * rounding and reduction order.
  *
- * Reads tree.parent and tree.n_nodes only.  A tree whose parent links are not
- * parent[t] < t for t >= 1, or whose depth exceeds 16, gets NaN outputs for that request.
+ * Reads tree.parent, tree.anc and tree.n_nodes only (the ancestor bitmask gives each
+ * node's depth and ancestors).  A request whose tree is inconsistent (parent[t] >= t,
+ * anc[t] != anc[parent[t]] | bit t-1, anc[0] != 0, or depth > 16) gets NaN outputs in all
+ * of its slots < n_nodes; a request with n_nodes outside [1, N+1] gets no output at all.
  *
  *   q, k      in_dtype [L][B][N+1][H][d_k]
  *   v         in_dtype [L][B][N+1][H][d_v]
