@@ -24,12 +24,16 @@
 // the tree (Gram entries, gates, the ancestor-restricted solve) is O(nodes * depth) work.
 //
 // Work decomposition: one workgroup per (layer, request, head) and slice of d_v rows; each
-// wave owns 32 value channels j (two 16-row MFMA tiles of S0^T) for all nodes.  S0^T rows
-// are contiguous in the [d_v][d_k] state layout, so each lane loads its MFMA A-operand
-// fragments straight from HBM at kernel entry, while the tree prologue runs.  Ancestor
-// sets come from the tree's ancestor bitmasks (depth = popcount), so no thread walks
-// parent links.  LDS holds only the n used rows, which lets two workgroups share a CU at
-// N = 64 and overlap one's prologue with the other's HBM traffic.
+// wave owns 32 value channels j (two 16-row MFMA tiles of S0^T) for all nodes.  All three
+// dense contractions run on MFMA: the Gram entries k_t.k_s and q_t.k_s; the effective
+// queries [qe]^T = g [q]^T - K^T W2^T; and o^T = S0^T [qe] + V^T W1^T.  W1 and W2 are
+// ancestor-masked node x node matrices, stored densely (hi + lo bf16) in LDS for the
+// product; the O(nodes * depth) solve that produces them runs one thread per node.  S0^T
+// rows are contiguous in the [d_v][d_k] state layout, so each lane loads its S0^T operand
+// fragments straight from HBM at kernel entry, together with its K^T and V^T fragments
+// (gathered along the node axis), while the tree prologue runs.  Ancestor sets come from
+// the tree's ancestor bitmasks (depth = popcount), so no thread walks parent links.  LDS
+// holds only the used rows (under 80 KiB at N = 64), so two workgroups share a CU.
 
 #include "gdntree_internal.h"
 
@@ -50,21 +54,30 @@ template <int D, bool BF16IN, int NT>
 struct VerifySmem {
   typedef typename InT<BF16IN>::T T;
   static constexpr int RM = (16 * NT < kMaxSlots) ? 16 * NT : kMaxSlots;  // rows held
-  static constexpr int RS = D + InT<BF16IN>::kPad;  // K/Q/V row stride (16 B pad)
+  static constexpr int RS = D + InT<BF16IN>::kPad;  // K/Q row stride (16 B pad)
   static constexpr int QS = D + 8;                  // qe hi/lo row stride (bf16)
-  alignas(16) T kv[RM * RS];                        // k rows, later v rows
+  static constexpr int SP = (16 * NT + 31) / 32 * 32;  // node axis padded for MFMA k-steps
+  static constexpr int DS = SP + 8;                 // dense W row stride (bf16)
+  static constexpr int KBYTES = RM * RS * (int)sizeof(T);
+  static constexpr int DBYTES = 2 * RM * DS * 2;
+  static constexpr int R1 = (KBYTES > DBYTES ? KBYTES : DBYTES);
+  // k rows while the Gram entries are formed; then -W2 (hi | lo), later W1 (hi | lo)
+  alignas(16) unsigned char r1[R1];
   alignas(16) T q[RM * RS];                         // q rows; bf16 input: then qe_hi
   alignas(16) uint16_t qhi[BF16IN ? 8 : RM * QS];
   alignas(16) uint16_t qlo[RM * QS];
   alignas(16) float lc[RM * kAR];                   // k.k Gram -> Lm rows
-  alignas(16) float mc[RM * kAR];                   // q.k Gram -> W2 rows
-  alignas(16) float wc[RM * kAR];                   // W1 rows
+  alignas(16) float mc[RM * kAR];                   // q.k Gram -> Mm rows
+  alignas(16) float wc[RM * kAR];                   // W1 rows (compact, by depth)
   alignas(16) int8_t anc[RM * kAR];                 // ancestor slot at each depth
   alignas(16) unsigned long long mask[RM];
   float alpha[RM], beta[RM], gamma[RM];
   int parent[RM];
   int8_t depth[RM];
   int bad;
+  __device__ T *k() { return reinterpret_cast<T *>(r1); }
+  __device__ uint16_t *dhi() { return reinterpret_cast<uint16_t *>(r1); }
+  __device__ uint16_t *dlo() { return reinterpret_cast<uint16_t *>(r1) + RM * DS; }
 };
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint16_t *row) {
@@ -149,20 +162,40 @@ __device__ __forceinline__ void load_anc20(const int8_t *p, int *a) {
   for (int e = 0; e < 20; ++e) a[e] = (int)((w[e >> 2] >> (8 * (e & 3))) & 0xffu);
 }
 
+// A transposed operand fragment: 8 consecutive node slots s (clamped to the used rows) of
+// one channel column `col` of a row-major [node][H][D] input.
+template <bool BF16IN, typename RowOff>
+__device__ __forceinline__ void gather_t(const typename InT<BF16IN>::T *g, RowOff row_off, int n,
+                                         int s0, int col, bf16x8 &hi, bf16x8 &lo) {
+  if constexpr (BF16IN) {
+    u16x8 f;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) f[x] = g[row_off(min(s0 + x, n - 1)) + col];
+    hi = __builtin_bit_cast(bf16x8, f);
+  } else {
+    float f[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) f[x] = g[row_off(min(s0 + x, n - 1)) + col];
+    split8(f, hi, lo);
+  }
+}
+
 template <int D, bool BF16IN, int NT, int W>
 __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
   typedef VerifySmem<D, BF16IN, NT> SM;
   typedef typename SM::T T;
-  constexpr int RS = SM::RS, QS = SM::QS;
+  constexpr int RS = SM::RS, QS = SM::QS, DS = SM::DS;
   constexpr int KS = D / 32;          // MFMA k-steps over d_k
+  constexpr int KSS = SM::SP / 32;    // MFMA k-steps over the node axis
   constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / CH;         // 16-byte chunks per row
   constexpr int nthr = 64 * W;
-  constexpr int VPT = BF16IN ? (SM::RM * CPR + nthr - 1) / nthr : 0;  // v chunks per thread
-  constexpr int S = D / (32 * W);  // d_v slices per head
+  constexpr int S = D / (32 * W);     // d_v slices per head
+  constexpr int NIS = D / 32;         // 32-channel slices of d_k
   __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
   int hh, js;
   if (S == 1) {
     hh = blockIdx.x;
@@ -186,30 +219,11 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
   const T *gb = static_cast<const T *>(p.beta);
   auto row_off = [&](int t) -> size_t { return ((rowbase + t) * p.H + h) * (size_t)D; };
 
-  // ---- 0. loads: S0^T fragments -> registers; k, q rows -> LDS; v rows -> registers ----
-  const int j0 = js * 32 * W + wave * 32;
-  const float *sbase = p.state + (size_t)hh * D * D;
-  f32x4 sraw[2][KS][2];
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const f32x4 *ptr = reinterpret_cast<const f32x4 *>(
-          sbase + (size_t)(j0 + 16 * mt + (lane & 15)) * D + 32 * ks + 8 * (lane >> 4));
-      sraw[mt][ks][0] = ptr[0];
-      sraw[mt][ks][1] = ptr[1];
-    }
-  for (int c = tid; c < 2 * n * CPR; c += nthr) {
-    const int m = c / (n * CPR), rem = c % (n * CPR), t = rem / CPR, cc = rem % CPR;
-    const uint4 val = *reinterpret_cast<const uint4 *>((m ? gq : gk) + row_off(t) + cc * CH);
-    *reinterpret_cast<uint4 *>((m ? s.q : s.kv) + t * RS + cc * CH) = val;
-  }
-  u32x4 vpre[VPT > 0 ? VPT : 1];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int c = min(tid + i * nthr, n * CPR - 1);
-    vpre[i] = *reinterpret_cast<const u32x4 *>(gv + row_off(c / CPR) + (c % CPR) * CH);
-  }
+  // ---- 0. loads ----------------------------------------------------------------------
+  // Order matters: vector-memory loads complete in issue order, so the node metadata and
+  // the k/q rows (needed first) are requested before the operand fragments of S0^T, V^T
+  // and K^T, which then stream in while the tree prologue runs; the first barrier waits
+  // only for the metadata and the k/q rows.
   if (tid == 0) s.bad = 0;
   for (int t = tid; t < n; t += nthr) {
     s.parent[t] = p.parent[(size_t)b * p.R + t];
@@ -218,33 +232,75 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
     s.alpha[t] = load_elem(ga, gi);
     s.beta[t] = load_elem(gb, gi);
   }
+  constexpr int KQPT = (2 * SM::RM * CPR + nthr - 1) / nthr;  // k/q chunks per thread
+  constexpr int KQB = KQPT < 9 ? KQPT : 9;                     // staged in one batch
+  const int nkq = 2 * n * CPR;
+  auto kq_src = [&](int c) -> const T * {
+    const int m = c / (n * CPR), rem = c - m * (n * CPR), t = rem / CPR, cc = rem - t * CPR;
+    return (m ? gq : gk) + row_off(t) + cc * CH;
+  };
+  auto kq_dst = [&](int c) -> T * {
+    const int m = c / (n * CPR), rem = c - m * (n * CPR), t = rem / CPR, cc = rem - t * CPR;
+    return (m ? s.q : s.k()) + t * RS + cc * CH;
+  };
+  u32x4 kq[KQB];
+#pragma unroll
+  for (int i = 0; i < KQB; ++i) kq[i] = *reinterpret_cast<const u32x4 *>(kq_src(min(tid + i * nthr, nkq - 1)));
+
+  const int j0 = js * 32 * W + wave * 32;
+  const float *sbase = p.state + (size_t)hh * D * D;
+  f32x4 sraw[2][KS][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f32x4 *ptr = reinterpret_cast<const f32x4 *>(sbase + (size_t)(j0 + 16 * mt + l16) * D + 32 * ks + 8 * g4);
+      sraw[mt][ks][0] = ptr[0];
+      sraw[mt][ks][1] = ptr[1];
+    }
+  // v: bf16 rows are parked in the (still unused) qe_lo region and gathered transposed
+  // from there; fp32 rows are gathered transposed straight from memory
+  constexpr int VPT = BF16IN ? (SM::RM * CPR + nthr - 1) / nthr : 1;
+  u32x4 vpre[VPT];
+  bf16x8 vt_hi[2][KSS], vt_lo[2][KSS];  // V^T rows j, node slots s
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = min(tid + i * nthr, n * CPR - 1);
+      vpre[i] = *reinterpret_cast<const u32x4 *>(gv + row_off(c / CPR) + (c % CPR) * CH);
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < KSS; ++kk)
+        gather_t<BF16IN>(gv, row_off, n, 32 * kk + 8 * g4, j0 + 16 * mt + l16, vt_hi[mt][kk], vt_lo[mt][kk]);
+  }
+#pragma unroll
+  for (int i = 0; i < KQB; ++i) {
+    const int c = tid + i * nthr;
+    if (c < nkq) *reinterpret_cast<u32x4 *>(kq_dst(c)) = kq[i];
+  }
+  for (int c = tid + KQB * nthr; c < nkq; c += nthr)  // only small workgroups get here
+    *reinterpret_cast<u32x4 *>(kq_dst(c)) = *reinterpret_cast<const u32x4 *>(kq_src(c));
   __syncthreads();
 
   // ---- 1a. per node: validate links, ancestors from the bitmask, path gate ------------
   for (int t = tid; t < n; t += nthr) {
     const unsigned long long m = s.mask[t];
     const int dt = __popcll(m);
-    bool ok = dt <= kMaxP;
-    if (t == 0) {
-      ok = ok && m == 0ull;
-    } else {
-      const int pt = s.parent[t];
-      ok = ok && pt >= 0 && pt < t && m == (s.mask[pt] | (1ull << (t - 1)));
-    }
-    if (!ok) {
-      s.bad = 1;
-      continue;
-    }
+    const int pt = s.parent[t];
+    const bool ok = (t == 0) ? (m == 0ull)
+                             : (dt <= kMaxP && pt >= 0 && pt < t && m == (s.mask[pt] | (1ull << (t - 1))));
+    if (!ok) s.bad = 1;
+    // a[e] = slot of the ancestor at depth e (bit index + 1); 0 (the root) beyond the depth
     int a[kAR];
-    a[0] = 0;
     unsigned long long mm = m;
+    a[0] = 0;
 #pragma unroll
     for (int e = 1; e < kAR; ++e) {
-      a[e] = 0;
-      if (e <= dt) {
-        a[e] = __ffsll((long long)mm);  // slot = bit index + 1
-        mm &= mm - 1;
-      }
+      a[e] = __ffsll((long long)mm);
+      mm &= mm - 1;
     }
     uint32_t w[5];
 #pragma unroll
@@ -253,38 +309,56 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
              ((uint32_t)a[4 * v + 3] << 24);
     *reinterpret_cast<uint4 *>(&s.anc[t * kAR]) = make_uint4(w[0], w[1], w[2], w[3]);
     *reinterpret_cast<uint32_t *>(&s.anc[t * kAR + 16]) = w[4];
-    s.depth[t] = (int8_t)dt;
+    s.depth[t] = (int8_t)min(dt, kMaxP);
     float g = 1.f;
 #pragma unroll
-    for (int e = 0; e < kA; ++e)
-      if (e <= dt) g *= s.alpha[a[e]];
+    for (int e = 0; e < kA; ++e) {
+      const float ae = s.alpha[a[e]];
+      g *= (e <= dt) ? ae : 1.f;
+    }
     s.gamma[t] = g;
+  }
+
+  // K^T fragments of this wave's first d_k slice, from the k rows in LDS (bf16 input)
+  bf16x8 kt_hi[2][KSS], kt_lo[2][KSS];
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int kk = 0; kk < KSS; ++kk) {
+        u16x8 f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x)
+          f[x] = s.k()[min(32 * kk + 8 * g4 + x, n - 1) * RS + 32 * wave + 16 * it + l16];
+        kt_hi[it][kk] = __builtin_bit_cast(bf16x8, f);
+      }
   }
 
   // ---- 1b. Gram entries k_t.k_s and q_t.k_s for s ancestor-or-self of t (MFMA) --------
   {
     constexpr int NPAIR = NT * (NT + 1) / 2;
-    for (int pi = wave; pi < 2 * NPAIR; pi += W) {
+#pragma unroll
+    for (int pi0 = 0; pi0 < 2 * NPAIR; pi0 += W) {
+      const int pi = pi0 + wave;
+      if (pi >= 2 * NPAIR) break;
       const int part = pi >= NPAIR;  // 0: k.k, 1: q.k
       const int qi = part ? pi - NPAIR : pi;
       int mt = 0;
       while ((mt + 1) * (mt + 2) / 2 <= qi) ++mt;
       const int nt = qi - mt * (mt + 1) / 2;
       if (16 * mt >= n) continue;
-      const int ra = min(16 * mt + (lane & 15), n - 1), rb = min(16 * nt + (lane & 15), n - 1);
-      const f32x4 g = gram_tile<D, BF16IN>(part ? s.q : s.kv, s.kv, RS, ra, rb, 8 * (lane >> 4));
-      const int sn = 16 * nt + (lane & 15);
-      if (sn >= n) continue;
-      const unsigned long long ms = s.mask[sn];
+      const int ra = min(16 * mt + l16, n - 1), rb = min(16 * nt + l16, n - 1);
+      const f32x4 g = gram_tile<D, BF16IN>(part ? s.q : s.k(), s.k(), RS, ra, rb, 8 * g4);
+      const int sn = 16 * nt + l16;
+      const unsigned long long ms = s.mask[rb];
       const int es = __popcll(ms);
+      float *dst = part ? s.mc : s.lc;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mt + 4 * (lane >> 4) + r;
-        if (t < n && sn <= t && es <= kMaxP) {
-          const unsigned long long mtt = s.mask[t];
-          const bool is_anc = (sn == 0) || ((mtt >> (sn - 1)) & 1ull);
-          if (is_anc) (part ? s.mc : s.lc)[t * kAR + es] = g[r];
-        }
+        const int t = 16 * mt + 4 * g4 + r;
+        const unsigned long long mtt = s.mask[min(t, n - 1)];
+        const bool anc = sn == 0 || ((mtt >> (sn - 1)) & 1ull);
+        if (t < n && sn <= t && es <= kMaxP && anc) dst[t * kAR + es] = g[r];
       }
     }
   }
@@ -299,7 +373,14 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
     return;
   }
 
-  // ---- 2. per node: Lm, Mm rows; then Wm solve; W1, W2 rows ---------------------------
+  // ---- 2. per node: Lm, Mm rows; then the Wm solve; W1 rows and the dense -W2 ---------
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + i * nthr;
+      if (c < n * CPR) *reinterpret_cast<u32x4 *>(s.qlo + (c / CPR) * QS + (c % CPR) * CH) = vpre[i];
+    }
+  }
   for (int t = tid; t < n; t += nthr) {
     const int dt = s.depth[t];
     int arow[kAR];
@@ -307,9 +388,6 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
     float gk[kAR], gqk[kAR];
     load_row20(&s.lc[t * kAR], gk);
     load_row20(&s.mc[t * kAR], gqk);
-    float al[kAR];
-#pragma unroll
-    for (int e = 0; e < kAR; ++e) al[e] = (e < kA && e <= dt) ? s.alpha[arow[e]] : 1.f;
     const float bt = s.beta[t];
     float rho = 1.f;  // g_t / g_{anc at depth e}
     float lrow[kAR], mrow[kAR];
@@ -318,85 +396,144 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
       const bool on = e < kA && e <= dt;
       mrow[e] = on ? rho * gqk[e] : 0.f;
       lrow[e] = (e < dt) ? bt * rho * gk[e] : 0.f;
-      if (on) rho *= al[e];
+      const float ae = (e < kA) ? s.alpha[arow[e]] : 1.f;
+      rho *= on ? ae : 1.f;
     }
     store_row20(&s.lc[t * kAR], lrow);
     store_row20(&s.mc[t * kAR], mrow);
   }
   __syncthreads();
+  if constexpr (BF16IN) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < KSS; ++kk) {
+        u16x8 f;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) f[x] = s.qlo[min(32 * kk + 8 * g4 + x, n - 1) * QS + j0 + 16 * mt + l16];
+        vt_hi[mt][kk] = __builtin_bit_cast(bf16x8, f);
+      }
+  }
   for (int t = tid; t < n; t += nthr) {
     const int dt = s.depth[t];
     int arow[kAR];
     load_anc20(&s.anc[t * kAR], arow);
     float w[kAR];
-    load_row20(&s.mc[t * kAR], w);
-    // right-looking solve of w (I + Lm) = Mm over the path, deepest ancestor first
+    load_row20(&s.mc[t * kAR], w);  // Mm row, zero beyond the depth
+    // right-looking solve of w (I + Lm) = Mm over the path, deepest ancestor first; for
+    // depths beyond dt, w is zero and arow is the root, whose Lm row is zero
 #pragma unroll
     for (int e2 = kA - 1; e2 >= 1; --e2) {
-      if (e2 <= dt) {
-        float lr[kAR];
-        load_row20(&s.lc[arow[e2] * kAR], lr);
+      float lr[kAR];
+      load_row20(&s.lc[arow[e2] * kAR], lr);
 #pragma unroll
-        for (int e = 0; e < e2; ++e) w[e] -= w[e2] * lr[e];
-      }
+      for (int e = 0; e < e2; ++e) w[e] -= w[e2] * lr[e];
     }
-    float w1[kAR], w2[kAR];
+    float w1[kAR];
+    uint16_t *dh = s.dhi() + t * DS, *dl = s.dlo() + t * DS;
 #pragma unroll
-    for (int e = 0; e < kAR; ++e) {
-      w1[e] = 0.f;
-      w2[e] = 0.f;
-      if (e < kA && e <= dt) {
-        const int sn = arow[e];
-        w1[e] = w[e] * s.beta[sn];
-        w2[e] = w1[e] * s.gamma[sn];
-      }
+    for (int v = 0; v < SM::SP / 8; ++v) {
+      reinterpret_cast<u32x4 *>(dh)[v] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4 *>(dl)[v] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // scatter -W2[t, anc at depth e] into column (slot) arow[e]; deepest first, so the
+    // zero entries beyond the depth (all aimed at the root's column) land before e = 0
+#pragma unroll
+    for (int e = kAR - 1; e >= 0; --e) {
+      const int sn = e < kA ? arow[e] : 0;
+      const bool on = e < kA && e <= dt;
+      w1[e] = on ? w[e] * s.beta[sn] : 0.f;
+      const float m2 = -w1[e] * s.gamma[sn];
+      const __bf16 hb = (__bf16)m2;
+      dh[sn] = __builtin_bit_cast(uint16_t, hb);
+      dl[sn] = __builtin_bit_cast(uint16_t, (__bf16)(m2 - (float)hb));
     }
     store_row20(&s.wc[t * kAR], w1);
-    store_row20(&s.mc[t * kAR], w2);
   }
   __syncthreads();
 
-  // ---- 3. effective queries qe_t = g_t q_t - sum_s W2[t,s] k_s, split hi/lo (bf16) ------
+  // ---- 3. effective queries: qe^T = g q^T - K^T W2^T (MFMA), split hi/lo (bf16) --------
   {
     uint16_t *qhi = BF16IN ? reinterpret_cast<uint16_t *>(s.q) : s.qhi;
-    constexpr int C8 = D / 8;
-    for (int it = tid; it < n * C8; it += nthr) {
-      const int t = it / C8, c = it % C8;
-      int a[kAR];
-      load_anc20(&s.anc[t * kAR], a);
-      float w2[kAR];
-      load_row20(&s.mc[t * kAR], w2);
-      const int dt = s.depth[t];
-      float x[8], y[8];
-      lds_row8(s.q + t * RS + 8 * c, x);
-      const float g = s.gamma[t];
+    const int ntiles = (n + 15) / 16;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] *= g;
+    for (int r = 0; r < (NIS + W - 1) / W; ++r) {
+      const int is = wave + r * W;  // d_k slice of 32 channels
+      if (is >= NIS) break;
+      if (!BF16IN || r > 0) {
 #pragma unroll
-      for (int e = 0; e < kA; ++e) {
-        if (e <= dt) {
-          lds_row8(s.kv + a[e] * RS + 8 * c, y);
+        for (int it = 0; it < 2; ++it)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] -= w2[e] * y[i];
+          for (int kk = 0; kk < KSS; ++kk)
+            gather_t<BF16IN>(gk, row_off, n, 32 * kk + 8 * g4, 32 * is + 16 * it + l16, kt_hi[it][kk], kt_lo[it][kk]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (nt >= ntiles) break;
+        const int t = 16 * nt + l16, tb = min(t, n - 1);
+        const float gt = s.gamma[tb];
+        f32x4 acc[2];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          float x[4];
+          const int i = 32 * is + 16 * it + 4 * g4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = gt * load_elem(s.q, (size_t)tb * RS + i + e);
+          acc[it] = f32x4{x[0], x[1], x[2], x[3]};
+        }
+#pragma unroll
+        for (int kk = 0; kk < KSS; ++kk) {
+          const bf16x8 bh = lds_frag(s.dhi() + tb * DS + 32 * kk + 8 * g4);
+          const bf16x8 bl = lds_frag(s.dlo() + tb * DS + 32 * kk + 8 * g4);
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            acc[it] = mfma(kt_hi[it][kk], bh, acc[it]);
+            acc[it] = mfma(kt_hi[it][kk], bl, acc[it]);
+            if constexpr (!BF16IN) acc[it] = mfma(kt_lo[it][kk], bh, acc[it]);
+          }
+        }
+        if (t < n) {
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int i = 32 * is + 16 * it + 4 * g4;
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 hv, lv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              hv[e] = (__bf16)acc[it][e];
+              lv[e] = (__bf16)(acc[it][e] - (float)hv[e]);
+            }
+            *reinterpret_cast<bf16x4 *>(qhi + t * QS + i) = hv;
+            *reinterpret_cast<bf16x4 *>(s.qlo + t * QS + i) = lv;
+          }
         }
       }
-      bf16x8 hi, lo;
-      split8(x, hi, lo);
-      *reinterpret_cast<bf16x8 *>(qhi + t * QS + 8 * c) = hi;
-      *reinterpret_cast<bf16x8 *>(s.qlo + t * QS + 8 * c) = lo;
     }
   }
   __syncthreads();
-  if constexpr (BF16IN) {  // k rows are dead: the v rows take their place
+  // the dense W1 (hi | lo) replaces -W2
+  for (int t = tid; t < n; t += nthr) {
+    int arow[kAR];
+    load_anc20(&s.anc[t * kAR], arow);
+    float w1[kAR];
+    load_row20(&s.wc[t * kAR], w1);
+    uint16_t *dh = s.dhi() + t * DS, *dl = s.dlo() + t * DS;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = tid + i * nthr;
-      if (c < n * CPR) *reinterpret_cast<u32x4 *>(s.kv + (c / CPR) * RS + (c % CPR) * CH) = vpre[i];
+    for (int v = 0; v < SM::SP / 8; ++v) {
+      reinterpret_cast<u32x4 *>(dh)[v] = u32x4{0u, 0u, 0u, 0u};
+      reinterpret_cast<u32x4 *>(dl)[v] = u32x4{0u, 0u, 0u, 0u};
     }
-    __syncthreads();
+#pragma unroll
+    for (int e = kAR - 1; e >= 0; --e) {
+      const int sn = e < kA ? arow[e] : 0;
+      const __bf16 hb = (__bf16)w1[e];
+      dh[sn] = __builtin_bit_cast(uint16_t, hb);
+      dl[sn] = __builtin_bit_cast(uint16_t, (__bf16)(w1[e] - (float)hb));
+    }
   }
+  __syncthreads();
 
-  // ---- 4. o^T = S0^T [qe] + V^T W1^T, node tile by node tile --------------------------
+  // ---- 4. o^T = S0^T [qe] + V^T W1^T (MFMA), node tile by node tile --------------------
   bf16x8 ahi[2][KS], alo[2][KS];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -408,11 +545,11 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
     }
   const uint16_t *qhi = BF16IN ? reinterpret_cast<const uint16_t *>(s.q) : s.qhi;
   const int ntiles = (n + 15) / 16;
-  const int jl = j0 + 4 * (lane >> 4);  // + 16*mt + r
+  const int jl = j0 + 4 * g4;  // + 16*mt + r
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     if (nt >= ntiles) break;
-    const int t = 16 * nt + (lane & 15);
+    const int t = 16 * nt + l16;
     const int tb = min(t, n - 1);
     f32x4 acc0[2], acc1[2];
 #pragma unroll
@@ -420,37 +557,10 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
       acc0[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // V^T W1^T on the vector ALUs (ancestor-sparse)
-    {
-      int a[kAR];
-      load_anc20(&s.anc[tb * kAR], a);
-      float w1[kAR];
-      load_row20(&s.wc[tb * kAR], w1);
-      const int dt = s.depth[tb];
-#pragma unroll
-      for (int e = 0; e < kA; ++e) {
-        if (e <= dt) {
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            float vv[4];
-            if constexpr (BF16IN) {
-              const uint2 u = *reinterpret_cast<const uint2 *>(s.kv + a[e] * RS + jl + 16 * mt);
-              vv[0] = __uint_as_float(u.x << 16); vv[1] = __uint_as_float(u.x & 0xffff0000u);
-              vv[2] = __uint_as_float(u.y << 16); vv[3] = __uint_as_float(u.y & 0xffff0000u);
-            } else {
-              const float4 u = *reinterpret_cast<const float4 *>(gv + row_off(a[e]) + jl + 16 * mt);
-              vv[0] = u.x; vv[1] = u.y; vv[2] = u.z; vv[3] = u.w;
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc0[mt][r] += w1[e] * vv[r];
-          }
-        }
-      }
-    }
-    // S0^T qe on MFMA: hi*hi into acc0, the two cross terms into acc1
+    // S0^T qe: hi*hi into acc0, the cross terms into acc1
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int col = 32 * ks + 8 * (lane >> 4);
+      const int col = 32 * ks + 8 * g4;
       const bf16x8 bhi = lds_frag(qhi + tb * QS + col);
       const bf16x8 blo = lds_frag(s.qlo + tb * QS + col);
 #pragma unroll
@@ -460,20 +570,30 @@ __global__ __launch_bounds__(64 * W, 2) void verify_kernel(VerifyParams p) {
         acc1[mt] = mfma(ahi[mt][ks], blo, acc1[mt]);
       }
     }
+    // V^T W1^T over the node axis
+#pragma unroll
+    for (int kk = 0; kk < KSS; ++kk) {
+      const bf16x8 wh = lds_frag(s.dhi() + tb * DS + 32 * kk + 8 * g4);
+      const bf16x8 wl = lds_frag(s.dlo() + tb * DS + 32 * kk + 8 * g4);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        acc0[mt] = mfma(vt_hi[mt][kk], wh, acc0[mt]);
+        acc1[mt] = mfma(vt_hi[mt][kk], wl, acc1[mt]);
+        if constexpr (!BF16IN) acc1[mt] = mfma(vt_lo[mt][kk], wh, acc1[mt]);
+      }
+    }
     if (t < n) {
       const size_t ob = row_off(t);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const int j = jl + 16 * mt;
-        const float o0 = acc0[mt][0] + acc1[mt][0], o1 = acc0[mt][1] + acc1[mt][1];
-        const float o2 = acc0[mt][2] + acc1[mt][2], o3 = acc0[mt][3] + acc1[mt][3];
+        const f32x4 o = acc0[mt] + acc1[mt];
         if (p.out_bf16) {
-          uint2 u;
-          u.x = (uint32_t)f32_to_bf16_bits(o0) | ((uint32_t)f32_to_bf16_bits(o1) << 16);
-          u.y = (uint32_t)f32_to_bf16_bits(o2) | ((uint32_t)f32_to_bf16_bits(o3) << 16);
-          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.o) + ob + j) = u;
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 ob4 = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+          *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.o) + ob + j) = ob4;
         } else {
-          *reinterpret_cast<float4 *>(static_cast<float *>(p.o) + ob + j) = make_float4(o0, o1, o2, o3);
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + ob + j) = o;
         }
       }
     }
