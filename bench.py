@@ -28,6 +28,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 256 << 20
+VERIFY_SRC = os.path.join(ROOT, "gdn_draft_tree_amd", "csrc", "verify_tree.hip")
+COUNTERS_MD = os.path.join(ROOT, "profiles", "verify_kernel_ragged_counters.md")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per verify launch from the committed counter summary, or None when there is
+    none for this workload or the kernel source has changed since the counters were taken
+    (the summary records the SHA-256 of the kernel source it measured)."""
+    import hashlib
+    import re
+    if workload != "ragged" or not os.path.exists(COUNTERS_MD):
+        return None
+    text = open(COUNTERS_MD).read()
+    src = hashlib.sha256(open(VERIFY_SRC, "rb").read()).hexdigest()
+    m_src = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    m_val = re.search(r"HBM bytes per verify launch: ([0-9]+)", text)
+    if not m_src or not m_val or m_src.group(1) != src:
+        return None
+    return int(m_val.group(1))
 
 
 def verify_bytes(cfg, n_nodes_total: int, out_elem: int) -> int:
@@ -77,6 +97,9 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated through (0: auto)")
     ap.add_argument("--cpu-reqs", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB copy kernel (dst = src * 1), the reference "
+                         "dispatch for scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
@@ -140,6 +163,12 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # whole-step throughput (no events inside the timed region)
     t0 = time.perf_counter()
@@ -172,7 +201,7 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.notes}", "B": cfg.B, "L": cfg.L, "H": cfg.H, "d": cfg.D,
                    "P": cfg.P, "K": cfg.K, "N": cfg.N, "io_dtype": cfg.dtype, "input_sets": nsets},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "verify_kernel",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload), "kernel": "verify_kernel",
                      "algorithmic_bytes": vbytes, "mean_us": t_verify},
         "kernels_us": {"build": t_build, "verify": t_verify, "accept_commit": t_commit},
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
