@@ -276,16 +276,20 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
                           s0r[j][ks][1][0], s0r[j][ks][1][1], s0r[j][ks][1][2], s0r[j][ks][1][3]};
       split8(x, s0h[j][ks], s0l[j][ks]);
     }
-  f32x4 pq[NT][JPW], pk[NT][JPW];
+  // P_Q is kept transposed (lane (g, t) holds P_Q[t][4 g + 0..3] of a channel tile: the C
+  // layout of S0^T Q^T), P_K in the node-major C layout (lane (g, c) holds P_K[4 g + 0..3][c]).
+  // Both come from the same registers: S0 fragments serve as the A operand of one product
+  // and the B operand of the other, and so do the row fragments.
+  f32x4 pqt[NT][JPW], pk[NT][JPW];
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int j = 0; j < JPW; ++j) {
-      pq[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      pqt[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
       pk[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (mt >= ntl) continue;
-    const int ra = min(16 * mt + l16, nl);
+    const int tme = 16 * mt + l16, ra = min(tme, nl);
     bf16x8 aqh[KS], aql[KS], akh[KS], akl[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -296,50 +300,51 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
     for (int j = 0; j < JPW; ++j)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        pq[mt][j] = mfma(aqh[ks], s0h[j][ks], pq[mt][j]);
-        pq[mt][j] = mfma(aqh[ks], s0l[j][ks], pq[mt][j]);
+        pqt[mt][j] = mfma(s0h[j][ks], aqh[ks], pqt[mt][j]);
+        pqt[mt][j] = mfma(s0l[j][ks], aqh[ks], pqt[mt][j]);
         pk[mt][j] = mfma(akh[ks], s0h[j][ks], pk[mt][j]);
         pk[mt][j] = mfma(akh[ks], s0l[j][ks], pk[mt][j]);
         if constexpr (!BF16IN) {
-          pq[mt][j] = mfma(aql[ks], s0h[j][ks], pq[mt][j]);
+          pqt[mt][j] = mfma(s0h[j][ks], aql[ks], pqt[mt][j]);
           pk[mt][j] = mfma(akl[ks], s0h[j][ks], pk[mt][j]);
         }
       }
-    // Gram tiles (mt, nt <= mt): tile pair index i = mt (mt + 1) / 2 + nt goes to wave 1 + i % 3
+    // Gram tiles, transposed: tile (nt <= mt) holds k_s . k_t and k_s . q_t with lane (g, t)
+    // owning node t = 16 mt + l16 and s = 16 nt + 4 g + 0..3.  Tile pair i = mt (mt + 1) / 2
+    // + nt goes to wave 1 + i % 3.
     if (wave == 0) continue;
-    unsigned long long mrow[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mrow[r] = s.mask[min(16 * mt + 4 * g4 + r, nl)];
+    const unsigned long long tmask = s.mask[ra];
+    const int trow = ra * kAR;
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
       if (1 + (mt * (mt + 1) / 2 + nt) % 3 != wave) continue;
-      const int sn = 16 * nt + l16, rb = min(sn, nl);
+      const int rb = min(16 * nt + l16, nl);
       f32x4 gk4 = {0.f, 0.f, 0.f, 0.f}, gq4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 bh, bl;
         row_frag<D, BF16IN>(krow, rb, 32 * ks + 8 * g4, bh, bl);
-        gk4 = mfma(akh[ks], bh, gk4);
-        gq4 = mfma(aqh[ks], bh, gq4);
+        gk4 = mfma(bh, akh[ks], gk4);
+        gq4 = mfma(bh, aqh[ks], gq4);
         if constexpr (!BF16IN) {
-          gk4 = mfma(akl[ks], bh, gk4);
-          gk4 = mfma(akh[ks], bl, gk4);
-          gq4 = mfma(aql[ks], bh, gq4);
-          gq4 = mfma(aqh[ks], bl, gq4);
+          gk4 = mfma(bl, akh[ks], gk4);
+          gk4 = mfma(bh, akl[ks], gk4);
+          gq4 = mfma(bl, aqh[ks], gq4);
+          gq4 = mfma(bh, aql[ks], gq4);
         }
       }
-      // keep the entries of ancestor pairs (s = sn an ancestor-or-self of row t), at depth(s)
-      const int es = __popcll(s.mask[rb]);
-      const int wsel = sn > 32, sh = (sn - 1) & 31;
+      // keep the entries of ancestor pairs at depth(s) = the number of t's ancestors in slots
+      // 1..s; everything else goes to the unused padding entries 17..19 of t's row (no branch)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mt + 4 * g4 + r;
-        const uint32_t word = wsel ? (uint32_t)(mrow[r] >> 32) : (uint32_t)mrow[r];
-        const bool anc = sn == 0 || ((word >> sh) & 1u);
-        if (t < n && sn <= t && es <= kMaxP && anc) {
-          s.mc[t * kAR + es] = gq4[r];
-          if (sn != t) s.lc[t * kAR + es] = gk4[r];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int sn = 16 * nt + 4 * g4 + i;
+        const unsigned long long below = sn >= 64 ? ~0ull : ((1ull << sn) - 1ull);
+        const int es = __popcll(tmask & below);
+        const bool anc = sn == 0 || ((tmask >> ((sn - 1) & 63)) & 1ull);
+        const bool keep = tme < n && sn <= tme && anc && es <= kMaxP;
+        const int dummy = trow + kMaxAnc + (i % 3);
+        s.mc[keep ? trow + es : dummy] = gq4[i];
+        s.lc[keep && sn != tme ? trow + es : dummy] = gk4[i];
       }
     }
   }
@@ -469,41 +474,40 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
   }
   lds_barrier();
 
-  // ---- 3. o = g P_Q + W1 V' for this wave's value channels, node tile by node tile ---------
+  // ---- 3. o^T = g P_Q^T + V'^T W1^T for this wave's value channels, node tile by node tile --
+  // A operand: V' (its registers are exactly the A layout of V'^T), B operand: W1 rows from
+  // LDS.  Lane (g, t) ends with o[t][16 jt + 4 g + 0..3]: one 8-byte (bf16) store per tile.
+  const size_t ostride = (size_t)p.H * D;
+  const size_t obase = (rowbase * p.H + h) * (size_t)D;
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
     if (mt >= ntl) break;
-    const float4 gm = *reinterpret_cast<const float4 *>(&s.gamma[16 * mt + 4 * g4]);
+    const int t = 16 * mt + l16, tr = min(t, nl);
+    const float gt = s.gamma[t];
     f32x4 acc[JPW];
 #pragma unroll
-    for (int j = 0; j < JPW; ++j) {
-      acc[j][0] = gm.x * pq[mt][j][0];
-      acc[j][1] = gm.y * pq[mt][j][1];
-      acc[j][2] = gm.z * pq[mt][j][2];
-      acc[j][3] = gm.w * pq[mt][j][3];
-    }
-    const int tr = min(16 * mt + l16, nl);
+    for (int j = 0; j < JPW; ++j) acc[j] = gt * pqt[mt][j];
 #pragma unroll
     for (int kk = 0; kk < KSS; ++kk) {
       const bf16x8 wh = frag16(w1h + tr * SP + 32 * kk + 8 * g4);
       const bf16x8 wl = frag16(w1l + tr * SP + 32 * kk + 8 * g4);
 #pragma unroll
       for (int j = 0; j < JPW; ++j) {
-        acc[j] = mfma(wh, vph[kk][j], acc[j]);
-        acc[j] = mfma(wh, vpl[kk][j], acc[j]);
-        acc[j] = mfma(wl, vph[kk][j], acc[j]);
+        acc[j] = mfma(vph[kk][j], wh, acc[j]);
+        acc[j] = mfma(vpl[kk][j], wh, acc[j]);
+        acc[j] = mfma(vph[kk][j], wl, acc[j]);
       }
     }
+    if (t < n) {
 #pragma unroll
-    for (int j = 0; j < JPW; ++j) {
-      const int ch = 16 * (JPW * wave + j) + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * mt + 4 * g4 + i;
-        if (t < n) {
-          const size_t oi = ((rowbase + t) * p.H + h) * (size_t)D + ch;
-          if (p.out_bf16) static_cast<__bf16 *>(p.o)[oi] = (__bf16)acc[j][i];
-          else static_cast<float *>(p.o)[oi] = acc[j][i];
+      for (int j = 0; j < JPW; ++j) {
+        const size_t oi = obase + (size_t)t * ostride + 16 * (JPW * wave + j) + 4 * g4;
+        if (p.out_bf16) {
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          const bf16x4 o4 = {(__bf16)acc[j][0], (__bf16)acc[j][1], (__bf16)acc[j][2], (__bf16)acc[j][3]};
+          *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.o) + oi) = o4;
+        } else {
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + oi) = acc[j];
         }
       }
     }
