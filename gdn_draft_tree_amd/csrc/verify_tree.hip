@@ -24,20 +24,22 @@
 // O(nodes * depth) work (Gram entries of ancestor pairs, the path solve) and one dense
 // node x node product W1 V'.
 //
-// Work decomposition: one workgroup of four waves per (layer, request, head), two
-// workgroups per CU.  Wave w owns value channels [32 w, 32 w + 32) (d = 128).  Per head:
-//  0. q, k, v rows go straight from HBM into LDS (buffer loads to LDS); tree masks and
-//     gates into LDS; each wave loads its S0 operand fragments into registers;
-//  1. every wave: P_Q = Q S0 and P_K = K S0 for its channels on MFMA (S0 split hi + lo
-//     bf16, rows exact in bf16), the C tiles kept in registers.  Waves 1-3 also compute the
-//     Gram tiles [Q; K] K^T of the lower node triangle on MFMA and keep the entries of
-//     ancestor pairs, compactly by the depth of the ancestor.  Wave 0 reads each node's
-//     ancestors from its bitmask and forms the path gate g_t;
+// Work decomposition: one workgroup of d / 16 waves per (layer, request, head), wave w owning
+// value channels [16 w, 16 w + 16); two workgroups per CU at d = 128 (16 waves per CU).
+// Per head:
+//  0. q, k, v rows go straight from HBM into LDS (buffer loads to LDS) and each wave loads
+//     its S0 operand fragments into registers.  Wave 0 owns the per-node tree work (lane l
+//     handles node l + 1): from its own early loads it checks the links, finds each node's
+//     ancestors in its bitmask and forms the path gate g_t while the bulk loads are in flight;
+//  1. every wave: P_Q = Q S0 and P_K = K S0 for its channels on MFMA (rows exact in bf16),
+//     the C tiles kept in registers; the Gram tiles [Q; K] K^T of the lower node triangle on
+//     MFMA, dealt over the waves, keeping the entries of ancestor pairs compactly by the depth
+//     of the ancestor;
 //  2. wave 0: one lane per node solves its path system and writes the node's W1 row (hi +
 //     lo bf16) to LDS; every wave: V' = V - g P_K for its channels (V enters the C tiles
 //     through a product with a 0/1 selector, so no transposed read of V is needed);
-//  3. every wave: o = g P_Q + W1 V' on MFMA (the C layout of V' is exactly the B-operand
-//     layout the product needs), then the stores.
+//  3. every wave: o^T = g P_Q^T + V'^T W1^T on MFMA (the C layout of V' is exactly the
+//     operand layout the product needs), then the stores.
 // Three barriers per head.
 
 #include <type_traits>
@@ -62,7 +64,9 @@ struct VerifySmem {
   static constexpr int RM = (16 * NT < kMaxSlots) ? 16 * NT : kMaxSlots;   // node rows held
   static constexpr int ROWB = (RM * D * (int)sizeof(T) + 1023) / 1024 * 1024;  // whole 1 KiB loads
   static constexpr int SP = (16 * NT + 31) / 32 * 32;  // node (contraction) axis of W1 V'
-  static constexpr int W1B = 2 * RM * SP * 2;          // W1 rows, hi and lo bf16
+  // W1 row stride in bf16 elements: 16 rows read at one column start in distinct banks
+  static constexpr int SPW = SP + 8;
+  static constexpr int W1B = 2 * RM * SPW * 2;         // W1 rows, hi and lo bf16
   static constexpr int QKB = (2 * ROWB > W1B) ? 2 * ROWB : W1B;
   alignas(16) unsigned char qk[QKB];   // q rows, k rows; W1 after phase 1
   alignas(16) unsigned char vrow[ROWB];
@@ -70,7 +74,8 @@ struct VerifySmem {
   alignas(16) float mc[RM * kAR];      // q_t . k_s for s an ancestor-or-self of t, at depth(s)
   alignas(16) unsigned long long mask[RM];
   alignas(16) float gamma[16 * NT];    // path gate; zero past the node count
-  float alpha[RM], beta[RM];
+  float beta[RM];                      // b per node
+  float cwl[kMaxAnc][64];              // wave 0's W1 weights, per depth and lane
   int bad;
 };
 
@@ -143,23 +148,33 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <int D, bool BF16IN, int NT>
-__global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParams p) {
+__device__ __forceinline__ float bperm_f32(int lane_src, float x) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(lane_src << 2, __float_as_int(x)));
+}
+__device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// S0LO: S0 enters the products as hi + lo bf16 (fp32 outputs); without it S0 is rounded to
+// bf16 once, which for bf16 outputs stays below the outputs' own rounding.
+template <int D, bool BF16IN, int NT, bool S0LO>
+__global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void verify_kernel(VerifyParams p) {
   typedef VerifySmem<D, BF16IN, NT> SM;
   typedef typename SM::T T;
-  constexpr int RM = SM::RM, SP = SM::SP;
+  constexpr int RM = SM::RM, SP = SM::SP, SPW = SM::SPW;
   constexpr int CH = 16 / (int)sizeof(T), CPR = D / CH;
   constexpr int KS = D / 32;               // MFMA k-steps over d_k
   constexpr int KSS = SP / 32;             // MFMA k-steps over the node axis
-  constexpr int JPW = D / 64;              // 16-channel value tiles per wave
-  constexpr int QMAX = SM::ROWB / 1024;    // 1 KiB row-load instructions per matrix
-  constexpr int NS0 = JPW * KS * 2;        // S0 fragment loads per lane
+  constexpr int NW = D / 16;               // waves, one 16-channel value tile each
+  constexpr int NTH = 64 * NW;             // threads
+  constexpr int QMAX = SM::ROWB / 1024;    // 1 KiB row chunks per matrix
+  constexpr int CPW = (3 * QMAX + NW - 1) / NW;  // row chunks per wave
+  constexpr int NS0 = KS * 2;              // S0 fragment loads per lane
   __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = blockIdx.x;  // (layer, request, head)
-  const int h = hh % p.H, lb = hh / p.H, b = lb % p.B;
+  const int u = blockIdx.x;  // (layer, request, head)
+  const int h = u % p.H, lb = u / p.H, b = lb % p.B;
   // n_nodes is read-only here: a scalar load
   const int32_t __attribute__((address_space(4))) *nn_c =
       (const int32_t __attribute__((address_space(4))) *)p.n_nodes;
@@ -169,37 +184,56 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
   const int ntl = (n + 15) / 16;  // node tiles in use
   const size_t rowbase = (size_t)lb * p.R;
   const size_t rstride = (size_t)p.H * D;  // elements between consecutive slots of one head
-  const T *gq = static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D;
-  const T *gk = static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D;
-  const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
   const T *qrow = reinterpret_cast<const T *>(s.qk);
   const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
   const T *vrow = reinterpret_cast<const T *>(s.vrow);
   uint16_t *w1h = reinterpret_cast<uint16_t *>(s.qk);
-  uint16_t *w1l = w1h + RM * SP;
+  uint16_t *w1l = w1h + RM * SPW;
 
   // ---- 0. loads ----------------------------------------------------------------------
-  // tree masks, gates and parents: raw loads, converted only after every HBM load is issued
-  // (unconditional loads at a clamped slot, so that no branch forces an early wait)
-  const int tcl = min(tid, nl);
-  const unsigned long long my_mask = p.anc[(size_t)b * p.R + tcl];
-  const T my_alpha = static_cast<const T *>(p.alpha)[(rowbase + tcl) * p.H + h];
-  const T my_beta = static_cast<const T *>(p.beta)[(rowbase + tcl) * p.H + h];
-  int my_par = -1;
-  if (wave == 0 && lane + 1 < n) my_par = p.parent[(size_t)b * p.R + lane + 1];
+  // Constant LDS stores first: issued before any load into LDS, they never wait for one.
+  static_assert(RM * kAR / 4 <= 2 * NTH, "compact Gram rows: two stores per thread");
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int i = tid + NTH * x;
+    if (i < RM * kAR / 4) {
+      reinterpret_cast<float4 *>(s.lc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      reinterpret_cast<float4 *>(s.mc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if (tid >= n && tid < 16 * NT) s.gamma[tid] = 0.f;
+  if (tid == 0) s.bad = 0;
+  // Wave 0 owns the per-node tree work: lane l handles node t = l + 1 (the root is trivial)
+  // and holds the gates of slot l for the other lanes.  These small loads go first, so wave 0
+  // can wait for them alone (memory counters complete in order) and finish its per-node
+  // prologue while the bulk loads below are still in flight.  All loads are unconditional at
+  // clamped slots, so no branch forces an early wait and the counters stay static.
+  const int t_me = lane + 1;
+  const size_t tb = (size_t)b * p.R;
+  const int tn = min(t_me, nl), ts = min(lane, nl);
+  const unsigned long long w_mask = p.anc[tb + tn];
+  const int w_par = p.parent[tb + tn];
+  const T w_a0 = static_cast<const T *>(p.alpha)[(rowbase + ts) * p.H + h];
+  const T w_b0 = static_cast<const T *>(p.beta)[(rowbase + ts) * p.H + h];
+  const T w_a1 = static_cast<const T *>(p.alpha)[(rowbase + tn) * p.H + h];
+  const T w_b1 = static_cast<const T *>(p.beta)[(rowbase + tn) * p.H + h];
+  const unsigned long long my_mask = p.anc[tb + min(tid, nl)];  // -> LDS for the Gram scatter
   __builtin_amdgcn_sched_barrier(0);
   {
     // q, k, v rows -> LDS: each wave instruction fills 64 consecutive 16-byte chunks; lane l
-    // of instruction qi holds physical chunk 64 qi + l and fetches the logical chunk that the
-    // swizzle places there.  Chunks of rows past the node count fetch row n-1 (never used).
+    // of chunk qi holds physical chunk 64 qi + l and fetches the logical chunk that the
+    // swizzle places there.  Rows past the node count fetch row n-1 (never used).  Every wave
+    // issues the same number of loads (the last chunk repeated, rewriting the same bytes).
+    const T *gq = static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D;
+    const T *gk = static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D;
+    const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
     const int nb = (int)(n * rstride * sizeof(T));
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)gq, 0, nb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)gk, 0, nb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)gv, 0, nb, 0x00020000);
 #pragma unroll
-    for (int x = 0; x < (3 * QMAX + 3) / 4; ++x) {
-      const int item = wave + 4 * x;
-      if (item >= 3 * QMAX) break;
+    for (int x = 0; x < CPW; ++x) {
+      const int item = min(wave + NW * x, 3 * QMAX - 1);
       const int mat = item / QMAX, qi = item % QMAX;
       const int pc = 64 * qi + lane, r = pc / CPR, c = (pc % CPR) ^ (r & (CPR - 1));
       const unsigned off = (unsigned)((min(r, nl) * (int)rstride + c * CH) * (int)sizeof(T));
@@ -209,85 +243,94 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  // S0 operand fragments of this wave's value channels (B operand of X S0: lane (g, c) holds
-  // S0[32 ks + 8 g + 0..7][channel c], contiguous in the [d_v][d_k] state layout).
-  f32x4 s0r[JPW][KS][2];
-#pragma unroll
-  for (int j = 0; j < JPW; ++j) {
-    const float *sr = p.state + ((size_t)hh * D + 16 * (JPW * wave + j) + l16) * D + 8 * g4;
+  // S0 operand fragments of this wave's value channels: lane (g, c) holds
+  // S0[32 ks + 8 g + 0..7][channel 16 wave + c], contiguous in the [d_v][d_k] state layout.
+  f32x4 s0r[KS][2];
+  {
+    const float *sr = p.state + ((size_t)u * D + 16 * wave + l16) * D + 8 * g4;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s0r[j][ks][0] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks);
-      s0r[j][ks][1] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks + 4);
+      s0r[ks][0] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks);
+      s0r[ks][1] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks + 4);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (tid < n) {
-    s.mask[tid] = my_mask;
-    s.alpha[tid] = load_elem(&my_alpha, 0);
-    s.beta[tid] = load_elem(&my_beta, 0);
-  } else if (tid < 16 * NT) {
-    s.gamma[tid] = 0.f;
-  }
-  for (int i = tid; i < RM * kAR / 4; i += 256) {
-    reinterpret_cast<float4 *>(s.lc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    reinterpret_cast<float4 *>(s.mc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (tid == 0) s.bad = 0;
-  // the row loads (issued before the S0 loads) have landed; S0 may still be in flight
-  __builtin_amdgcn_s_waitcnt(0x0070 | ((NS0 & 15) | ((NS0 >> 4) << 14)));  // vmcnt(NS0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  if (tid < n) s.mask[tid] = my_mask;
 
-  // ---- 1a. wave 0: per node, ancestors from the bitmask, depth, path gate ---------------
-  // Lane l of wave 0 owns node l + 1 (through phase 2); the root is handled by wave 1.
-  const int t_me = lane + 1;
+  // ---- 0b. wave 0, per node: link check, ancestors by depth, path gate, W1 weights -------
   uint32_t ancw[5] = {0u, 0u, 0u, 0u, 0u};  // slot of the ancestor at depth e, byte e
   int d_me = 0;
-  if (wave == 0 && t_me < n) {
-    const unsigned long long m = s.mask[t_me];
+  if (wave == 0) {
+    const bool tv = t_me < n;
+    const float a0 = to_f32(w_a0), b0 = to_f32(w_b0), a1 = to_f32(w_a1), b1 = to_f32(w_b1);
+    const unsigned long long m = w_mask;
     d_me = __popcll(m);
-    const bool pin = my_par >= 0 && my_par < t_me;
-    const bool ok = d_me <= kMaxP && pin && m == (s.mask[pin ? my_par : 0] | (1ull << (t_me - 1)));
-    if (!ok) s.bad = 1;
+    // the parent's mask is the node mask held by lane parent - 1 (the root's mask is zero)
+    const int pl = min(max(w_par - 1, 0), 63);
+    const uint32_t pm_lo = (uint32_t)__builtin_amdgcn_ds_bpermute(pl << 2, (int)(uint32_t)m);
+    const uint32_t pm_hi = (uint32_t)__builtin_amdgcn_ds_bpermute(pl << 2, (int)(uint32_t)(m >> 32));
+    const unsigned long long pm = w_par == 0 ? 0ull : (((unsigned long long)pm_hi << 32) | pm_lo);
+    const bool ok = d_me <= kMaxP && w_par >= 0 && w_par < t_me && m == (pm | (1ull << (t_me - 1)));
+    if (tv && !ok) s.bad = 1;
     d_me = min(d_me, kMaxP);
+    float bet[kMaxAnc], alp[kMaxAnc];  // b and a of the ancestor at depth e
+    alp[0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a0), 0));
+    bet[0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b0), 0));
+    float g = alp[0];
     unsigned long long mm = m;
-    float g = s.alpha[0];
 #pragma unroll
     for (int e = 1; e <= kMaxP; ++e) {
       const int a = min(__ffsll((long long)mm), nl);  // 0 (the root) beyond the depth
       mm &= mm - 1;
       ancw[e >> 2] |= (uint32_t)a << (8 * (e & 3));
-      const float ae = s.alpha[a];
-      g *= (e <= d_me) ? ae : 1.f;
+      // gates of slot a: held by lane a, except t itself (slot 64 has no lane)
+      float av = bperm_f32(a, a0), bv = bperm_f32(a, b0);
+      if (a == t_me) { av = a1; bv = b1; }
+      alp[e] = av;
+      bet[e] = bv;
+      g *= (e <= d_me) ? av : 1.f;
     }
-    s.gamma[t_me] = g;
-  } else if (wave == 1 && lane == 0) {
-    s.gamma[0] = s.alpha[0];
-    if (s.mask[0] != 0ull) s.bad = 1;
+    // W1[t, anc e] = cw[e] z[e] with cw[e] = b_{anc e} g_t / g_{anc e}
+    float rr = 1.f;
+#pragma unroll
+    for (int e = kMaxP; e >= 0; --e) {
+      s.cwl[e][lane] = (e <= d_me) ? rr * bet[e] : 0.f;
+      rr *= (e <= d_me) ? alp[e] : 1.f;
+    }
+    if (tv) {
+      s.gamma[t_me] = g;
+      s.beta[t_me] = b1;
+    }
+    if (lane == 0) {
+      s.gamma[0] = alp[0];
+      s.beta[0] = bet[0];
+    }
   }
+  // the row loads (issued before the S0 loads) have landed; S0 may still be in flight
+  __builtin_amdgcn_s_waitcnt(0x0070 | ((NS0 & 15) | ((NS0 >> 4) << 14)));  // vmcnt(NS0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
 
-  // ---- 1b. P_Q = Q S0, P_K = K S0 (all waves); Gram tiles (waves 1-3) ---------------------
-  bf16x8 s0h[JPW][KS], s0l[JPW][KS];
+  // ---- 1. P_Q = Q S0, P_K = K S0 (all waves); Gram tiles -------------------------------
+  if (wave == 1 && lane == 0 && s.mask[0] != 0ull) s.bad = 1;  // the root has no ancestors
+  bf16x8 s0h[KS], s0l[KS];
 #pragma unroll
-  for (int j = 0; j < JPW; ++j)
+  for (int ks = 0; ks < KS; ++ks) {
+    const float x[8] = {s0r[ks][0][0], s0r[ks][0][1], s0r[ks][0][2], s0r[ks][0][3],
+                        s0r[ks][1][0], s0r[ks][1][1], s0r[ks][1][2], s0r[ks][1][3]};
+    if constexpr (S0LO) {
+      split8(x, s0h[ks], s0l[ks]);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float x[8] = {s0r[j][ks][0][0], s0r[j][ks][0][1], s0r[j][ks][0][2], s0r[j][ks][0][3],
-                          s0r[j][ks][1][0], s0r[j][ks][1][1], s0r[j][ks][1][2], s0r[j][ks][1][3]};
-      split8(x, s0h[j][ks], s0l[j][ks]);
+      for (int e = 0; e < 8; ++e) s0h[ks][e] = (__bf16)x[e];
     }
-  // P_Q is kept transposed (lane (g, t) holds P_Q[t][4 g + 0..3] of a channel tile: the C
-  // layout of S0^T Q^T), P_K in the node-major C layout (lane (g, c) holds P_K[4 g + 0..3][c]).
-  // Both come from the same registers: S0 fragments serve as the A operand of one product
-  // and the B operand of the other, and so do the row fragments.
-  f32x4 pqt[NT][JPW], pk[NT][JPW];
+  }
+  // P_Q is kept transposed (lane (g, t) holds P_Q[t][16 wave + 4 g + 0..3]: the C layout of
+  // S0^T Q^T), P_K node-major (lane (g, c) holds P_K[4 g + 0..3][16 wave + c]).  Both come
+  // from the same registers: the S0 fragments are the A operand of one product and the B
+  // operand of the other, and so are the row fragments.
+  f32x4 pqt[NT], pk[NT];  // tiles past the node count are never read
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
-#pragma unroll
-    for (int j = 0; j < JPW; ++j) {
-      pqt[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      pk[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     if (mt >= ntl) continue;
     const int tme = 16 * mt + l16, ra = min(tme, nl);
     bf16x8 aqh[KS], aql[KS], akh[KS], akl[KS];
@@ -296,28 +339,34 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
       row_frag<D, BF16IN>(qrow, ra, 32 * ks + 8 * g4, aqh[ks], aql[ks]);
       row_frag<D, BF16IN>(krow, ra, 32 * ks + 8 * g4, akh[ks], akl[ks]);
     }
+    pqt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pk[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < JPW; ++j)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        pqt[mt][j] = mfma(s0h[j][ks], aqh[ks], pqt[mt][j]);
-        pqt[mt][j] = mfma(s0l[j][ks], aqh[ks], pqt[mt][j]);
-        pk[mt][j] = mfma(akh[ks], s0h[j][ks], pk[mt][j]);
-        pk[mt][j] = mfma(akh[ks], s0l[j][ks], pk[mt][j]);
-        if constexpr (!BF16IN) {
-          pqt[mt][j] = mfma(s0h[j][ks], aql[ks], pqt[mt][j]);
-          pk[mt][j] = mfma(akl[ks], s0h[j][ks], pk[mt][j]);
-        }
+    for (int ks = 0; ks < KS; ++ks) {
+      pqt[mt] = mfma(s0h[ks], aqh[ks], pqt[mt]);
+      pk[mt] = mfma(akh[ks], s0h[ks], pk[mt]);
+      if constexpr (S0LO) {
+        pqt[mt] = mfma(s0l[ks], aqh[ks], pqt[mt]);
+        pk[mt] = mfma(akh[ks], s0l[ks], pk[mt]);
       }
-    // Gram tiles, transposed: tile (nt <= mt) holds k_s . k_t and k_s . q_t with lane (g, t)
-    // owning node t = 16 mt + l16 and s = 16 nt + 4 g + 0..3.  Tile pair i = mt (mt + 1) / 2
-    // + nt goes to wave 1 + i % 3.
-    if (wave == 0) continue;
+      if constexpr (!BF16IN) {
+        pqt[mt] = mfma(s0h[ks], aql[ks], pqt[mt]);
+        pk[mt] = mfma(akl[ks], s0h[ks], pk[mt]);
+      }
+    }
+    // Gram tiles (mt, nt <= mt), transposed, computed with the row fragments just loaded: lane
+    // (g, t) owns node t = 16 mt + l16 and gets k_s . k_t and k_s . q_t for s = 16 nt + 4 g +
+    // 0..3.  Tile pair i = mt (mt + 1) / 2 + nt goes to wave NW - 1 - i % NW.  Entries of
+    // ancestor pairs are kept at depth(s) = (t's ancestors-or-self in slots 0..s) - 1 (the k.k
+    // ones times b_t, the factor the path solve applies); the rest go to padding entries 17..19.
     const unsigned long long tmask = s.mask[ra];
+    const unsigned long long aset = (tmask << 1) | 1ull;  // slot s <= 63 -> bit s; root in
+    const float bt = s.beta[ra];
     const int trow = ra * kAR;
+    const bool rowok = tme < n;
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
-      if (1 + (mt * (mt + 1) / 2 + nt) % 3 != wave) continue;
+      if (wave != NW - 1 - (mt * (mt + 1) / 2 + nt) % NW) continue;
       const int rb = min(16 * nt + l16, nl);
       f32x4 gk4 = {0.f, 0.f, 0.f, 0.f}, gq4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -333,129 +382,126 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
           gq4 = mfma(bh, aql[ks], gq4);
         }
       }
-      // keep the entries of ancestor pairs at depth(s) = the number of t's ancestors in slots
-      // 1..s; everything else goes to the unused padding entries 17..19 of t's row (no branch)
+      const int sn0 = 16 * nt + 4 * g4;
+      uint32_t bits;  // ancestor flags of slots sn0 .. sn0 + 3
+      int cbelow;     // t's ancestors-or-self in slots 0 .. sn0 - 1
+      if (nt < 4) {
+        bits = (uint32_t)(aset >> sn0) & 0xfu;
+        cbelow = __popcll(aset & ((1ull << sn0) - 1ull));
+      } else {  // slots 64..79: only slot 64, and only as t itself
+        bits = (g4 == 0) ? (uint32_t)(tmask >> 63) : 0u;
+        cbelow = __popcll(aset);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sn = 16 * nt + 4 * g4 + i;
-        const unsigned long long below = sn >= 64 ? ~0ull : ((1ull << sn) - 1ull);
-        const int es = __popcll(tmask & below);
-        const bool anc = sn == 0 || ((tmask >> ((sn - 1) & 63)) & 1ull);
-        const bool keep = tme < n && sn <= tme && anc && es <= kMaxP;
-        const int dummy = trow + kMaxAnc + (i % 3);
-        s.mc[keep ? trow + es : dummy] = gq4[i];
-        s.lc[keep && sn != tme ? trow + es : dummy] = gk4[i];
+      for (int r = 0; r < 4; ++r) {
+        const int sn = sn0 + r;
+        const int es = cbelow + __popc(bits & ((2u << r) - 1u)) - 1;
+        const bool keep = rowok && ((bits >> r) & 1u) && sn <= tme && es <= kMaxP;
+        const int dummy = trow + kMaxAnc + (r % 3);
+        s.mc[keep ? trow + es : dummy] = gq4[r];
+        s.lc[keep && sn != tme ? trow + es : dummy] = gk4[r] * bt;
       }
     }
   }
   lds_barrier();
+  const bool bad = s.bad != 0;
 
-  if (s.bad) {  // an inconsistent tree: NaN outputs for this request
-    for (int c = tid; c < n * D; c += 256) {
-      const size_t oi = ((rowbase + c / D) * p.H + h) * (size_t)D + c % D;
-      if (p.out_bf16) static_cast<uint16_t *>(p.o)[oi] = 0x7fc0;
-      else static_cast<float *>(p.o)[oi] = __builtin_nanf("");
-    }
-    return;
-  }
-
-  // ---- 2a. V' = V - g P_K for this wave's channels, packed as the B operand of W1 V' ------
+  // ---- 2a. V' = V - g P_K for this wave's channels, packed as the A operand of V'^T W1^T ---
   // V enters the C tiles through one product with a 0/1 selector B[k][c] = (k == c + off):
   // the A operand is a plain row fragment of V, so V is never read transposed.
-  bf16x8 vph[KSS][JPW], vpl[KSS][JPW];
+  bf16x8 vph[KSS], vpl[KSS];
   {
-    bf16x8 isel[JPW];
+    bf16x8 isel;
+    const int off = 16 * (wave & 1);
 #pragma unroll
-    for (int j = 0; j < JPW; ++j) {
-      const int off = 16 * ((JPW * wave + j) & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) isel[j][e] = (__bf16)((8 * g4 + e == l16 + off) ? 1.f : 0.f);
-    }
-    const int vcol = 32 * ((JPW * wave) >> 1) + 8 * g4;  // this wave's 32-channel chunk
+    for (int e = 0; e < 8; ++e) isel[e] = (__bf16)((8 * g4 + e == l16 + off) ? 1.f : 0.f);
+    const int vcol = 32 * (wave >> 1) + 8 * g4;  // this wave's 32-channel chunk
 #pragma unroll
     for (int mt = 0; mt < 2 * KSS; ++mt) {
-      f32x4 vp[JPW];
-#pragma unroll
-      for (int j = 0; j < JPW; ++j) vp[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 vp = {0.f, 0.f, 0.f, 0.f};
       if (mt < NT && mt < ntl) {
         const int mc_ = mt < NT ? mt : NT - 1;  // (static index; mt < NT here)
         const float4 gm = *reinterpret_cast<const float4 *>(&s.gamma[16 * mt + 4 * g4]);
         bf16x8 avh, avl;
         row_frag<D, BF16IN>(vrow, min(16 * mt + l16, nl), vcol, avh, avl);
-#pragma unroll
-        for (int j = 0; j < JPW; ++j) {
-          vp[j][0] = -gm.x * pk[mc_][j][0];
-          vp[j][1] = -gm.y * pk[mc_][j][1];
-          vp[j][2] = -gm.z * pk[mc_][j][2];
-          vp[j][3] = -gm.w * pk[mc_][j][3];
-          vp[j] = mfma(avh, isel[j], vp[j]);
-          if constexpr (!BF16IN) vp[j] = mfma(avl, isel[j], vp[j]);
-        }
+        vp[0] = -gm.x * pk[mc_][0];
+        vp[1] = -gm.y * pk[mc_][1];
+        vp[2] = -gm.z * pk[mc_][2];
+        vp[3] = -gm.w * pk[mc_][3];
+        vp = mfma(avh, isel, vp);
+        if constexpr (!BF16IN) vp = mfma(avl, isel, vp);
       }
 #pragma unroll
-      for (int j = 0; j < JPW; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const __bf16 hv = (__bf16)vp[j][i];
-          vph[mt >> 1][j][4 * (mt & 1) + i] = hv;
-          vpl[mt >> 1][j][4 * (mt & 1) + i] = (__bf16)(vp[j][i] - (float)hv);
-        }
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 hv = (__bf16)vp[i];
+        vph[mt >> 1][4 * (mt & 1) + i] = hv;
+        vpl[mt >> 1][4 * (mt & 1) + i] = (__bf16)(vp[i] - (float)hv);
+      }
     }
   }
 
-  // ---- 2b. path solve, one lane of wave 0 per node; the root by wave 1 ------------------
+  // ---- 2b. path solve, one lane of wave 0 per node; the root's row by wave 1 -------------
   if (wave == 0) {
-    const int dmax = wave_max_i32(t_me < n ? d_me : 0);
-    if (t_me < n) {
-      const int t = t_me;
-      auto anc_at = [&](int e) -> int { return (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu); };
-      float z[kAR];  // right-hand side q_t . k_{anc e}; zero beyond the depth
+    const bool tv = t_me < n;
+    const int t = tn;
+    const int dmax = wave_max_i32(tv ? d_me : 0);
+    auto anc_at = [&](int e) -> int { return (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu); };
+    // this node's W1 row is cleared first (up to its 32-node chunk, the last one the output
+    // product reads), so the stores overlap the solve's loads
+    uint4 *rh = reinterpret_cast<uint4 *>(w1h + t * SPW);
+    uint4 *rl = reinterpret_cast<uint4 *>(w1l + t * SPW);
+    if (tv) {
 #pragma unroll
-      for (int v = 0; v < kAR / 4; ++v) {
-        const float4 x = reinterpret_cast<const float4 *>(&s.mc[t * kAR])[v];
-        z[4 * v] = x.x; z[4 * v + 1] = x.y; z[4 * v + 2] = x.z; z[4 * v + 3] = x.w;
+      for (int v = 0; v < SP / 8; ++v) {
+        if (v < 4 * (t / 32 + 1)) {
+          rh[v] = make_uint4(0u, 0u, 0u, 0u);
+          rl[v] = make_uint4(0u, 0u, 0u, 0u);
+        }
       }
-      float bet[kMaxAnc];
+    }
+    float z[kAR];  // right-hand side q_t . k_{anc e}; zero beyond the depth
 #pragma unroll
-      for (int e = 0; e <= kMaxP; ++e) bet[e] = s.beta[anc_at(e)];
-      // deepest ancestor first; beyond a lane's depth z is zero and the ancestor slot is the
-      // root, so those steps change nothing.  Steps deeper than every lane are skipped.
+    for (int v = 0; v < kAR / 4; ++v) {
+      const float4 x = reinterpret_cast<const float4 *>(&s.mc[t * kAR])[v];
+      z[4 * v] = x.x; z[4 * v + 1] = x.y; z[4 * v + 2] = x.z; z[4 * v + 3] = x.w;
+    }
+    // deepest ancestor first, two steps per group with the group's rows loaded together.
+    // Beyond a lane's depth z is zero and the ancestor slot is the root, so those steps
+    // change nothing; groups deeper than every lane are skipped.
 #pragma unroll
-      for (int e2 = kMaxP; e2 >= 1; --e2) {
-        if (e2 > dmax) continue;
-        const float c = z[e2] * bet[e2];
+    for (int grp = kMaxP / 2 - 1; grp >= 0; --grp) {
+      if (2 * grp + 1 > dmax) continue;
+      float4 rw[2][4];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e2 = 2 * grp + 2 - r;
         const float4 *row = reinterpret_cast<const float4 *>(&s.lc[anc_at(e2) * kAR]);
 #pragma unroll
+        for (int v = 0; v < (e2 + 3) / 4; ++v) rw[r][v] = row[v];
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int e2 = 2 * grp + 2 - r;
+        const float c = z[e2];  // the b of the step is folded into the stored k.k entries
+#pragma unroll
         for (int v = 0; v < (e2 + 3) / 4; ++v) {
-          const float4 x = row[v];
-          const float xs[4] = {x.x, x.y, x.z, x.w};
+          const float xs[4] = {rw[r][v].x, rw[r][v].y, rw[r][v].z, rw[r][v].w};
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (4 * v + i < e2) z[4 * v + i] -= c * xs[i];
         }
       }
-      // W1[t, anc e] = (g_t / g_{anc e}) b_{anc e} z[e]; the gate ratio is the product of the
-      // gates strictly below depth e on the path
-      uint4 *rh = reinterpret_cast<uint4 *>(w1h + t * SP);
-      uint4 *rl = reinterpret_cast<uint4 *>(w1l + t * SP);
+    }
 #pragma unroll
-      for (int v = 0; v < SP / 8; ++v) {
-        rh[v] = make_uint4(0u, 0u, 0u, 0u);
-        rl[v] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      float rr = 1.f;
-#pragma unroll
-      for (int e = kMaxP; e >= 0; --e) {
-        if (e <= d_me) {
-          const int ae = anc_at(e);
-          const float w = rr * bet[e] * z[e];
-          const __bf16 hv = (__bf16)w;
-          const __bf16 lv = (__bf16)(w - (float)hv);
-          const int pos = t * SP + w1_pos(ae);
-          w1h[pos] = __builtin_bit_cast(uint16_t, hv);
-          w1l[pos] = __builtin_bit_cast(uint16_t, lv);
-          rr *= s.alpha[ae];
-        }
+    for (int e = 0; e <= kMaxP; ++e) {
+      if (e > dmax) break;
+      if (tv && e <= d_me) {
+        const float w = s.cwl[e][lane] * z[e];
+        const __bf16 hv = (__bf16)w;
+        const __bf16 lv = (__bf16)(w - (float)hv);
+        const int pos = t * SPW + w1_pos(anc_at(e));
+        w1h[pos] = __builtin_bit_cast(uint16_t, hv);
+        w1l[pos] = __builtin_bit_cast(uint16_t, lv);
       }
     }
   } else if (wave == 1 && lane == 0) {
@@ -463,7 +509,7 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
     uint4 *rh = reinterpret_cast<uint4 *>(w1h);
     uint4 *rl = reinterpret_cast<uint4 *>(w1l);
 #pragma unroll
-    for (int v = 0; v < SP / 8; ++v) {
+    for (int v = 0; v < 4; ++v) {
       rh[v] = make_uint4(0u, 0u, 0u, 0u);
       rl[v] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -476,39 +522,42 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
 
   // ---- 3. o^T = g P_Q^T + V'^T W1^T for this wave's value channels, node tile by node tile --
   // A operand: V' (its registers are exactly the A layout of V'^T), B operand: W1 rows from
-  // LDS.  Lane (g, t) ends with o[t][16 jt + 4 g + 0..3]: one 8-byte (bf16) store per tile.
-  const size_t ostride = (size_t)p.H * D;
-  const size_t obase = (rowbase * p.H + h) * (size_t)D;
+  // LDS; W1 is zero above the diagonal, so node chunks past the tile are skipped.  Lane
+  // (g, t) ends with o[t][16 wave + 4 g + 0..3]: one 8-byte (bf16) store per tile, through a
+  // buffer whose range ends at the last node, so rows past the node count are dropped.  An
+  // inconsistent tree gives NaN outputs.
+  {
+    const int oes = p.out_bf16 ? 2 : 4;
+    const unsigned ostride = (unsigned)(p.H * D * oes);
+    char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
+    const int orange = (nl * p.H * D + D) * oes;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
 #pragma unroll
-  for (int mt = 0; mt < NT; ++mt) {
-    if (mt >= ntl) break;
-    const int t = 16 * mt + l16, tr = min(t, nl);
-    const float gt = s.gamma[t];
-    f32x4 acc[JPW];
+    for (int mt = 0; mt < NT; ++mt) {
+      if (mt >= ntl) break;
+      const int t = 16 * mt + l16, tr = min(t, nl);
+      const float gt = s.gamma[t];
+      f32x4 acc = gt * pqt[mt];
 #pragma unroll
-    for (int j = 0; j < JPW; ++j) acc[j] = gt * pqt[mt][j];
-#pragma unroll
-    for (int kk = 0; kk < KSS; ++kk) {
-      const bf16x8 wh = frag16(w1h + tr * SP + 32 * kk + 8 * g4);
-      const bf16x8 wl = frag16(w1l + tr * SP + 32 * kk + 8 * g4);
-#pragma unroll
-      for (int j = 0; j < JPW; ++j) {
-        acc[j] = mfma(vph[kk][j], wh, acc[j]);
-        acc[j] = mfma(vpl[kk][j], wh, acc[j]);
-        acc[j] = mfma(vph[kk][j], wl, acc[j]);
+      for (int kk = 0; kk < KSS; ++kk) {
+        if (32 * kk > 16 * mt + 15) break;
+        const bf16x8 wh = frag16(w1h + tr * SPW + 32 * kk + 8 * g4);
+        const bf16x8 wl = frag16(w1l + tr * SPW + 32 * kk + 8 * g4);
+        acc = mfma(vph[kk], wh, acc);
+        acc = mfma(vpl[kk], wh, acc);
+        acc = mfma(vph[kk], wl, acc);
       }
-    }
-    if (t < n) {
-#pragma unroll
-      for (int j = 0; j < JPW; ++j) {
-        const size_t oi = obase + (size_t)t * ostride + 16 * (JPW * wave + j) + 4 * g4;
-        if (p.out_bf16) {
-          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 o4 = {(__bf16)acc[j][0], (__bf16)acc[j][1], (__bf16)acc[j][2], (__bf16)acc[j][3]};
-          *reinterpret_cast<bf16x4 *>(static_cast<__bf16 *>(p.o) + oi) = o4;
-        } else {
-          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + oi) = acc[j];
-        }
+      if (bad) acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      const unsigned vo = (unsigned)t * ostride + (unsigned)((16 * wave + 4 * g4) * oes);
+      if (p.out_bf16) {
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[1]) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[3]) << 16);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, (int)vo, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, (int)vo, 0, 0);
       }
     }
   }
@@ -516,8 +565,14 @@ __global__ __launch_bounds__(256, BF16IN ? 2 : 1) void verify_kernel(VerifyParam
 
 template <int D, bool BF16IN, int NT>
 hipError_t launch_one(const VerifyParams &p, hipStream_t stream) {
-  const int units = p.L * p.B * p.H;
-  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT>), dim3((unsigned)units), dim3(256), 0, stream, p);
+  const unsigned units = (unsigned)(p.L * p.B * p.H);
+  if constexpr (BF16IN) {
+    if (p.out_bf16) {
+      hipLaunchKernelGGL((verify_kernel<D, true, NT, false>), dim3(units), dim3(4 * D), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, true>), dim3(units), dim3(4 * D), 0, stream, p);
   return hipGetLastError();
 }
 
