@@ -207,8 +207,9 @@ def main():
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
         "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),
         "tau_mean": float(np.mean(taus)) / cfg.B,
-        "precision": "bf16 rows and outputs; fp32 state, gates and accumulation (S0 and the "
-                     "effective queries split hi+lo bf16 on MFMA); fp64 tree scores",
+        "precision": "bf16 rows and outputs; fp32 state, gates and accumulation; S0 rounded to "
+                     "bf16 for the dense MFMA product (below the bf16 output rounding), W1 and "
+                     "V' as hi+lo bf16 pairs; fp64 tree scores",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_reqs, cfg.B))
