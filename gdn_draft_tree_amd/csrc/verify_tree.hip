@@ -67,9 +67,8 @@ struct VerifySmem {
   // W1 row stride in bf16 elements: 16 rows read at one column start in distinct banks
   static constexpr int SPW = SP + 8;
   static constexpr int W1B = 2 * RM * SPW * 2;         // W1 rows, hi and lo bf16
-  static constexpr int QKB = (2 * ROWB > W1B) ? 2 * ROWB : W1B;
-  alignas(16) unsigned char qk[QKB];   // q rows, k rows; W1 after phase 1
-  alignas(16) unsigned char vrow[ROWB];
+  alignas(16) unsigned char qk[2 * ROWB];  // q rows, k rows
+  alignas(16) uint16_t w1[W1B / 2];        // W1 rows: hi, then lo
   alignas(16) float lc[RM * kAR];      // k_t . k_s for s a strict ancestor of t, at depth(s)
   alignas(16) float mc[RM * kAR];      // q_t . k_s for s an ancestor-or-self of t, at depth(s)
   alignas(16) unsigned long long mask[RM];
@@ -106,6 +105,14 @@ __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+// 16 x 16 x 16 product on bf16 bit patterns: lane l holds A[l % 16][4 (l / 16) + 0..3] and
+// B[4 (l / 16) + 0..3][l % 16].
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
 
 // Eight consecutive elements of one LDS row (a 16-byte chunk for bf16, two for fp32): the
 // operand fragment of a product that contracts over d.
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
   constexpr int NW = D / 16;               // waves, one 16-channel value tile each
   constexpr int NTH = 64 * NW;             // threads
   constexpr int QMAX = SM::ROWB / 1024;    // 1 KiB row chunks per matrix
-  constexpr int CPW = (3 * QMAX + NW - 1) / NW;  // row chunks per wave
+  constexpr int CPWQK = (2 * QMAX + NW - 1) / NW;  // q and k row chunks per wave
   constexpr int NS0 = KS * 2;              // S0 fragment loads per lane
   __shared__ SM s;
 
@@ -186,8 +193,7 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
   const size_t rstride = (size_t)p.H * D;  // elements between consecutive slots of one head
   const T *qrow = reinterpret_cast<const T *>(s.qk);
   const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
-  const T *vrow = reinterpret_cast<const T *>(s.vrow);
-  uint16_t *w1h = reinterpret_cast<uint16_t *>(s.qk);
+  uint16_t *w1h = s.w1;
   uint16_t *w1l = w1h + RM * SPW;
 
   // ---- 0. loads ----------------------------------------------------------------------
@@ -200,6 +206,12 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
       reinterpret_cast<float4 *>(s.lc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
       reinterpret_cast<float4 *>(s.mc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
+  }
+  static_assert(SM::W1B % 16 == 0, "W1 in 16-byte stores");
+#pragma unroll
+  for (int x = 0; x < (SM::W1B / 16 + NTH - 1) / NTH; ++x) {
+    const int i = tid + NTH * x;
+    if (i < SM::W1B / 16) reinterpret_cast<uint4 *>(s.w1)[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (tid >= n && tid < 16 * NT) s.gamma[tid] = 0.f;
   if (tid == 0) s.bad = 0;
@@ -218,28 +230,32 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
   const T w_a1 = static_cast<const T *>(p.alpha)[(rowbase + tn) * p.H + h];
   const T w_b1 = static_cast<const T *>(p.beta)[(rowbase + tn) * p.H + h];
   const unsigned long long my_mask = p.anc[tb + min(tid, nl)];  // -> LDS for the Gram scatter
+  // Bulk loads in the order they are needed: q and k rows (the Gram tiles and the path solve
+  // start on them alone), this wave's S0 fragments, then its v fragments (needed last).
+  // q and k rows go straight into LDS: each wave instruction fills 64 consecutive 16-byte chunks; lane
+  // l of chunk qi holds physical chunk 64 qi + l and fetches the logical chunk that the
+  // swizzle places there.  Rows past the node count fetch row n-1 (never used).  Every wave
+  // issues the same number of loads (its last chunk repeated, rewriting the same bytes).
+  const T *gq = static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D;
+  const T *gk = static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D;
+  const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
+  const int nb = (int)(n * rstride * sizeof(T));
+  auto row_chunk = [&](const __amdgpu_buffer_rsrc_t &rs, unsigned char *mat_lds, int qi) {
+    const int pc = 64 * qi + lane, r = pc / CPR, c = (pc % CPR) ^ (r & (CPR - 1));
+    const unsigned off = (unsigned)((min(r, nl) * (int)rstride + c * CH) * (int)sizeof(T));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(mat_lds + 1024 * qi), 16, off, 0, 0, 0);
+  };
   __builtin_amdgcn_sched_barrier(0);
   {
-    // q, k, v rows -> LDS: each wave instruction fills 64 consecutive 16-byte chunks; lane l
-    // of chunk qi holds physical chunk 64 qi + l and fetches the logical chunk that the
-    // swizzle places there.  Rows past the node count fetch row n-1 (never used).  Every wave
-    // issues the same number of loads (the last chunk repeated, rewriting the same bytes).
-    const T *gq = static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D;
-    const T *gk = static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D;
-    const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
-    const int nb = (int)(n * rstride * sizeof(T));
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)gq, 0, nb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)gk, 0, nb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)gv, 0, nb, 0x00020000);
 #pragma unroll
-    for (int x = 0; x < CPW; ++x) {
-      const int item = min(wave + NW * x, 3 * QMAX - 1);
-      const int mat = item / QMAX, qi = item % QMAX;
-      const int pc = 64 * qi + lane, r = pc / CPR, c = (pc % CPR) ^ (r & (CPR - 1));
-      const unsigned off = (unsigned)((min(r, nl) * (int)rstride + c * CH) * (int)sizeof(T));
-      unsigned char *dst = (mat == 2 ? s.vrow : s.qk + mat * SM::ROWB) + 1024 * qi;
-      const __amdgpu_buffer_rsrc_t rs = mat == 0 ? rq : (mat == 1 ? rk : rv);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)dst, 16, off, 0, 0, 0);
+    for (int x = 0; x < CPWQK; ++x) {
+      const int item = min(wave + NW * x, 2 * QMAX - 1);
+      if (item < QMAX)
+        row_chunk(rq, s.qk, item);
+      else
+        row_chunk(rk, s.qk + SM::ROWB, item - QMAX);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -252,6 +268,23 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
     for (int ks = 0; ks < KS; ++ks) {
       s0r[ks][0] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks);
       s0r[ks][1] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks + 4);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // v fragments of this wave's 16 channels, the A operand of a 16 x 16 x 16 product: lane
+  // (g, r) holds V[16 mt + r][16 wave + 4 g + 0..3].  Rows past the node count lie beyond the
+  // buffer's range and read as zero.
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typename std::conditional<BF16IN, u32x2, u32x4>::type vld[NT];
+  {
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)gv, 0, nb, 0x00020000);
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) {
+      const int off = ((16 * mt + l16) * (int)rstride + 16 * wave + 4 * g4) * (int)sizeof(T);
+      if constexpr (BF16IN)
+        vld[mt] = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+      else
+        vld[mt] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -306,82 +339,50 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
       s.beta[0] = bet[0];
     }
   }
-  // the row loads (issued before the S0 loads) have landed; S0 may still be in flight
-  __builtin_amdgcn_s_waitcnt(0x0070 | ((NS0 & 15) | ((NS0 >> 4) << 14)));  // vmcnt(NS0) lgkmcnt(0)
+  // q and k rows have landed; S0 and v may still be in flight
+  constexpr int kAfterQK = NS0 + NT;
+  static_assert(kAfterQK < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | ((kAfterQK & 15) | ((kAfterQK >> 4) << 14)));  // vmcnt(..) lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
 
-  // ---- 1. P_Q = Q S0, P_K = K S0 (all waves); Gram tiles -------------------------------
+  // ---- 1. Gram tiles [Q; K] K^T of the lower node triangle, dealt over the waves ----------
+  // Tile pair i = mt (mt + 1) / 2 + nt goes to wave NW - 1 - i % NW (wave 0, which has the
+  // path solve next, gets the fewest).  Transposed: lane (g, t) owns node t = 16 mt + l16 and
+  // gets k_s . k_t and k_s . q_t for s = 16 nt + 4 g + 0..3.  Entries of ancestor pairs are
+  // kept at depth(s) = (t's ancestors-or-self in slots 0..s) - 1 (the k.k ones times b_t, the
+  // factor the path solve applies); the rest go to padding entries 17..19.
   if (wave == 1 && lane == 0 && s.mask[0] != 0ull) s.bad = 1;  // the root has no ancestors
-  bf16x8 s0h[KS], s0l[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const float x[8] = {s0r[ks][0][0], s0r[ks][0][1], s0r[ks][0][2], s0r[ks][0][3],
-                        s0r[ks][1][0], s0r[ks][1][1], s0r[ks][1][2], s0r[ks][1][3]};
-    if constexpr (S0LO) {
-      split8(x, s0h[ks], s0l[ks]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s0h[ks][e] = (__bf16)x[e];
-    }
-  }
-  // P_Q is kept transposed (lane (g, t) holds P_Q[t][16 wave + 4 g + 0..3]: the C layout of
-  // S0^T Q^T), P_K node-major (lane (g, c) holds P_K[4 g + 0..3][16 wave + c]).  Both come
-  // from the same registers: the S0 fragments are the A operand of one product and the B
-  // operand of the other, and so are the row fragments.
-  f32x4 pqt[NT], pk[NT];  // tiles past the node count are never read
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
-    if (mt >= ntl) continue;
-    const int tme = 16 * mt + l16, ra = min(tme, nl);
-    bf16x8 aqh[KS], aql[KS], akh[KS], akl[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      row_frag<D, BF16IN>(qrow, ra, 32 * ks + 8 * g4, aqh[ks], aql[ks]);
-      row_frag<D, BF16IN>(krow, ra, 32 * ks + 8 * g4, akh[ks], akl[ks]);
-    }
-    pqt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    pk[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      pqt[mt] = mfma(s0h[ks], aqh[ks], pqt[mt]);
-      pk[mt] = mfma(akh[ks], s0h[ks], pk[mt]);
-      if constexpr (S0LO) {
-        pqt[mt] = mfma(s0l[ks], aqh[ks], pqt[mt]);
-        pk[mt] = mfma(akh[ks], s0l[ks], pk[mt]);
-      }
-      if constexpr (!BF16IN) {
-        pqt[mt] = mfma(s0h[ks], aql[ks], pqt[mt]);
-        pk[mt] = mfma(akl[ks], s0h[ks], pk[mt]);
-      }
-    }
-    // Gram tiles (mt, nt <= mt), transposed, computed with the row fragments just loaded: lane
-    // (g, t) owns node t = 16 mt + l16 and gets k_s . k_t and k_s . q_t for s = 16 nt + 4 g +
-    // 0..3.  Tile pair i = mt (mt + 1) / 2 + nt goes to wave NW - 1 - i % NW.  Entries of
-    // ancestor pairs are kept at depth(s) = (t's ancestors-or-self in slots 0..s) - 1 (the k.k
-    // ones times b_t, the factor the path solve applies); the rest go to padding entries 17..19.
-    const unsigned long long tmask = s.mask[ra];
-    const unsigned long long aset = (tmask << 1) | 1ull;  // slot s <= 63 -> bit s; root in
-    const float bt = s.beta[ra];
-    const int trow = ra * kAR;
-    const bool rowok = tme < n;
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
-      if (wave != NW - 1 - (mt * (mt + 1) / 2 + nt) % NW) continue;
-      const int rb = min(16 * nt + l16, nl);
+      if (wave != NW - 1 - (mt * (mt + 1) / 2 + nt) % NW || mt >= ntl) continue;
+      // Row fragments are read at the tile's rows as they are: rows past the node count hold
+      // finite values (copies of the last row, or the next LDS region), and the entries they
+      // produce are never kept.
+      const int tme = 16 * mt + l16, ra = min(tme, nl);
+      const int rb = 16 * nt + l16;
       f32x4 gk4 = {0.f, 0.f, 0.f, 0.f}, gq4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 bh, bl;
+        bf16x8 aqh, aql, akh, akl, bh, bl;
+        row_frag<D, BF16IN>(qrow, tme, 32 * ks + 8 * g4, aqh, aql);
+        row_frag<D, BF16IN>(krow, tme, 32 * ks + 8 * g4, akh, akl);
         row_frag<D, BF16IN>(krow, rb, 32 * ks + 8 * g4, bh, bl);
-        gk4 = mfma(bh, akh[ks], gk4);
-        gq4 = mfma(bh, aqh[ks], gq4);
+        gk4 = mfma(bh, akh, gk4);
+        gq4 = mfma(bh, aqh, gq4);
         if constexpr (!BF16IN) {
-          gk4 = mfma(bl, akh[ks], gk4);
-          gk4 = mfma(bh, akl[ks], gk4);
-          gq4 = mfma(bl, aqh[ks], gq4);
-          gq4 = mfma(bh, aql[ks], gq4);
+          gk4 = mfma(bl, akh, gk4);
+          gk4 = mfma(bh, akl, gk4);
+          gq4 = mfma(bl, aqh, gq4);
+          gq4 = mfma(bh, aql, gq4);
         }
       }
+      const unsigned long long tmask = s.mask[ra];
+      const unsigned long long aset = (tmask << 1) | 1ull;  // slot s <= 63 -> bit s; root in
+      const float bt = s.beta[ra];
+      const int trow = ra * kAR;
+      const bool rowok = tme < n;
       const int sn0 = 16 * nt + 4 * g4;
       uint32_t bits;  // ancestor flags of slots sn0 .. sn0 + 3
       int cbelow;     // t's ancestors-or-self in slots 0 .. sn0 - 1
@@ -404,61 +405,14 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
     }
   }
   lds_barrier();
-  const bool bad = s.bad != 0;
 
-  // ---- 2a. V' = V - g P_K for this wave's channels, packed as the A operand of V'^T W1^T ---
-  // V enters the C tiles through one product with a 0/1 selector B[k][c] = (k == c + off):
-  // the A operand is a plain row fragment of V, so V is never read transposed.
-  bf16x8 vph[KSS], vpl[KSS];
-  {
-    bf16x8 isel;
-    const int off = 16 * (wave & 1);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) isel[e] = (__bf16)((8 * g4 + e == l16 + off) ? 1.f : 0.f);
-    const int vcol = 32 * (wave >> 1) + 8 * g4;  // this wave's 32-channel chunk
-#pragma unroll
-    for (int mt = 0; mt < 2 * KSS; ++mt) {
-      f32x4 vp = {0.f, 0.f, 0.f, 0.f};
-      if (mt < NT && mt < ntl) {
-        const int mc_ = mt < NT ? mt : NT - 1;  // (static index; mt < NT here)
-        const float4 gm = *reinterpret_cast<const float4 *>(&s.gamma[16 * mt + 4 * g4]);
-        bf16x8 avh, avl;
-        row_frag<D, BF16IN>(vrow, min(16 * mt + l16, nl), vcol, avh, avl);
-        vp[0] = -gm.x * pk[mc_][0];
-        vp[1] = -gm.y * pk[mc_][1];
-        vp[2] = -gm.z * pk[mc_][2];
-        vp[3] = -gm.w * pk[mc_][3];
-        vp = mfma(avh, isel, vp);
-        if constexpr (!BF16IN) vp = mfma(avl, isel, vp);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 hv = (__bf16)vp[i];
-        vph[mt >> 1][4 * (mt & 1) + i] = hv;
-        vpl[mt >> 1][4 * (mt & 1) + i] = (__bf16)(vp[i] - (float)hv);
-      }
-    }
-  }
-
-  // ---- 2b. path solve, one lane of wave 0 per node; the root's row by wave 1 -------------
+  // ---- 2. wave 0: path solve, one lane per node, and its W1 row (overlapping the S0 loads);
+  //         every wave: P_Q = Q S0 and P_K = K S0 for its channels on MFMA, and V' -----------
   if (wave == 0) {
     const bool tv = t_me < n;
     const int t = tn;
     const int dmax = wave_max_i32(tv ? d_me : 0);
     auto anc_at = [&](int e) -> int { return (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu); };
-    // this node's W1 row is cleared first (up to its 32-node chunk, the last one the output
-    // product reads), so the stores overlap the solve's loads
-    uint4 *rh = reinterpret_cast<uint4 *>(w1h + t * SPW);
-    uint4 *rl = reinterpret_cast<uint4 *>(w1l + t * SPW);
-    if (tv) {
-#pragma unroll
-      for (int v = 0; v < SP / 8; ++v) {
-        if (v < 4 * (t / 32 + 1)) {
-          rh[v] = make_uint4(0u, 0u, 0u, 0u);
-          rl[v] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-    }
     float z[kAR];  // right-hand side q_t . k_{anc e}; zero beyond the depth
 #pragma unroll
     for (int v = 0; v < kAR / 4; ++v) {
@@ -492,33 +446,111 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
         }
       }
     }
+    // W1[t, anc e] = cw[e] z[e] into the (cleared) dense row, hi + lo bf16
+    if (tv) {
 #pragma unroll
-    for (int e = 0; e <= kMaxP; ++e) {
-      if (e > dmax) break;
-      if (tv && e <= d_me) {
-        const float w = s.cwl[e][lane] * z[e];
-        const __bf16 hv = (__bf16)w;
-        const __bf16 lv = (__bf16)(w - (float)hv);
-        const int pos = t * SPW + w1_pos(anc_at(e));
-        w1h[pos] = __builtin_bit_cast(uint16_t, hv);
-        w1l[pos] = __builtin_bit_cast(uint16_t, lv);
+      for (int e = 0; e <= kMaxP; ++e) {
+        if (e <= d_me) {
+          const float w = s.cwl[e][lane] * z[e];
+          const __bf16 hv = (__bf16)w;
+          const __bf16 lv = (__bf16)(w - (float)hv);
+          const int pos = t * SPW + w1_pos(anc_at(e));
+          w1h[pos] = __builtin_bit_cast(uint16_t, hv);
+          w1l[pos] = __builtin_bit_cast(uint16_t, lv);
+        }
       }
     }
   } else if (wave == 1 && lane == 0) {
     // the root: W1[0, 0] = b_0 (q_0 . k_0)
-    uint4 *rh = reinterpret_cast<uint4 *>(w1h);
-    uint4 *rl = reinterpret_cast<uint4 *>(w1l);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      rh[v] = make_uint4(0u, 0u, 0u, 0u);
-      rl[v] = make_uint4(0u, 0u, 0u, 0u);
-    }
     const float w = s.beta[0] * s.mc[0];
     const __bf16 hv = (__bf16)w;
     w1h[0] = __builtin_bit_cast(uint16_t, hv);
     w1l[0] = __builtin_bit_cast(uint16_t, (__bf16)(w - (float)hv));
   }
+  bf16x8 s0h[KS], s0l[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float x[8] = {s0r[ks][0][0], s0r[ks][0][1], s0r[ks][0][2], s0r[ks][0][3],
+                        s0r[ks][1][0], s0r[ks][1][1], s0r[ks][1][2], s0r[ks][1][3]};
+    if constexpr (S0LO) {
+      split8(x, s0h[ks], s0l[ks]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s0h[ks][e] = (__bf16)x[e];
+    }
+  }
+  // P_Q is kept transposed (lane (g, t) holds P_Q[t][16 wave + 4 g + 0..3]: the C layout of
+  // S0^T Q^T), P_K node-major (lane (g, c) holds P_K[4 g + 0..3][16 wave + c]).  Both come
+  // from the same registers: the S0 fragments are the A operand of one product and the B
+  // operand of the other, and so are the row fragments.
+  f32x4 pqt[NT], pk[NT];  // tiles past the node count are never read
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt) {
+    if (mt >= ntl) continue;
+    const int ra = 16 * mt + l16;  // rows past the node count: finite, never used
+    pqt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    pk[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 aqh, aql, akh, akl;
+      row_frag<D, BF16IN>(qrow, ra, 32 * ks + 8 * g4, aqh, aql);
+      row_frag<D, BF16IN>(krow, ra, 32 * ks + 8 * g4, akh, akl);
+      pqt[mt] = mfma(s0h[ks], aqh, pqt[mt]);
+      pk[mt] = mfma(akh, s0h[ks], pk[mt]);
+      if constexpr (S0LO) {
+        pqt[mt] = mfma(s0l[ks], aqh, pqt[mt]);
+        pk[mt] = mfma(akh, s0l[ks], pk[mt]);
+      }
+      if constexpr (!BF16IN) {
+        pqt[mt] = mfma(s0h[ks], aql, pqt[mt]);
+        pk[mt] = mfma(akl, s0h[ks], pk[mt]);
+      }
+    }
+  }
+  // V' = V - g P_K for this wave's channels.  V enters the C tiles (lane (g, c): rows 4 g +
+  // 0..3 of channel c) through a product with the identity, and the result is packed as hi +
+  // lo bf16, the A operand of V'^T W1^T.
+  bf16x8 vph[KSS], vpl[KSS];
+  {
+    s16x4 ident;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ident[e] = (short)((4 * g4 + e == l16) ? 0x3f80 : 0);  // bf16 1
+#pragma unroll
+    for (int mt = 0; mt < 2 * KSS; ++mt) {
+      f32x4 vp = {0.f, 0.f, 0.f, 0.f};
+      if (mt < NT && mt < ntl) {
+        const int mc_ = mt < NT ? mt : NT - 1;  // (static index; mt < NT here)
+        const float4 gm = *reinterpret_cast<const float4 *>(&s.gamma[16 * mt + 4 * g4]);
+        vp[0] = -gm.x * pk[mc_][0];
+        vp[1] = -gm.y * pk[mc_][1];
+        vp[2] = -gm.z * pk[mc_][2];
+        vp[3] = -gm.w * pk[mc_][3];
+        if constexpr (BF16IN) {
+          vp = mfma16(__builtin_bit_cast(s16x4, vld[mc_]), ident, vp);
+        } else {
+          const f32x4 x = __builtin_bit_cast(f32x4, vld[mc_]);
+          s16x4 vh, vl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const __bf16 hv = (__bf16)x[i];
+            vh[i] = __builtin_bit_cast(short, hv);
+            vl[i] = bf16_bits(x[i] - (float)hv);
+          }
+          vp = mfma16(vh, ident, vp);
+          vp = mfma16(vl, ident, vp);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 hv = (__bf16)vp[i];
+        vph[mt >> 1][4 * (mt & 1) + i] = hv;
+        vpl[mt >> 1][4 * (mt & 1) + i] = (__bf16)(vp[i] - (float)hv);
+      }
+    }
+  }
+  // W1 is complete
   lds_barrier();
+  const bool bad = s.bad != 0;
 
   // ---- 3. o^T = g P_Q^T + V'^T W1^T for this wave's value channels, node tile by node tile --
   // A operand: V' (its registers are exactly the A layout of V'^T), B operand: W1 rows from
@@ -535,7 +567,7 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
       if (mt >= ntl) break;
-      const int t = 16 * mt + l16, tr = min(t, nl);
+      const int t = 16 * mt + l16, tr = t;  // W1 rows past the node count: never stored
       const float gt = s.gamma[t];
       f32x4 acc = gt * pqt[mt];
 #pragma unroll
