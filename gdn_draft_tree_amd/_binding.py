@@ -35,7 +35,7 @@ class CTree(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gdn_draft_tree_amd.build_lib`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python __graft_entry__.py` (or __graft_entry__.build())")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.gdntree_build.argtypes = [vp, vp, vp, i, i, i, i, CTree, vp]

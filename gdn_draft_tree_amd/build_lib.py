@@ -1,6 +1,6 @@
 """Builds libgdntree.so (the gfx950 kernels and the C ABI) with hipcc.
 
-    python -m gdn_draft_tree_amd.build_lib      (or __graft_entry__.build())
+    python __graft_entry__.py      (or __graft_entry__.build())
 """
 from __future__ import annotations
 
