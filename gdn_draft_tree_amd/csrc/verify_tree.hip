@@ -9,38 +9,37 @@
 //
 // Tree form of the WY / UT transform.  Let g_t be the product of the gates a over the path
 // root..t.  Unrolling the recurrence along t's path gives S_t = g_t S0 + sum_s (g_t/g_s)
-// k_s u_s^T over the ancestors-or-self s of t, where the pseudo-values u solve a system that
-// is triangular along root paths with right-hand side b_s v'_s,
-//     v'_s = v_s - g_s S0^T k_s,
-// and the readout collapses to
-//     o_t = g_t S0^T q_t + sum_s W1[t,s] v'_s.
-// W1 is supported on the ancestors-or-self of t.  Scaling the unknowns by the path gates
-// removes every gate from the system: if z solves, along t's path (depths e = 0..d_t,
-// deepest first),
-//     z[e] + sum_{e2 > e} z[e2] b_{anc e2} (k_{anc e2} . k_{anc e}) = q_t . k_{anc e},
-// then W1[t, anc e] = (g_t / g_{anc e}) b_{anc e} z[e].
-// So S0, the only large operand (d_k x d_v fp32), enters through ONE dense product
-// [Q; K] S0 that does not depend on the tree at all, and the tree enters through small
-// O(nodes * depth) work (Gram entries of ancestor pairs, the path solve) and one dense
-// node x node product W1 V'.
+// k_s u_s^T over the ancestors-or-self s of t, with pseudo-values u that solve a system
+// triangular along root paths.  Scaling the unknowns by the path gates removes every gate
+// from that system: for node t with ancestors-or-self anc e at depths e = 0..d_t, let z
+// solve (deepest first)
+//     z[e] + sum_{e2 > e} z[e2] b_{anc e2} (k_{anc e2} . k_{anc e}) = q_t . k_{anc e}.
+// With Y[t, anc e] = b_{anc e} z[e] and W1[t, anc e] = (g_t / g_{anc e}) Y[t, anc e],
+//     o_t = S0^T E_t + sum_s W1[t, s] v_s,     E_t = g_t (q_t - sum_s Y[t, s] k_s).
+// So the committed state S0, the only large operand (d_k x d_v fp32), enters through ONE
+// dense product S0^T E, and the tree enters through small work that needs q, k, a and b
+// only: Gram entries of ancestor pairs, one path solve per node, and the "effective
+// queries" E.  Y and W1 are bounded by one in magnitude when |q| = |k| = 1 and a, b lie in
+// [0, 1] (W1[t, s] is the coefficient of v_s in o_t, and z does not depend on the gates).
 //
-// Work decomposition: one workgroup of d / 16 waves per (layer, request, head), wave w owning
-// value channels [16 w, 16 w + 16); two workgroups per CU at d = 128 (16 waves per CU).
-// Per head:
-//  0. q, k, v rows go straight from HBM into LDS (buffer loads to LDS) and each wave loads
-//     its S0 operand fragments into registers.  Wave 0 owns the per-node tree work (lane l
-//     handles node l + 1): from its own early loads it checks the links, finds each node's
-//     ancestors in its bitmask and forms the path gate g_t while the bulk loads are in flight;
-//  1. every wave: P_Q = Q S0 and P_K = K S0 for its channels on MFMA (rows exact in bf16),
-//     the C tiles kept in registers; the Gram tiles [Q; K] K^T of the lower node triangle on
-//     MFMA, dealt over the waves, keeping the entries of ancestor pairs compactly by the depth
-//     of the ancestor;
-//  2. wave 0: one lane per node solves its path system and writes the node's W1 row (hi +
-//     lo bf16) to LDS; every wave: V' = V - g P_K for its channels (V enters the C tiles
-//     through a product with a 0/1 selector, so no transposed read of V is needed);
-//  3. every wave: o^T = g P_Q^T + V'^T W1^T on MFMA (the C layout of V' is exactly the
-//     operand layout the product needs), then the stores.
-// Three barriers per head.
+// Work decomposition: one workgroup per (layer, request, head) with two kinds of waves.
+//  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they only stream
+//    this head's committed state and v rows into registers, wait at the workgroup's one
+//    barrier, then form o^T = S0^T E^T + V^T W1^T on MFMA and store.
+//  * two tree waves: they stream the q and k rows into LDS (buffer loads to LDS), then
+//    compute the Gram tiles [Q; K] K^T of the lower node triangle (dealt between them),
+//    the per-node path solves (one lane per node) that give Y and W1, and E on MFMA, and
+//    arrive at the barrier.  The two tree waves order their phases through an LDS counter.
+// A product wave that issues its state loads stalls until the memory pipeline accepts
+// them, so the waves that carry the latency-bound tree work issue only the small row
+// loads (and run at raised priority).  When the state lands, only one dense product and
+// the stores remain.
+//
+// Precision: MFMA operands are fp16 with fp32 accumulation.  Rows in bf16 convert to fp16
+// exactly; the state and v columns of a product wave are scaled by one power of two (from
+// their largest magnitude) before the conversion and the outputs are scaled back, so the
+// fp16 range holds for any state scale.  The Gram entries are exact for bf16 rows (fp32
+// inputs enter the Gram as hi + lo bf16 pairs), and the path solve runs in fp32.
 
 #include <type_traits>
 
@@ -50,6 +49,7 @@ namespace gdntree {
 namespace {
 
 constexpr int kAR = 20;  // compact row: ancestor depths 0..16, padded to five 16-byte vectors
+constexpr int kLdsBytes = 160 * 1024;
 
 template <bool BF16IN>
 struct InT;
@@ -58,24 +58,47 @@ struct InT<true> { typedef uint16_t T; };
 template <>
 struct InT<false> { typedef float T; };
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 template <int D, bool BF16IN, int NT>
 struct VerifySmem {
   typedef typename InT<BF16IN>::T T;
-  static constexpr int RM = (16 * NT < kMaxSlots) ? 16 * NT : kMaxSlots;   // node rows held
+  static constexpr int RM = (16 * NT < kMaxSlots) ? 16 * NT : kMaxSlots;  // node rows held
   static constexpr int ROWB = (RM * D * (int)sizeof(T) + 1023) / 1024 * 1024;  // whole 1 KiB loads
-  static constexpr int SP = (16 * NT + 31) / 32 * 32;  // node (contraction) axis of W1 V'
-  // W1 row stride in bf16 elements: 16 rows read at one column start in distinct banks
+  static constexpr int SP = (16 * NT + 31) / 32 * 32;  // node (contraction) axis of Y K and W1 V
+  // Y / W1 row stride in fp16 elements: 16 rows read at one column start hit distinct banks
   static constexpr int SPW = SP + 8;
-  static constexpr int W1B = 2 * RM * SPW * 2;         // W1 rows, hi and lo bf16
-  alignas(16) unsigned char qk[2 * ROWB];  // q rows, k rows
-  alignas(16) uint16_t w1[W1B / 2];        // W1 rows: hi, then lo
-  alignas(16) float lc[RM * kAR];      // k_t . k_s for s a strict ancestor of t, at depth(s)
-  alignas(16) float mc[RM * kAR];      // q_t . k_s for s an ancestor-or-self of t, at depth(s)
+  // fp16 rows of E: in place of the q rows for bf16 inputs, a region of their own for fp32
+  static constexpr int EB = BF16IN ? 16 : (RM * D * 2 + 15) / 16 * 16;
+  alignas(16) unsigned char qk[2 * ROWB];  // q rows (then E for bf16 inputs), k rows
+  alignas(16) unsigned char e16[EB];
+  alignas(16) _Float16 y[RM * SPW];        // Y rows, the node axis in the MFMA k order
+  alignas(16) _Float16 w1[RM * SPW];       // W1 rows, same layout
+  alignas(16) float lc[RM * kAR];          // b_t k_t . k_s for s a strict ancestor of t, at depth(s)
+  alignas(16) float mc[RM * kAR];          // q_t . k_s for s an ancestor-or-self of t, at depth(s)
   alignas(16) unsigned long long mask[RM];
-  alignas(16) float gamma[16 * NT];    // path gate; zero past the node count
-  float beta[RM];                      // b per node
-  float cwl[kMaxAnc][64];              // wave 0's W1 weights, per depth and lane
+  alignas(16) float gamma[16 * NT];        // path gate
+  float beta[RM];                          // b per node
+  float cwl[kMaxAnc][64];                  // W1 weights b_{anc e} g_t / g_{anc e}, per depth and lane
   int bad;
+  int sync;                                // tree-wave phase counter
+};
+
+constexpr int kTreeWaves = 4;
+
+template <int D, bool BF16IN, int NT>
+struct VerifyShape {
+  static constexpr int NW = D / 16;        // product waves
+  static constexpr int WAVES = NW + kTreeWaves;
+  static constexpr int NTH = 64 * WAVES;
+  static constexpr int LDS = (int)sizeof(VerifySmem<D, BF16IN, NT>);
+  static constexpr int WG_PER_CU0 = kLdsBytes / LDS < 1 ? 1 : kLdsBytes / LDS;
+  static constexpr int WG_PER_CU = WG_PER_CU0 < 2 ? WG_PER_CU0 : 2;
+  // A workgroup's waves are dealt over the CU's four SIMDs, so the register budget must let
+  // every SIMD hold ceil(WAVES / 4) waves of each resident workgroup.
+  static constexpr int WPEU = WG_PER_CU * ((WAVES + 3) / 4);
 };
 
 // Rows live in LDS unpadded with their 16-byte chunks XOR-swizzled by the row index, so that
@@ -91,6 +114,9 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ __forceinline__ bf16x8 frag16(const void *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
+__device__ __forceinline__ f16x8 hfrag(const void *p) {
+  return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4 *>(p));
+}
 
 // x = hi + lo with hi, lo bf16 (round to nearest even); x - hi is exact in fp32.
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
@@ -102,20 +128,19 @@ __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
   }
 }
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-// 16 x 16 x 16 product on bf16 bit patterns: lane l holds A[l % 16][4 (l / 16) + 0..3] and
-// B[4 (l / 16) + 0..3][l % 16].
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ short bf16_bits(float x) { return __builtin_bit_cast(short, (__bf16)x); }
+// 16 x 16 x 16: lane l holds A[l % 16][4 (l / 16) + 0..3] and B[4 (l / 16) + 0..3][l % 16].
+__device__ __forceinline__ f32x4 mfma16_f16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
 
 // Eight consecutive elements of one LDS row (a 16-byte chunk for bf16, two for fp32): the
-// operand fragment of a product that contracts over d.
+// operand fragment of a Gram product that contracts over d.
 template <int D, bool BF16IN>
 __device__ __forceinline__ void row_frag(const typename InT<BF16IN>::T *rows, int r, int col, bf16x8 &hi,
                                          bf16x8 &lo) {
@@ -129,10 +154,24 @@ __device__ __forceinline__ void row_frag(const typename InT<BF16IN>::T *rows, in
   }
 }
 
-// Position of node s inside its 32-node chunk of a W1 row.  The B operand of W1 V' is V' in
-// the C layout of two 16-node tiles: lane (g, c) holds nodes 4 g + 0..3 of the first tile and
-// 16 + 4 g + 0..3 of the second, so the k index 8 g + e of the product stands for node
-// 4 g + e (e < 4) or 16 + 4 g + e - 4 (e >= 4); W1 rows are stored in that k order.
+// Four consecutive elements of one LDS row as fp32 (col is a multiple of 4).
+template <int D, bool BF16IN>
+__device__ __forceinline__ f32x4 row4(const typename InT<BF16IN>::T *rows, int r, int col) {
+  if constexpr (BF16IN) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(rows + swz<D, 8>(r, col));
+    return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                 __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+  } else {
+    const float4 x = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
+    return f32x4{x.x, x.y, x.z, x.w};
+  }
+}
+
+// Position of node s inside its 32-node chunk of a Y / W1 row.  The A operand of Y K and
+// V^T W1^T holds, in lane (g, c), nodes 4 g + 0..3 of the chunk's first 16-node tile and
+// 16 + 4 g + 0..3 of its second (the C layout of two products with the identity), so the k
+// index 8 g + e of the product stands for node 4 g + e (e < 4) or 16 + 4 g + e - 4 (e >= 4);
+// the rows are stored in that k order.
 __device__ __forceinline__ int w1_pos(int s) {
   const int sl = s & 31;
   return (s & ~31) + 8 * ((sl & 15) >> 2) + ((sl >> 4) << 2) + (sl & 3);
@@ -148,34 +187,39 @@ __device__ __forceinline__ int wave_max_i32(int x) {
   return max(max(r0, r1), max(r2, r3));
 }
 
-// Barrier that orders LDS only: every wave's LDS traffic is complete, in-flight HBM loads
-// into registers are not waited for.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
-
 __device__ __forceinline__ float bperm_f32(int lane_src, float x) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(lane_src << 2, __float_as_int(x)));
 }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
-// S0LO: S0 enters the products as hi + lo bf16 (fp32 outputs); without it S0 is rounded to
-// bf16 once, which for bf16 outputs stays below the outputs' own rounding.
-template <int D, bool BF16IN, int NT, bool S0LO>
-__global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void verify_kernel(VerifyParams p) {
+// The two tree waves meet here: each finishes its own memory work (loads into LDS
+// included), counts itself in, and waits for the other.  The wait is bounded; a wave that
+// gives up marks the request bad (NaN outputs) instead of hanging.
+__device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int lane) {
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  int spins = 0;
+  while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > (1 << 22)) {
+      *bad = 1;
+      break;
+    }
+  }
+}
+
+template <int D, bool BF16IN, int NT>
+__global__ __launch_bounds__((VerifyShape<D, BF16IN, NT>::NTH), (VerifyShape<D, BF16IN, NT>::WPEU))
+void verify_kernel(VerifyParams p) {
   typedef VerifySmem<D, BF16IN, NT> SM;
   typedef typename SM::T T;
-  constexpr int RM = SM::RM, SP = SM::SP, SPW = SM::SPW;
+  constexpr int RM = SM::RM, SPW = SM::SPW;
   constexpr int CH = 16 / (int)sizeof(T), CPR = D / CH;
   constexpr int KS = D / 32;               // MFMA k-steps over d_k
-  constexpr int KSS = SP / 32;             // MFMA k-steps over the node axis
-  constexpr int NW = D / 16;               // waves, one 16-channel value tile each
-  constexpr int NTH = 64 * NW;             // threads
+  constexpr int KSS = SM::SP / 32;         // MFMA k-steps over the node axis
+  constexpr int NW = D / 16;               // product waves; also the channel tiles of E
   constexpr int QMAX = SM::ROWB / 1024;    // 1 KiB row chunks per matrix
-  constexpr int CPWQK = (2 * QMAX + NW - 1) / NW;  // q and k row chunks per wave
-  constexpr int NS0 = KS * 2;              // S0 fragment loads per lane
   __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
@@ -191,111 +235,248 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
   const int ntl = (n + 15) / 16;  // node tiles in use
   const size_t rowbase = (size_t)lb * p.R;
   const size_t rstride = (size_t)p.H * D;  // elements between consecutive slots of one head
-  const T *qrow = reinterpret_cast<const T *>(s.qk);
-  const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
-  uint16_t *w1h = s.w1;
-  uint16_t *w1l = w1h + RM * SPW;
+  const int nb = (int)(n * rstride * sizeof(T));  // byte range of this head's used rows
+  // fp16 rows of E (same swizzled layout as bf16 rows)
+  _Float16 *erow = reinterpret_cast<_Float16 *>(BF16IN ? s.qk : s.e16);
 
-  // ---- 0. loads ----------------------------------------------------------------------
-  // Constant LDS stores first: issued before any load into LDS, they never wait for one.
-  static_assert(RM * kAR / 4 <= 2 * NTH, "compact Gram rows: two stores per thread");
+  if (wave < NW) {
+    // ================================ product waves ==================================
+    // The tree waves issue their row loads before this barrier, so they are queued ahead of
+    // the state loads below.
+    __builtin_amdgcn_s_barrier();
+    const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
+    // v fragments, the A operand of a 16 x 16 x 16 product: lane (g, r) holds V[16 mt + r]
+    // [16 wave + 4 g + 0..3].  Rows past the node count lie beyond the buffer's range and
+    // read as zero.
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    typename std::conditional<BF16IN, u32x2, u32x4>::type vld[NT];
+    {
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)gv, 0, nb, 0x00020000);
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int i = tid + NTH * x;
-    if (i < RM * kAR / 4) {
-      reinterpret_cast<float4 *>(s.lc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      reinterpret_cast<float4 *>(s.mc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int mt = 0; mt < NT; ++mt) {
+        const int off = ((16 * mt + l16) * (int)rstride + 16 * wave + 4 * g4) * (int)sizeof(T);
+        if constexpr (BF16IN)
+          vld[mt] = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+        else
+          vld[mt] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      }
     }
-  }
-  static_assert(SM::W1B % 16 == 0, "W1 in 16-byte stores");
+    // state fragments of this wave's value channels, the A operand of S0^T E^T: lane (g, c)
+    // holds S0[32 ks + 8 g + 0..7][channel 16 wave + c], contiguous in the [d_v][d_k] layout.
+    f32x4 s0r[KS][2];
+    {
+      const float *sr = p.state + ((size_t)u * D + 16 * wave + l16) * D + 8 * g4;
 #pragma unroll
-  for (int x = 0; x < (SM::W1B / 16 + NTH - 1) / NTH; ++x) {
-    const int i = tid + NTH * x;
-    if (i < SM::W1B / 16) reinterpret_cast<uint4 *>(s.w1)[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
-  if (tid >= n && tid < 16 * NT) s.gamma[tid] = 0.f;
-  if (tid == 0) s.bad = 0;
-  // Wave 0 owns the per-node tree work: lane l handles node t = l + 1 (the root is trivial)
-  // and holds the gates of slot l for the other lanes.  These small loads go first, so wave 0
-  // can wait for them alone (memory counters complete in order) and finish its per-node
-  // prologue while the bulk loads below are still in flight.  All loads are unconditional at
-  // clamped slots, so no branch forces an early wait and the counters stay static.
-  const int t_me = lane + 1;
-  const size_t tb = (size_t)b * p.R;
-  const int tn = min(t_me, nl), ts = min(lane, nl);
-  const unsigned long long w_mask = p.anc[tb + tn];
-  const int w_par = p.parent[tb + tn];
-  const T w_a0 = static_cast<const T *>(p.alpha)[(rowbase + ts) * p.H + h];
-  const T w_b0 = static_cast<const T *>(p.beta)[(rowbase + ts) * p.H + h];
-  const T w_a1 = static_cast<const T *>(p.alpha)[(rowbase + tn) * p.H + h];
-  const T w_b1 = static_cast<const T *>(p.beta)[(rowbase + tn) * p.H + h];
-  const unsigned long long my_mask = p.anc[tb + min(tid, nl)];  // -> LDS for the Gram scatter
-  // Bulk loads in the order they are needed: q and k rows (the Gram tiles and the path solve
-  // start on them alone), this wave's S0 fragments, then its v fragments (needed last).
-  // q and k rows go straight into LDS: each wave instruction fills 64 consecutive 16-byte chunks; lane
-  // l of chunk qi holds physical chunk 64 qi + l and fetches the logical chunk that the
-  // swizzle places there.  Rows past the node count fetch row n-1 (never used).  Every wave
-  // issues the same number of loads (its last chunk repeated, rewriting the same bytes).
-  const T *gq = static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D;
-  const T *gk = static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D;
-  const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
-  const int nb = (int)(n * rstride * sizeof(T));
-  auto row_chunk = [&](const __amdgpu_buffer_rsrc_t &rs, unsigned char *mat_lds, int qi) {
-    const int pc = 64 * qi + lane, r = pc / CPR, c = (pc % CPR) ^ (r & (CPR - 1));
-    const unsigned off = (unsigned)((min(r, nl) * (int)rstride + c * CH) * (int)sizeof(T));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(mat_lds + 1024 * qi), 16, off, 0, 0, 0);
-  };
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc((void *)gq, 0, nb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)gk, 0, nb, 0x00020000);
-#pragma unroll
-    for (int x = 0; x < CPWQK; ++x) {
-      const int item = min(wave + NW * x, 2 * QMAX - 1);
-      if (item < QMAX)
-        row_chunk(rq, s.qk, item);
-      else
-        row_chunk(rk, s.qk + SM::ROWB, item - QMAX);
+      for (int ks = 0; ks < KS; ++ks) {
+        s0r[ks][0] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks);
+        s0r[ks][1] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks + 4);
+      }
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // S0 operand fragments of this wave's value channels: lane (g, c) holds
-  // S0[32 ks + 8 g + 0..7][channel 16 wave + c], contiguous in the [d_v][d_k] state layout.
-  f32x4 s0r[KS][2];
-  {
-    const float *sr = p.state + ((size_t)u * D + 16 * wave + l16) * D + 8 * g4;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s0r[ks][0] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks);
-      s0r[ks][1] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks + 4);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // v fragments of this wave's 16 channels, the A operand of a 16 x 16 x 16 product: lane
-  // (g, r) holds V[16 mt + r][16 wave + 4 g + 0..3].  Rows past the node count lie beyond the
-  // buffer's range and read as zero.
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  typename std::conditional<BF16IN, u32x2, u32x4>::type vld[NT];
-  {
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)gv, 0, nb, 0x00020000);
+    __builtin_amdgcn_s_barrier();  // (1) W1 is in LDS
+
+    // ---- V^T W1^T for this wave's channels, before the state has landed ------------------
+    // v is scaled by a power of two 2^-ev chosen from its largest magnitude (the scaled
+    // values lie in [2^14, 2^15) at most), so the fp16 range holds for any v scale.
+    float mv = 0.f;
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
-      const int off = ((16 * mt + l16) * (int)rstride + 16 * wave + 4 * g4) * (int)sizeof(T);
-      if constexpr (BF16IN)
-        vld[mt] = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
-      else
-        vld[mt] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      if constexpr (BF16IN) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          mv = fmaxf(mv, fabsf(__uint_as_float(vld[mt][i] << 16)));
+          mv = fmaxf(mv, fabsf(__uint_as_float(vld[mt][i] & 0xffff0000u)));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(__uint_as_float(vld[mt][i])));
+      }
+    }
+    // non-negative floats order like their bit patterns; ex = clamped biased exponent
+    const int exv = min(max((wave_max_i32(__float_as_int(mv)) >> 23) & 0xff, 15), 254);
+    // V^T in the C layout (lane (g, c): rows 4 g + 0..3 of channel c) through a product with
+    // the identity, packed as the A operand of V^T W1^T.
+    f32x4 acc[NT];
+    {
+      f16x8 vph[KSS];
+      f16x4 ident;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ident[e] = (_Float16)((4 * g4 + e == l16) ? 1.f : 0.f);
+#pragma unroll
+      for (int mt = 0; mt < 2 * KSS; ++mt) {
+        f32x4 vp = {0.f, 0.f, 0.f, 0.f};
+        if (mt < NT && mt < ntl) {
+          const int mc_ = mt < NT ? mt : NT - 1;  // (static index; mt < NT here)
+          f16x4 a;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float x;
+            if constexpr (BF16IN)
+              x = (i & 1) ? __uint_as_float(vld[mc_][i >> 1] & 0xffff0000u) : __uint_as_float(vld[mc_][i >> 1] << 16);
+            else
+              x = __uint_as_float(vld[mc_][i]);
+            a[i] = (_Float16)__builtin_amdgcn_ldexpf(x, 141 - exv);
+          }
+          vp = mfma16_f16(a, ident, vp);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vph[mt >> 1][4 * (mt & 1) + i] = (_Float16)vp[i];
+      }
+      // W1 is zero above the diagonal, so node chunks past the tile are skipped
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (mt >= ntl) continue;
+        const int t = 16 * mt + l16;
+#pragma unroll
+        for (int kk = 0; kk < KSS; ++kk) {
+          if (32 * kk > 16 * mt + 15) break;
+          acc[mt] = mfma_f16(vph[kk], hfrag(s.w1 + t * SPW + 32 * kk + 8 * g4), acc[mt]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_barrier();  // (2) E is in LDS
+    const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
+
+    // ---- + S0^T E^T, once the state has landed --------------------------------------------
+    // The state is scaled by 2^(141 - ex) with ex >= the v exponent, so both scaled operands
+    // stay inside the fp16 range; the V^T W1^T part is rescaled to match (exact).
+    float ms = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(s0r[ks][j][i]));
+    const int exs = min(max((wave_max_i32(__float_as_int(ms)) >> 23) & 0xff, 15), 254);
+    const int ex = max(exs, exv);
+    f16x8 s0h[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s0h[ks][e] = (_Float16)__builtin_amdgcn_ldexpf(s0r[ks][e >> 2][e & 3], 141 - ex);
+
+    // Lane (g, t) ends with o[t][16 wave + 4 g + 0..3]: one 8-byte (bf16) store per tile,
+    // through a buffer whose range ends at the last node, so rows past the node count are
+    // dropped.  An inconsistent tree gives NaN outputs.
+    const int oes = p.out_bf16 ? 2 : 4;
+    const unsigned ostride = (unsigned)(p.H * D * oes);
+    char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
+    const int orange = (nl * p.H * D + D) * oes;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) {
+      if (mt >= ntl) break;
+      const int t = 16 * mt + l16;  // rows past the node count: never stored
+      f32x4 o4 = acc[mt];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = __builtin_amdgcn_ldexpf(o4[i], exv - ex);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) o4 = mfma_f16(s0h[ks], hfrag(erow + swz<D, 8>(t, 32 * ks + 8 * g4)), o4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = __builtin_amdgcn_ldexpf(o4[i], ex - 141);
+      if (bad) o4 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      const unsigned vo = (unsigned)t * ostride + (unsigned)((16 * wave + 4 * g4) * oes);
+      if (p.out_bf16) {
+        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[0]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[1]) << 16);
+        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[2]) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[3]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, (int)vo, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), ro, (int)vo, 0, 0);
+      }
+    }
+    return;
+  }
+
+  // ================================== tree waves =====================================
+  __builtin_amdgcn_s_setprio(3);
+  const int tw = wave - NW;  // 0: per-node tree work and the path solves; 1..3: clears
+  const T *qrow = reinterpret_cast<const T *>(s.qk);
+  const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
+  const size_t tb = (size_t)b * p.R;
+  // tw 0 issues only the small per-node loads: an LDS write of a wave waits for that wave's
+  // own loads into LDS, and its prologue writes LDS early.  tw 1..3 clear Y, W1 (zero off the
+  // ancestor pattern) and the compact Gram rows first, for the same reason, then load the q
+  // and k rows.
+  const int t_me = lane + 1;
+  const int tn = min(t_me, nl);
+  const int ts = min(lane, nl);
+  unsigned long long w_mask = 0ull, my_mask = 0ull;
+  int w_par = 0;
+  uint32_t w_a0 = 0u, w_b0 = 0u, w_a1 = 0u, w_b1 = 0u;  // gate bits
+  if (tw == 0) {
+    if (lane == 0) {
+      s.sync = 0;
+      s.bad = 0;
+    }
+    w_mask = p.anc[tb + tn];
+    w_par = p.parent[tb + tn];
+    my_mask = p.anc[tb + ts];
+    const T *ga = static_cast<const T *>(p.alpha), *gb = static_cast<const T *>(p.beta);
+    if constexpr (BF16IN) {
+      w_a0 = reinterpret_cast<const uint16_t *>(ga)[(rowbase + ts) * p.H + h];
+      w_b0 = reinterpret_cast<const uint16_t *>(gb)[(rowbase + ts) * p.H + h];
+      w_a1 = reinterpret_cast<const uint16_t *>(ga)[(rowbase + tn) * p.H + h];
+      w_b1 = reinterpret_cast<const uint16_t *>(gb)[(rowbase + tn) * p.H + h];
+    } else {
+      w_a0 = reinterpret_cast<const uint32_t *>(ga)[(rowbase + ts) * p.H + h];
+      w_b0 = reinterpret_cast<const uint32_t *>(gb)[(rowbase + ts) * p.H + h];
+      w_a1 = reinterpret_cast<const uint32_t *>(ga)[(rowbase + tn) * p.H + h];
+      w_b1 = reinterpret_cast<const uint32_t *>(gb)[(rowbase + tn) * p.H + h];
+    }
+  } else {
+    constexpr int NY = 2 * RM * SPW * 2 / 16, NL = 2 * RM * kAR * 4 / 16;
+    static_assert(offsetof(SM, w1) == offsetof(SM, y) + RM * SPW * 2, "Y and W1 adjacent");
+    static_assert(offsetof(SM, mc) == offsetof(SM, lc) + RM * kAR * 4, "lc and mc adjacent");
+    constexpr int NC = kTreeWaves - 1;
+#pragma unroll
+    for (int x = 0; x < (NY + 64 * NC - 1) / (64 * NC); ++x) {
+      const int i = (tw - 1) * 64 + lane + 64 * NC * x;
+      if (i < NY) reinterpret_cast<uint4 *>(s.y)[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int x = 0; x < (NL + 64 * NC - 1) / (64 * NC); ++x) {
+      const int i = (tw - 1) * 64 + lane + 64 * NC * x;
+      if (i < NL) reinterpret_cast<uint4 *>(s.lc)[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    // q and k rows straight into LDS, 1 KiB chunks dealt over tw 1..3: each wave instruction
+    // fills 64 consecutive 16-byte chunks; lane l of chunk qi holds physical chunk 64 qi + l
+    // and fetches the logical chunk that the swizzle places there.  Rows past the node count
+    // fetch row n-1 (never used).
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D), 0, nb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D), 0, nb, 0x00020000);
+#pragma unroll
+    for (int x = 0; x < (2 * QMAX + NC - 1) / NC; ++x) {
+      const int c = (tw - 1) + NC * x;
+      if (c < 2 * QMAX) {
+        const int qi = c < QMAX ? c : c - QMAX;
+        const int pc = 64 * qi + lane, r = pc / CPR, cc = (pc % CPR) ^ (r & (CPR - 1));
+        const unsigned off = (unsigned)((min(r, nl) * (int)rstride + cc * CH) * (int)sizeof(T));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c < QMAX ? rq : rk,
+                                                 (lds_void_t *)(s.qk + (c < QMAX ? 0 : SM::ROWB) + 1024 * qi), 16,
+                                                 off, 0, 0, 0);
+      }
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (tid < n) s.mask[tid] = my_mask;
+  __builtin_amdgcn_s_barrier();  // the counter is clear; the product waves may queue their loads
+  // keep every use of tw 0's loaded values (and the wait for them) after the barrier
+  asm volatile("" : "+v"(w_mask), "+v"(my_mask), "+v"(w_par), "+v"(w_a0), "+v"(w_b0), "+v"(w_a1), "+v"(w_b1));
 
-  // ---- 0b. wave 0, per node: link check, ancestors by depth, path gate, W1 weights -------
   uint32_t ancw[5] = {0u, 0u, 0u, 0u, 0u};  // slot of the ancestor at depth e, byte e
   int d_me = 0;
-  if (wave == 0) {
+  if (tw == 0) {
+    const auto gate = [](uint32_t x) { return BF16IN ? __uint_as_float(x << 16) : __uint_as_float(x); };
+    const float a0 = gate(w_a0), b0 = gate(w_b0), a1 = gate(w_a1), b1 = gate(w_b1);
+    if (lane < n) s.mask[lane] = my_mask;
+    if constexpr (RM == kMaxSlots) {
+      if (lane == 63 && n == kMaxSlots) s.mask[64] = w_mask;  // slot 64 has no lane of its own
+    }
+    if (lane == 0 && my_mask != 0ull) s.bad = 1;  // the root has no ancestors
     const bool tv = t_me < n;
-    const float a0 = to_f32(w_a0), b0 = to_f32(w_b0), a1 = to_f32(w_a1), b1 = to_f32(w_b1);
     const unsigned long long m = w_mask;
     d_me = __popcll(m);
     // the parent's mask is the node mask held by lane parent - 1 (the root's mask is zero)
@@ -318,7 +499,10 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
       ancw[e >> 2] |= (uint32_t)a << (8 * (e & 3));
       // gates of slot a: held by lane a, except t itself (slot 64 has no lane)
       float av = bperm_f32(a, a0), bv = bperm_f32(a, b0);
-      if (a == t_me) { av = a1; bv = b1; }
+      if (a == t_me) {
+        av = a1;
+        bv = b1;
+      }
       alp[e] = av;
       bet[e] = bv;
       g *= (e <= d_me) ? av : 1.f;
@@ -339,27 +523,19 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
       s.beta[0] = bet[0];
     }
   }
-  // q and k rows have landed; S0 and v may still be in flight
-  constexpr int kAfterQK = NS0 + NT;
-  static_assert(kAfterQK < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0070 | ((kAfterQK & 15) | ((kAfterQK >> 4) << 14)));  // vmcnt(..) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  tree_sync(&s.sync, &s.bad, kTreeWaves, lane);  // rows, masks, gates and cleared regions are in LDS
 
-  // ---- 1. Gram tiles [Q; K] K^T of the lower node triangle, dealt over the waves ----------
-  // Tile pair i = mt (mt + 1) / 2 + nt goes to wave NW - 1 - i % NW (wave 0, which has the
-  // path solve next, gets the fewest).  Transposed: lane (g, t) owns node t = 16 mt + l16 and
-  // gets k_s . k_t and k_s . q_t for s = 16 nt + 4 g + 0..3.  Entries of ancestor pairs are
-  // kept at depth(s) = (t's ancestors-or-self in slots 0..s) - 1 (the k.k ones times b_t, the
-  // factor the path solve applies); the rest go to padding entries 17..19.
-  if (wave == 1 && lane == 0 && s.mask[0] != 0ull) s.bad = 1;  // the root has no ancestors
+  // ---- Gram tiles [Q; K] K^T of the lower node triangle, dealt between the tree waves ----
+  // Transposed: lane (g, t) owns node t = 16 mt + l16 and gets k_s . k_t and k_s . q_t for
+  // s = 16 nt + 4 g + 0..3.  Entries of ancestor pairs are kept at depth(s) = (t's
+  // ancestors-or-self in slots 0..s) - 1 (the k.k ones times b_t, the factor the path solve
+  // applies); the rest go to padding entries 17..19.  Rows past the node count read finite
+  // or arbitrary LDS contents; the entries they produce are never kept.
 #pragma unroll
   for (int mt = 0; mt < NT; ++mt) {
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
-      if (wave != NW - 1 - (mt * (mt + 1) / 2 + nt) % NW || mt >= ntl) continue;
-      // Row fragments are read at the tile's rows as they are: rows past the node count hold
-      // finite values (copies of the last row, or the next LDS region), and the entries they
-      // produce are never kept.
+      if ((mt * (mt + 1) / 2 + nt) % kTreeWaves != kTreeWaves - 1 - tw || mt >= ntl) continue;
       const int tme = 16 * mt + l16, ra = min(tme, nl);
       const int rb = 16 * nt + l16;
       f32x4 gk4 = {0.f, 0.f, 0.f, 0.f}, gq4 = {0.f, 0.f, 0.f, 0.f};
@@ -369,13 +545,13 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
         row_frag<D, BF16IN>(qrow, tme, 32 * ks + 8 * g4, aqh, aql);
         row_frag<D, BF16IN>(krow, tme, 32 * ks + 8 * g4, akh, akl);
         row_frag<D, BF16IN>(krow, rb, 32 * ks + 8 * g4, bh, bl);
-        gk4 = mfma(bh, akh, gk4);
-        gq4 = mfma(bh, aqh, gq4);
+        gk4 = mfma_bf16(bh, akh, gk4);
+        gq4 = mfma_bf16(bh, aqh, gq4);
         if constexpr (!BF16IN) {
-          gk4 = mfma(bl, akh, gk4);
-          gk4 = mfma(bh, akl, gk4);
-          gq4 = mfma(bl, aqh, gq4);
-          gq4 = mfma(bh, aql, gq4);
+          gk4 = mfma_bf16(bl, akh, gk4);
+          gk4 = mfma_bf16(bh, akl, gk4);
+          gq4 = mfma_bf16(bl, aqh, gq4);
+          gq4 = mfma_bf16(bh, aql, gq4);
         }
       }
       const unsigned long long tmask = s.mask[ra];
@@ -404,11 +580,10 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
       }
     }
   }
-  lds_barrier();
+  tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the compact Gram rows are complete
 
-  // ---- 2. wave 0: path solve, one lane per node, and its W1 row (overlapping the S0 loads);
-  //         every wave: P_Q = Q S0 and P_K = K S0 for its channels on MFMA, and V' -----------
-  if (wave == 0) {
+  // ---- tw 0: path solve, one lane per node, then the node's Y and W1 rows (fp16) --------
+  if (tw == 0) {
     const bool tv = t_me < n;
     const int t = tn;
     const int dmax = wave_max_i32(tv ? d_me : 0);
@@ -417,7 +592,10 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
 #pragma unroll
     for (int v = 0; v < kAR / 4; ++v) {
       const float4 x = reinterpret_cast<const float4 *>(&s.mc[t * kAR])[v];
-      z[4 * v] = x.x; z[4 * v + 1] = x.y; z[4 * v + 2] = x.z; z[4 * v + 3] = x.w;
+      z[4 * v] = x.x;
+      z[4 * v + 1] = x.y;
+      z[4 * v + 2] = x.z;
+      z[4 * v + 3] = x.w;
     }
     // deepest ancestor first, two steps per group with the group's rows loaded together.
     // Beyond a lane's depth z is zero and the ancestor slot is the root, so those steps
@@ -446,165 +624,96 @@ __global__ __launch_bounds__(4 * D, (BF16IN && !S0LO ? 2 : 1) * D / 64) void ver
         }
       }
     }
-    // W1[t, anc e] = cw[e] z[e] into the (cleared) dense row, hi + lo bf16
     if (tv) {
 #pragma unroll
       for (int e = 0; e <= kMaxP; ++e) {
         if (e <= d_me) {
-          const float w = s.cwl[e][lane] * z[e];
-          const __bf16 hv = (__bf16)w;
-          const __bf16 lv = (__bf16)(w - (float)hv);
-          const int pos = t * SPW + w1_pos(anc_at(e));
-          w1h[pos] = __builtin_bit_cast(uint16_t, hv);
-          w1l[pos] = __builtin_bit_cast(uint16_t, lv);
+          const int a = anc_at(e);
+          const int pos = t * SPW + w1_pos(a);
+          s.w1[pos] = (_Float16)(s.cwl[e][lane] * z[e]);
+          s.y[pos] = (_Float16)(s.beta[a] * z[e]);
         }
       }
     }
-  } else if (wave == 1 && lane == 0) {
-    // the root: W1[0, 0] = b_0 (q_0 . k_0)
-    const float w = s.beta[0] * s.mc[0];
-    const __bf16 hv = (__bf16)w;
-    w1h[0] = __builtin_bit_cast(uint16_t, hv);
-    w1l[0] = __builtin_bit_cast(uint16_t, (__bf16)(w - (float)hv));
+  } else if (tw == 1 && lane == 0) {
+    // the root: Y[0, 0] = W1[0, 0] = b_0 (q_0 . k_0)
+    const _Float16 w = (_Float16)(s.beta[0] * s.mc[0]);
+    s.w1[0] = w;
+    s.y[0] = w;
   }
-  bf16x8 s0h[KS], s0l[KS];
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): Y and W1 are written
+  __builtin_amdgcn_s_barrier();        // (1) the product waves may form V^T W1^T
+
+  // ---- E = g (Q - Y K) on MFMA, channel tiles dealt over the tree waves, written as fp16
+  //      over the q rows --------------------------------------------------------------------
+  // Per channel tile ct: K^T in the C layout (lane (g, c): nodes 4 g + 0..3 of each 16-node
+  // tile at channel 16 ct + c) through products with the negated identity (exact), packed as
+  // the A operand; then E^T tile by node tile with Q^T as the initial C tile and Y^T as the
+  // B operand (Y is zero above the diagonal).  Lane (g, t) ends with E[t][16 ct + 4 g + 0..3].
+  static_assert(NW % kTreeWaves == 0, "channel tiles dealt evenly");
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const float x[8] = {s0r[ks][0][0], s0r[ks][0][1], s0r[ks][0][2], s0r[ks][0][3],
-                        s0r[ks][1][0], s0r[ks][1][1], s0r[ks][1][2], s0r[ks][1][3]};
-    if constexpr (S0LO) {
-      split8(x, s0h[ks], s0l[ks]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s0h[ks][e] = (__bf16)x[e];
-    }
-  }
-  // P_Q is kept transposed (lane (g, t) holds P_Q[t][16 wave + 4 g + 0..3]: the C layout of
-  // S0^T Q^T), P_K node-major (lane (g, c) holds P_K[4 g + 0..3][16 wave + c]).  Both come
-  // from the same registers: the S0 fragments are the A operand of one product and the B
-  // operand of the other, and so are the row fragments.
-  f32x4 pqt[NT], pk[NT];  // tiles past the node count are never read
-#pragma unroll
-  for (int mt = 0; mt < NT; ++mt) {
-    if (mt >= ntl) continue;
-    const int ra = 16 * mt + l16;  // rows past the node count: finite, never used
-    pqt[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    pk[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 aqh, aql, akh, akl;
-      row_frag<D, BF16IN>(qrow, ra, 32 * ks + 8 * g4, aqh, aql);
-      row_frag<D, BF16IN>(krow, ra, 32 * ks + 8 * g4, akh, akl);
-      pqt[mt] = mfma(s0h[ks], aqh, pqt[mt]);
-      pk[mt] = mfma(akh, s0h[ks], pk[mt]);
-      if constexpr (S0LO) {
-        pqt[mt] = mfma(s0l[ks], aqh, pqt[mt]);
-        pk[mt] = mfma(akh, s0l[ks], pk[mt]);
-      }
-      if constexpr (!BF16IN) {
-        pqt[mt] = mfma(s0h[ks], aql, pqt[mt]);
-        pk[mt] = mfma(akl, s0h[ks], pk[mt]);
-      }
-    }
-  }
-  // V' = V - g P_K for this wave's channels.  V enters the C tiles (lane (g, c): rows 4 g +
-  // 0..3 of channel c) through a product with the identity, and the result is packed as hi +
-  // lo bf16, the A operand of V'^T W1^T.
-  bf16x8 vph[KSS], vpl[KSS];
-  {
-    s16x4 ident;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ident[e] = (short)((4 * g4 + e == l16) ? 0x3f80 : 0);  // bf16 1
+  for (int cc = 0; cc < NW / kTreeWaves; ++cc) {
+    const int ct = tw + kTreeWaves * cc;
+    f16x8 kt[KSS];
 #pragma unroll
     for (int mt = 0; mt < 2 * KSS; ++mt) {
-      f32x4 vp = {0.f, 0.f, 0.f, 0.f};
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
       if (mt < NT && mt < ntl) {
-        const int mc_ = mt < NT ? mt : NT - 1;  // (static index; mt < NT here)
-        const float4 gm = *reinterpret_cast<const float4 *>(&s.gamma[16 * mt + 4 * g4]);
-        vp[0] = -gm.x * pk[mc_][0];
-        vp[1] = -gm.y * pk[mc_][1];
-        vp[2] = -gm.z * pk[mc_][2];
-        vp[3] = -gm.w * pk[mc_][3];
+        const int r = min(16 * mt + l16, nl);  // rows past the node count: zeroed below
         if constexpr (BF16IN) {
-          vp = mfma16(__builtin_bit_cast(s16x4, vld[mc_]), ident, vp);
-        } else {
-          const f32x4 x = __builtin_bit_cast(f32x4, vld[mc_]);
-          s16x4 vh, vl;
+          s16x4 nid;  // bf16 -1 on the diagonal
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const __bf16 hv = (__bf16)x[i];
-            vh[i] = __builtin_bit_cast(short, hv);
-            vl[i] = bf16_bits(x[i] - (float)hv);
+          for (int e = 0; e < 4; ++e) nid[e] = (short)((4 * g4 + e == l16) ? 0xbf80 : 0);
+          const s16x4 a = *reinterpret_cast<const s16x4 *>(krow + swz<D, 8>(r, 16 * ct + 4 * g4));
+          c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, nid, c, 0, 0, 0);
+        } else {
+          f16x4 nid, a;
+          const f32x4 kv = row4<D, false>(krow, r, 16 * ct + 4 * g4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            nid[e] = (_Float16)((4 * g4 + e == l16) ? -1.f : 0.f);
+            a[e] = (_Float16)kv[e];
           }
-          vp = mfma16(vh, ident, vp);
-          vp = mfma16(vl, ident, vp);
+          c = mfma16_f16(a, nid, c);
+        }
+        if (mt == ntl - 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * mt + 4 * g4 + i >= n) c[i] = 0.f;
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 hv = (__bf16)vp[i];
-        vph[mt >> 1][4 * (mt & 1) + i] = hv;
-        vpl[mt >> 1][4 * (mt & 1) + i] = (__bf16)(vp[i] - (float)hv);
-      }
+      for (int i = 0; i < 4; ++i) kt[mt >> 1][4 * (mt & 1) + i] = (_Float16)c[i];
     }
-  }
-  // W1 is complete
-  lds_barrier();
-  const bool bad = s.bad != 0;
-
-  // ---- 3. o^T = g P_Q^T + V'^T W1^T for this wave's value channels, node tile by node tile --
-  // A operand: V' (its registers are exactly the A layout of V'^T), B operand: W1 rows from
-  // LDS; W1 is zero above the diagonal, so node chunks past the tile are skipped.  Lane
-  // (g, t) ends with o[t][16 wave + 4 g + 0..3]: one 8-byte (bf16) store per tile, through a
-  // buffer whose range ends at the last node, so rows past the node count are dropped.  An
-  // inconsistent tree gives NaN outputs.
-  {
-    const int oes = p.out_bf16 ? 2 : 4;
-    const unsigned ostride = (unsigned)(p.H * D * oes);
-    char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
-    const int orange = (nl * p.H * D + D) * oes;
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
       if (mt >= ntl) break;
-      const int t = 16 * mt + l16, tr = t;  // W1 rows past the node count: never stored
-      const float gt = s.gamma[t];
-      f32x4 acc = gt * pqt[mt];
+      const int t = 16 * mt + l16;
+      const int tq = min(t, nl);
+      f32x4 acc = row4<D, BF16IN>(qrow, tq, 16 * ct + 4 * g4);
 #pragma unroll
       for (int kk = 0; kk < KSS; ++kk) {
         if (32 * kk > 16 * mt + 15) break;
-        const bf16x8 wh = frag16(w1h + tr * SPW + 32 * kk + 8 * g4);
-        const bf16x8 wl = frag16(w1l + tr * SPW + 32 * kk + 8 * g4);
-        acc = mfma(vph[kk], wh, acc);
-        acc = mfma(vpl[kk], wh, acc);
-        acc = mfma(vph[kk], wl, acc);
+        acc = mfma_f16(kt[kk], hfrag(s.y + tq * SPW + 32 * kk + 8 * g4), acc);
       }
-      if (bad) acc = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      const unsigned vo = (unsigned)t * ostride + (unsigned)((16 * wave + 4 * g4) * oes);
-      if (p.out_bf16) {
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[0]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[1]) << 16);
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[3]) << 16);
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, (int)vo, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), ro, (int)vo, 0, 0);
+      if (t < n) {
+        const float gt = s.gamma[t];
+        f16x4 ev;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ev[i] = (_Float16)(gt * acc[i]);
+        *reinterpret_cast<f16x4 *>(erow + swz<D, 8>(t, 16 * ct + 4 * g4)) = ev;
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): E is written
+  __builtin_amdgcn_s_barrier();        // (2) the product waves may read E
 }
 
 template <int D, bool BF16IN, int NT>
 hipError_t launch_one(const VerifyParams &p, hipStream_t stream) {
   const unsigned units = (unsigned)(p.L * p.B * p.H);
-  if constexpr (BF16IN) {
-    if (p.out_bf16) {
-      hipLaunchKernelGGL((verify_kernel<D, true, NT, false>), dim3(units), dim3(4 * D), 0, stream, p);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, true>), dim3(units), dim3(4 * D), 0, stream, p);
+  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT>), dim3(units), dim3(VerifyShape<D, BF16IN, NT>::NTH), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
