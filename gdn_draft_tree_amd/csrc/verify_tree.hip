@@ -334,12 +334,9 @@ void verify_kernel(VerifyParams p) {
         }
       }
     }
-    __builtin_amdgcn_s_barrier();  // (2) E is in LDS
-    const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
-
-    // ---- + S0^T E^T, once the state has landed --------------------------------------------
-    // The state is scaled by 2^(141 - ex) with ex >= the v exponent, so both scaled operands
-    // stay inside the fp16 range; the V^T W1^T part is rescaled to match (exact).
+    // The state, as soon as it has landed (before E is ready), is scaled by 2^(141 - ex) with
+    // ex >= the v exponent, so both scaled operands stay inside the fp16 range; the V^T W1^T
+    // part is rescaled to match (exact; nothing to do in the usual case ex == exv).
     float ms = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -354,7 +351,16 @@ void verify_kernel(VerifyParams p) {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int e = 0; e < 8; ++e) s0h[ks][e] = (_Float16)__builtin_amdgcn_ldexpf(s0r[ks][e >> 2][e & 3], 141 - ex);
+    if (ex != exv) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_amdgcn_ldexpf(acc[mt][i], exv - ex);
+    }
+    __builtin_amdgcn_s_barrier();  // (2) E is in LDS
+    const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
+    // ---- + S0^T E^T ------------------------------------------------------------------------
     // Lane (g, t) ends with o[t][16 wave + 4 g + 0..3]: one 8-byte (bf16) store per tile,
     // through a buffer whose range ends at the last node, so rows past the node count are
     // dropped.  An inconsistent tree gives NaN outputs.
@@ -368,8 +374,6 @@ void verify_kernel(VerifyParams p) {
       if (mt >= ntl) break;
       const int t = 16 * mt + l16;  // rows past the node count: never stored
       f32x4 o4 = acc[mt];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = __builtin_amdgcn_ldexpf(o4[i], exv - ex);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) o4 = mfma_f16(s0h[ks], hfrag(erow + swz<D, 8>(t, 32 * ks + 8 * g4)), o4);
 #pragma unroll
@@ -651,6 +655,9 @@ void verify_kernel(VerifyParams p) {
   // the A operand; then E^T tile by node tile with Q^T as the initial C tile and Y^T as the
   // B operand (Y is zero above the diagonal).  Lane (g, t) ends with E[t][16 ct + 4 g + 0..3].
   static_assert(NW % kTreeWaves == 0, "channel tiles dealt evenly");
+  // Straight-line code over all node tiles (rows past the node count are clamped, their K
+  // entries zeroed and their E rows never used), so the LDS reads of a channel tile can all
+  // be issued ahead of its products.
 #pragma unroll
   for (int cc = 0; cc < NW / kTreeWaves; ++cc) {
     const int ct = tw + kTreeWaves * cc;
@@ -658,28 +665,27 @@ void verify_kernel(VerifyParams p) {
 #pragma unroll
     for (int mt = 0; mt < 2 * KSS; ++mt) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      if (mt < NT && mt < ntl) {
-        const int r = min(16 * mt + l16, nl);  // rows past the node count: zeroed below
-        if constexpr (BF16IN) {
-          s16x4 nid;  // bf16 -1 on the diagonal
+      if constexpr (true) {
+        if (mt < NT) {
+          const int r = min(16 * mt + l16, nl);
+          if constexpr (BF16IN) {
+            s16x4 nid;  // bf16 -1 on the diagonal
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nid[e] = (short)((4 * g4 + e == l16) ? 0xbf80 : 0);
-          const s16x4 a = *reinterpret_cast<const s16x4 *>(krow + swz<D, 8>(r, 16 * ct + 4 * g4));
-          c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, nid, c, 0, 0, 0);
-        } else {
-          f16x4 nid, a;
-          const f32x4 kv = row4<D, false>(krow, r, 16 * ct + 4 * g4);
+            for (int e = 0; e < 4; ++e) nid[e] = (short)((4 * g4 + e == l16) ? 0xbf80 : 0);
+            const s16x4 a = *reinterpret_cast<const s16x4 *>(krow + swz<D, 8>(r, 16 * ct + 4 * g4));
+            c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, nid, c, 0, 0, 0);
+          } else {
+            f16x4 nid, a;
+            const f32x4 kv = row4<D, false>(krow, r, 16 * ct + 4 * g4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            nid[e] = (_Float16)((4 * g4 + e == l16) ? -1.f : 0.f);
-            a[e] = (_Float16)kv[e];
+            for (int e = 0; e < 4; ++e) {
+              nid[e] = (_Float16)((4 * g4 + e == l16) ? -1.f : 0.f);
+              a[e] = (_Float16)kv[e];
+            }
+            c = mfma16_f16(a, nid, c);
           }
-          c = mfma16_f16(a, nid, c);
-        }
-        if (mt == ntl - 1) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * mt + 4 * g4 + i >= n) c[i] = 0.f;
+          for (int i = 0; i < 4; ++i) c[i] = (16 * mt + 4 * g4 + i < n) ? c[i] : 0.f;
         }
       }
 #pragma unroll
@@ -687,7 +693,6 @@ void verify_kernel(VerifyParams p) {
     }
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
-      if (mt >= ntl) break;
       const int t = 16 * mt + l16;
       const int tq = min(t, nl);
       f32x4 acc = row4<D, BF16IN>(qrow, tq, 16 * ct + 4 * g4);
@@ -696,13 +701,12 @@ void verify_kernel(VerifyParams p) {
         if (32 * kk > 16 * mt + 15) break;
         acc = mfma_f16(kt[kk], hfrag(s.y + tq * SPW + 32 * kk + 8 * g4), acc);
       }
-      if (t < n) {
-        const float gt = s.gamma[t];
-        f16x4 ev;
+      const float gt = s.gamma[t];
+      f16x4 ev;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ev[i] = (_Float16)(gt * acc[i]);
-        *reinterpret_cast<f16x4 *>(erow + swz<D, 8>(t, 16 * ct + 4 * g4)) = ev;
-      }
+      for (int i = 0; i < 4; ++i) ev[i] = (_Float16)(gt * acc[i]);
+      // rows n..RM-1 are unused scratch; rows past RM do not exist
+      if (mt < NT - 1 || t < RM) *reinterpret_cast<f16x4 *>(erow + swz<D, 8>(t, 16 * ct + 4 * g4)) = ev;
     }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): E is written

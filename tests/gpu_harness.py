@@ -77,20 +77,26 @@ def assert_tree_equal(gt, ot):
         np.testing.assert_array_equal(gt["anc"][b, :n].view(np.uint64), ot["anc"][b, :n], err_msg=f"anc b={b}")
 
 
+def worst(errs) -> float:
+    """The largest error, with any NaN (a non-finite GPU result) reported as +inf: Python's
+    max() would silently skip it."""
+    a = np.asarray([np.max(e) for e in errs], dtype=np.float64)
+    return float("inf") if np.isnan(a).any() else float(a.max())
+
+
 def output_errors(g_o, o_ref, hnorm, n_nodes):
     """max over channels of |o_gpu - o_ref| / ||S_ref(t)||_F for every used (l, b, t, h)."""
     errs = []
     for b, n in enumerate(n_nodes):
         n = int(n)
-        e = np.abs(g_o[:, b, :n] - o_ref[:, b, :n]).max(-1) / hnorm[:, b, :n]
-        errs.append(e.max())
-    return float(max(errs))
+        errs.append(np.abs(g_o[:, b, :n] - o_ref[:, b, :n]).max(-1) / hnorm[:, b, :n])
+    return worst(errs)
 
 
 def state_errors(g_s, s_ref):
     num = np.abs(g_s - s_ref).max(axis=(-2, -1))
     den = np.sqrt((s_ref ** 2).sum(axis=(-2, -1)))
-    return float((num / den).max())
+    return worst([num / den])
 
 
 def check_all(w, out_dtype=None, gpu=None, ref=None):

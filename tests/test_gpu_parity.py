@@ -33,6 +33,7 @@ def test_tiny_full():
     ("ragged", 0, 4, None, None),           # N = 64: 65 rows, a ragged last node tile
     ("ragged", 2, 8, 16, None),
     ("deep", 0, 2, None, 48),               # 48 layers share one tree
+    ("ragged", 3, None, 24, None),          # 768 heads: more than one head per workgroup
 ])
 def test_configs(name, seed, heads, reqs, layers):
     w = generate(name, seed=seed, B=reqs)
@@ -61,7 +62,7 @@ def test_full_size_sampled(name):
     np.testing.assert_array_equal(gpu["acc_len"], acc_len)
     np.testing.assert_array_equal(gpu["acc_tok"], acc_tok)
     np.testing.assert_array_equal(gpu["acc_node"], acc_node)
-    worst_o = worst_s = 0.0
+    errs_o, errs_s = [], []
     for l in layers:
         for b in reqs:
             n = int(tree["n_nodes"][b])
@@ -73,10 +74,11 @@ def test_full_size_sampled(name):
                                                a[:, None], bb[:, None], h0[None])
                 hn = np.sqrt((st[:, 0] ** 2).sum(axis=(-2, -1)))
                 err = np.abs(gpu["o"][l, b, :n, h] - ou[:, 0]).max(-1) / hn
-                worst_o = max(worst_o, float(err.max()))
+                errs_o.append(err)
                 u = int(acc_node[b, int(acc_len[b]) - 1])
                 se = np.abs(gpu["state"][l, b, h] - st[u, 0]).max() / np.linalg.norm(st[u, 0])
-                worst_s = max(worst_s, float(se))
+                errs_s.append(se)
+    worst_o, worst_s = H.worst(errs_o), H.worst(errs_s)
     _say(f"{name} full size: sampled out_err={worst_o:.2e} state_err={worst_s:.2e}")
     assert worst_o <= H.TOL and worst_s <= H.TOL
 

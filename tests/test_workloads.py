@@ -60,3 +60,11 @@ def test_resolve_target():
     # slot 0: depth 0, rank 1 -> lat_tok[0][1]; slot 1: depth 1, rank 0 -> lat_tok[1][0];
     # slot 2: uniform choice; slot 3: depth 2 == P -> uniform; slot 4 unused -> uniform
     assert t.tolist() == [[101, 103, 9, 10, 11]]
+
+
+def test_error_reduction_reports_nan_as_failure():
+    """A NaN GPU result must fail the parity bar, not vanish in a max()."""
+    import numpy as np
+    from tests.gpu_harness import worst
+    assert worst([np.array([1e-4, 2e-4]), np.array([3e-4])]) == 3e-4
+    assert worst([np.array([1e-4, np.nan])]) == float("inf")
