@@ -89,8 +89,11 @@ gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
  *     S_t = alpha_t (I - beta_t k_t k_t^T) S_p + beta_t k_t v_t^T,    o_t = S_t^T q_t
  * (SpecPilot summary, Prerequisites > hybrid recurrent architecture).  Node states are
  * derived along root paths from h0 and never written to memory (no per-node snapshots);
- * only o is written.  No 1/sqrt(d_k) scale is applied.  The result is exact up to fp32
- * rounding and reduction order.
+ * only o is written.  No 1/sqrt(d_k) scale is applied.  Arithmetic: gates, path solves and
+ * accumulation in fp32; the matrix products take fp16 operands (bf16 rows convert exactly;
+ * the state and v are scaled by a power of two per 16 value channels, so any finite scale
+ * fits), which keeps the error within 2e-3 of each node state's Frobenius norm for
+ * L2-normalised q and k, alpha and beta in [0, 1] (the Gated DeltaNet setting).
  *
  * Reads tree.parent, tree.anc and tree.n_nodes only (the ancestor bitmask gives each
  * node's depth and ancestors).  A request whose tree is inconsistent (parent[t] >= t,
