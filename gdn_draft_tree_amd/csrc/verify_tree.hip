@@ -24,16 +24,19 @@
 //
 // Work decomposition: one workgroup per (layer, request, head) with two kinds of waves.
 //  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they only stream
-//    this head's committed state and v rows into registers, wait at the workgroup's one
-//    barrier, then form o^T = S0^T E^T + V^T W1^T on MFMA and store.
-//  * two tree waves: they stream the q and k rows into LDS (buffer loads to LDS), then
-//    compute the Gram tiles [Q; K] K^T of the lower node triangle (dealt between them),
-//    the per-node path solves (one lane per node) that give Y and W1, and E on MFMA, and
-//    arrive at the barrier.  The two tree waves order their phases through an LDS counter.
-// A product wave that issues its state loads stalls until the memory pipeline accepts
-// them, so the waves that carry the latency-bound tree work issue only the small row
-// loads (and run at raised priority).  When the state lands, only one dense product and
-// the stores remain.
+//    this head's committed state and v rows into registers, form V^T W1^T once W1 is in
+//    LDS, convert the state to fp16 as it lands, and once E is in LDS add S0^T E^T.
+//  * four tree waves: wave 0 loads the per-node inputs and does the per-node prologue; waves
+//    1..3 stream the q and k rows into LDS (buffer loads to LDS).  Together they compute the
+//    Gram tiles [Q; K] K^T of the lower node triangle, then wave 0 does the per-node path
+//    solves (one lane per node) that give Y and W1, and all four form E on MFMA.  They order
+//    their phases through an LDS counter.
+// A first workgroup barrier orders the loads (below); three more hand over W1, then E, then
+// the finished output rows, which are staged in LDS and stored as whole rows by every wave.
+// A product wave that issues its
+// state loads stalls until the memory pipeline accepts them, so the waves that carry the
+// latency-bound tree work issue only the small row loads, ahead of the state (and run at
+// raised priority).  When the state lands, only one dense product and the stores remain.
 //
 // Precision: MFMA operands are fp16 with fp32 accumulation.  Rows in bf16 convert to fp16
 // exactly; the state and v columns of a product wave are scaled by one power of two (from
@@ -193,8 +196,8 @@ __device__ __forceinline__ float bperm_f32(int lane_src, float x) {
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 
-// The two tree waves meet here: each finishes its own memory work (loads into LDS
-// included), counts itself in, and waits for the other.  The wait is bounded; a wave that
+// The tree waves meet here: each finishes its own memory work (loads into LDS included),
+// counts itself in, and waits for the others.  The wait is bounded; a wave that
 // gives up marks the request bad (NaN outputs) instead of hanging.
 __device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int lane) {
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
@@ -206,6 +209,24 @@ __device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int la
       *bad = 1;
       break;
     }
+  }
+}
+
+// Output rows of one head, staged in LDS with swizzled 16-byte chunks, stored as whole rows
+// (16-byte pieces, consecutive lanes along a row) by every wave of the workgroup.
+template <int D>
+__device__ __forceinline__ void store_rows(const VerifyParams &p, const unsigned char *stage, int n,
+                                           size_t rowbase, int h, int tid, int nth) {
+  const int oes = p.out_bf16 ? 2 : 4;
+  const int cpr = D * oes / 16;  // 16-byte chunks per row: a power of two
+  const unsigned ostride = (unsigned)(p.H * D * oes);
+  char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
+  const int orange = ((n - 1) * p.H * D + D) * oes;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
+  for (int c = tid; c < n * cpr; c += nth) {
+    const int r = c / cpr, lc = c % cpr;
+    const u32x4 x = *reinterpret_cast<const u32x4 *>(stage + 16 * (r * cpr + (lc ^ (r & (cpr - 1)))));
+    __builtin_amdgcn_raw_buffer_store_b128(x, ro, (int)((unsigned)r * ostride + 16u * lc), 0, 0);
   }
 }
 
@@ -238,6 +259,10 @@ void verify_kernel(VerifyParams p) {
   const int nb = (int)(n * rstride * sizeof(T));  // byte range of this head's used rows
   // fp16 rows of E (same swizzled layout as bf16 rows)
   _Float16 *erow = reinterpret_cast<_Float16 *>(BF16IN ? s.qk : s.e16);
+  // Output rows are staged from the k rows on: once E is formed nothing reads the k rows, Y,
+  // W1 or the compact Gram rows again.
+  unsigned char *ostage = s.qk + SM::ROWB;
+  static_assert(offsetof(SM, mask) - SM::ROWB >= (size_t)SM::RM * D * 4, "output staging fits");
 
   if (wave < NW) {
     // ================================ product waves ==================================
@@ -361,35 +386,33 @@ void verify_kernel(VerifyParams p) {
     const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
     // ---- + S0^T E^T ------------------------------------------------------------------------
-    // Lane (g, t) ends with o[t][16 wave + 4 g + 0..3]: one 8-byte (bf16) store per tile,
-    // through a buffer whose range ends at the last node, so rows past the node count are
-    // dropped.  An inconsistent tree gives NaN outputs.
-    const int oes = p.out_bf16 ? 2 : 4;
-    const unsigned ostride = (unsigned)(p.H * D * oes);
-    char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
-    const int orange = (nl * p.H * D + D) * oes;
-    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
+    // Lane (g, t) ends with o[t][16 wave + 4 g + 0..3], written into the output rows staged in
+    // LDS (rows past the node count are not written).  An inconsistent tree gives NaN outputs.
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
       if (mt >= ntl) break;
-      const int t = 16 * mt + l16;  // rows past the node count: never stored
+      const int t = 16 * mt + l16;
       f32x4 o4 = acc[mt];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) o4 = mfma_f16(s0h[ks], hfrag(erow + swz<D, 8>(t, 32 * ks + 8 * g4)), o4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) o4[i] = __builtin_amdgcn_ldexpf(o4[i], ex - 141);
       if (bad) o4 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      const unsigned vo = (unsigned)t * ostride + (unsigned)((16 * wave + 4 * g4) * oes);
-      if (p.out_bf16) {
-        const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[0]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[1]) << 16);
-        const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[2]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[3]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, ro, (int)vo, 0, 0);
-      } else {
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o4), ro, (int)vo, 0, 0);
+      if (t < n) {
+        if (p.out_bf16) {
+          const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[0]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[1]) << 16);
+          const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[2]) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[3]) << 16);
+          *reinterpret_cast<u32x2 *>(ostage + 2 * swz<D, 8>(t, 16 * wave + 4 * g4)) = u32x2{lo, hi};
+        } else {
+          *reinterpret_cast<f32x4 *>(ostage + 4 * swz<D, 4>(t, 16 * wave + 4 * g4)) = o4;
+        }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's output rows are staged
+    __builtin_amdgcn_s_barrier();        // (3) every output row is staged
+    store_rows<D>(p, ostage, n, rowbase, h, 64 * wave + lane, 64 * (NW + kTreeWaves));
     return;
   }
 
@@ -711,6 +734,8 @@ void verify_kernel(VerifyParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): E is written
   __builtin_amdgcn_s_barrier();        // (2) the product waves may read E
+  __builtin_amdgcn_s_barrier();        // (3) every output row is staged
+  store_rows<D>(p, ostage, n, rowbase, h, 64 * wave + lane, 64 * (NW + kTreeWaves));
 }
 
 template <int D, bool BF16IN, int NT>
