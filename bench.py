@@ -12,7 +12,8 @@ than the 256 MB last-level cache), so each step reads its rows and states from H
 Prints ONE JSON line.  value = verified (node, layer) pairs per second over whole steps.
 roofline: the verify kernel (the dominant one), algorithmic bytes per launch / its mean
 duration, from HIP events on the launch stream around the same launches run back to back.
-cpu_baseline: the fp64 oracle on a bounded sample of the same workload, on the host.
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload, on the host, in worker
+processes (one request per task), with a single-process figure beside it.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload ragged]
 """
@@ -63,29 +64,67 @@ def commit_bytes(cfg, tau_total: int) -> int:
     return cfg.L * cfg.H * (cfg.B * 8 * cfg.D * cfg.D + tau_total * (2 * cfg.D * e + 2 * e))
 
 
-def cpu_baseline(name: str, reqs: int) -> dict:
+# The workload the CPU baseline's worker processes share (set before they are forked).
+_CPU_WORK: dict = {}
+
+
+def _oracle_on_requests(job):
+    """Worker: the oracle's whole pipeline on requests [b0, b1) and layers [l0, l1) of one
+    generated workload."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
-    from workloads import generate, resolve_target
-    w = generate(name, seed=0, B=reqs)
-    cfg = w.cfg
+    from workloads import resolve_target
+    seed, b0, b1, l0, l1 = job
+    w, x = _CPU_WORK[seed]
+    sl, ll = slice(b0, b1), slice(l0, l1)
+    lat_tok, tch, tun = w.lat_tok[sl], w.tgt_choice[sl], w.tgt_uniform[sl]
 
     def target_fn(tree):
-        return resolve_target(tree["depth"], tree["n_nodes"], w.lat_tok, w.tgt_choice, w.tgt_uniform)
+        return resolve_target(tree["depth"], tree["n_nodes"], lat_tok, tch, tun)
 
-    args = (w.lat_logp, w.lat_tok, w.root_tok, cfg.N, w.f64("q"), w.f64("k"), w.f64("v"),
-            w.f64("alpha"), w.f64("beta"), w.h0.double().numpy())
     with threadpool_limits(limits=1):
+        r = oracle.pipeline(w.lat_logp[sl], lat_tok, w.root_tok[sl], w.cfg.N, x["q"][ll, sl], x["k"][ll, sl],
+                            x["v"][ll, sl], x["alpha"][ll, sl], x["beta"][ll, sl], x["h0"][ll, sl], target_fn)
+    return int(np.asarray(r["tree"]["n_nodes"]).sum()) * (l1 - l0)
+
+
+def cpu_baseline(name: str, reqs: int, seeds: int, workers: int) -> dict:
+    """The fp64 oracle (unchanged) timed on the host: once in one process on `reqs` requests,
+    and in up to `workers` forked processes over `seeds` x `reqs` requests split into (request,
+    layer) tasks (each runs the oracle's full pipeline on one request and one layer, BLAS
+    limited to one thread). Runs before the GPU is touched, so forking is safe."""
+    import multiprocessing as mp
+
+    from workloads import generate
+    for s in range(seeds):  # inputs widened to fp64 up front, outside the timed region
+        w = generate(name, seed=s, B=reqs)
+        _CPU_WORK[s] = (w, {f: w.f64(f) for f in ("q", "k", "v", "alpha", "beta", "h0")})
+    L = _CPU_WORK[0][0].cfg.L
+    t0 = time.perf_counter()
+    nodes1 = _oracle_on_requests((0, 0, reqs, 0, L))
+    dt1 = time.perf_counter() - t0
+    jobs = [(s, b, b + 1, l, l + 1) for s in range(seeds) for b in range(reqs) for l in range(L)]
+    workers = min(workers, len(jobs))
+    with mp.get_context("fork").Pool(workers) as pool:
+        pool.map(abs, range(workers))  # workers started before the clock
         t0 = time.perf_counter()
-        r = oracle.pipeline(*args, target_fn)
+        nodes = sum(pool.map(_oracle_on_requests, jobs, chunksize=1))
         dt = time.perf_counter() - t0
-    nodes = int(np.asarray(r["tree"]["n_nodes"]).sum()) * cfg.L
-    return {"value": nodes / dt, "unit": "nodes/s", "cores": 1, "kind": "oracle",
-            "sample": f"{name} workload (seed 0), its first {reqs} requests: the full "
-                      f"build+verify+accept+commit pipeline in fp64 numpy, {dt:.1f} s, "
-                      f"BLAS limited to 1 thread"}
+    model = ""
+    try:
+        model = next(x.split(":", 1)[1].strip() for x in open("/proc/cpuinfo") if x.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    _CPU_WORK.clear()
+    return {"value": nodes / dt, "unit": "nodes/s", "cores": workers, "kind": "oracle",
+            "sample": f"{name} workload, seeds 0..{seeds - 1}, the first {reqs} requests of each "
+                      f"({seeds * reqs} requests x {L} layers): the oracle's full build+verify+accept+commit "
+                      f"pipeline in fp64 numpy, one (request, layer) per task over {workers} worker "
+                      f"processes (BLAS 1 thread each), {dt:.1f} s wall",
+            "value_1core": nodes1 / dt1, "sample_1core": f"seed 0, {reqs} requests x {L} layers in one process, {dt1:.1f} s",
+            "cpu_model": model}
 
 
 def main():
@@ -95,7 +134,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ragged")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated through (0: auto)")
-    ap.add_argument("--cpu-reqs", type=int, default=32, help="requests of the workload the oracle runs on the host")
+    ap.add_argument("--cpu-reqs", type=int, default=32, help="requests per seed the oracle runs on the host")
+    ap.add_argument("--cpu-seeds", type=int, default=4, help="input seeds of the multi-process oracle run")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: the CPUs this process may use, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB copy kernel (dst = src * 1), the reference "
@@ -106,6 +148,12 @@ def main():
               "multi-GPU mode (the verify step shards by request or head with no exchange).",
               file=sys.stderr)
         sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, len(os.sched_getaffinity(0)))
+        cfg0 = __import__("workloads").CONFIGS[args.workload]
+        cpu = cpu_baseline(args.workload, min(args.cpu_reqs, cfg0.B), args.cpu_seeds, workers)
 
     import numpy as np
     import torch
@@ -198,6 +246,25 @@ def main():
     torch.cuda.synchronize()
     t_verify = e0.elapsed_time(e1) * 1e3 / args.steps
 
+    # a real model calls verify once per layer: for stacked layers, the same work as L launches
+    # of one layer each (back to back, rotating input sets)
+    t_verify_layers = None
+    if cfg.L > 1:
+        nl = max(1, args.steps // 5)
+        e0.record(stream)
+        for i in range(nl):
+            d = sets[(args.warmup + i) % nsets]
+            for l in range(cfg.L):
+                sl = slice(l, l + 1)
+                g.gdntree_verify(d["tree"], d["q"][sl], d["k"][sl], d["v"][sl], d["alpha"][sl], d["beta"][sl],
+                                 d["state"][sl], o=d["o"][sl], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_verify_layers = e0.elapsed_time(e1) * 1e3 / nl
+
+    depth = np.concatenate([d["tree"].depth.cpu().numpy()[b, :int(n)] for d in sets
+                            for b, n in enumerate(d["tree"].n_nodes.cpu().numpy())])
+    tau_all = np.concatenate([d["acc"][0].cpu().numpy() for d in sets])
     n_nodes = [int(d["tree"].n_nodes.sum()) for d in sets]
     taus = [int(d["acc"][0].sum()) for d in sets]
     nodes_per_step = float(np.mean(n_nodes)) * cfg.L
@@ -221,13 +288,18 @@ def main():
                        "verify_back_to_back": t_verify},
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
         "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),
+        "verify_draft_nodes_per_s": (nodes_per_step - cfg.B * cfg.L) / (t_verify * 1e-6),
+        "verify_per_layer_launches_us": t_verify_layers,
+        "tree": {"depth_max": int(depth.max()), "depth_mean": float(depth.mean()),
+                 "depth_hist": np.bincount(depth).tolist(),
+                 "tau_hist": np.bincount(tau_all, minlength=2)[1:].tolist()},
         "tau_mean": float(np.mean(taus)) / cfg.B,
         "precision": "bf16 rows and outputs; fp32 state, gates, path solve and accumulation; MFMA "
                      "operands in fp16 (state and v columns scaled by a power of two per 16-channel "
                      "slice); fp64 tree scores",
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, min(args.cpu_reqs, cfg.B))
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -127,7 +127,12 @@ __global__ __launch_bounds__(256) void accept_commit_kernel(CommitParams p) {
     }
   }
 #pragma unroll
-  for (int m = 0; m < F4; ++m) *reinterpret_cast<float4 *>(col + 4 * (sub + 8 * m)) = st[m];
+  // Non-temporal stores: the committed state is next read by the following step's verify, long
+  // after this batch's other traffic, so it is written through instead of lingering dirty in
+  // the caches (measured: the next verify runs 1.3-1.4 us faster, the commit no slower).
+  for (int m = 0; m < F4; ++m)
+    __builtin_nontemporal_store(f32x4{st[m].x, st[m].y, st[m].z, st[m].w},
+                                reinterpret_cast<f32x4 *>(col + 4 * (sub + 8 * m)));
 }
 
 template <int D, bool BF16IN>
