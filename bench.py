@@ -1,7 +1,12 @@
 """Throughput of the draft-tree verification step on one MI355X.
 
-A step is one pass of the whole path over one batch: gdntree_build -> gdntree_verify ->
-gdntree_accept_commit.  The default workload is the large ragged batch: 32 requests x one
+A step is one pass of the whole path over one batch: tree build, verify, acceptance and
+state commit.  Steps are pipelined the way a decode loop can run them: gdntree_verify ->
+gdntree_accept -> gdntree_commit_build, where the last call commits this step's states and
+builds the next batch's tree in one launch (the next build needs only this step's
+acceptance: it stands for the next draft, which needs the accepted tokens); the next verify
+runs after it.  The same steps strictly in order
+(build -> verify -> accept_commit) are reported beside it as `sequential`.  The default workload is the large ragged batch: 32 requests x one
 GDN layer (32 heads, d = 128), 16-position x top-16 lattices, N = 64 draft nodes per
 request, bf16 rows, fp32 state.  The synthetic target argmax (the stand-in for the target
 model's LM head) is resolved once per input set, untimed, from the deterministic tree.
@@ -208,8 +213,30 @@ def main():
         if events:
             events[3].record(stream)
 
+    # Pipelined steps: the end of a step is split into acceptance and commit, and the commit
+    # runs in one launch with the next batch's tree build (which needs only this step's
+    # acceptance: it stands for the next draft, which needs the accepted tokens); the next
+    # verify runs after that launch.  One stream, no events.
+    def run_pipelined(i0, k):
+        d0 = sets[i0 % nsets]
+        g.gdntree_build(d0["lat_logp"], d0["lat_tok"], d0["root_tok"], cfg.N, out=d0["tree"], stream=stream)
+        for i in range(i0, i0 + k):
+            d = sets[i % nsets]
+            g.gdntree_verify(d["tree"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o=d["o"],
+                             stream=stream)
+            g.gdntree_accept(d["tree"], d["target"], cfg.P, acc=d["acc"], stream=stream)
+            if i + 1 < i0 + k:
+                dn = sets[(i + 1) % nsets]
+                g.gdntree_commit_build(d["tree"], d["acc"][0], d["acc"][2], d["k"], d["v"], d["alpha"], d["beta"],
+                                       d["state"], cfg.P, dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N,
+                                       dn["tree"], stream=stream)
+            else:
+                g.gdntree_commit(d["tree"], d["acc"][0], d["acc"][2], d["k"], d["v"], d["alpha"], d["beta"],
+                                 d["state"], cfg.P, stream=stream)
+
     for i in range(args.warmup):
         step(i)
+    run_pipelined(0, args.warmup)
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -218,12 +245,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # whole-step throughput (no events inside the timed region)
+    # whole-step throughput (no timing events inside the timed region): pipelined steps (the
+    # reported value), then the same steps strictly one after the other
+    t0 = time.perf_counter()
+    run_pipelined(args.warmup, args.steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_seq = time.perf_counter() - t0
 
     # per-kernel durations with HIP events on the launch stream
     for i in range(args.steps):
@@ -269,6 +301,7 @@ def main():
     taus = [int(d["acc"][0].sum()) for d in sets]
     nodes_per_step = float(np.mean(n_nodes)) * cfg.L
     ms = elapsed / args.steps * 1e3
+    ms_seq = elapsed_seq / args.steps * 1e3
     vbytes = float(np.mean([verify_bytes(cfg, n, e) for n in n_nodes]))
     cbytes = float(np.mean([commit_bytes(cfg, t) for t in taus]))
     achieved = vbytes / (t_verify * 1e-6) / 1e9
@@ -286,6 +319,10 @@ def main():
                      "mean_us_in_step": t_verify_step},
         "kernels_us": {"build": t_build, "verify": t_verify_step, "accept_commit": t_commit,
                        "verify_back_to_back": t_verify},
+        "sequential": {"ms_per_step": ms_seq, "value": nodes_per_step / (ms_seq * 1e-3),
+                       "order": "build -> verify -> accept_commit, each step after the previous one"},
+        "pipelining": "build -> verify(i) -> accept(i) -> [commit(i) + build(i+1) in one launch] -> "
+                      "verify(i+1) ...; one stream",
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
         "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),
         "verify_draft_nodes_per_s": (nodes_per_step - cfg.B * cfg.L) / (t_verify * 1e-6),

@@ -4,11 +4,12 @@ target, as hand-written gfx950 (MI355X) HIP kernels behind a C ABI (include/gdnt
     tree = gdntree_build(lat_logp, lat_tok, root_tok, N)
     o    = gdntree_verify(tree, q, k, v, alpha, beta, state)          # per GDN layer
     acc  = gdntree_accept_commit(tree, target_argmax, k, v, alpha, beta, state, P)
+    # or, split: acc = gdntree_accept(tree, target_argmax, P); gdntree_commit(tree, acc[0], acc[2], ...)
 
 Importing this package loads libgdntree.so and raises if it has not been built.
 """
 from ._binding import (EXPORTED, GDNTREE_BF16, GDNTREE_ERR_ARG, GDNTREE_ERR_DEVICE,  # noqa: F401
                        GDNTREE_ERR_UNSUPPORTED, GDNTREE_F32, GDNTREE_OK, LIB, LIB_PATH, CTree,
-                       GdnTreeError, Tree, gdntree_accept_commit, gdntree_build,
-                       gdntree_status_str, gdntree_verify)
+                       GdnTreeError, Tree, gdntree_accept, gdntree_accept_commit, gdntree_build,
+                       gdntree_commit, gdntree_commit_build, gdntree_status_str, gdntree_verify)
 from .layout import state_from_math, state_to_math  # noqa: F401

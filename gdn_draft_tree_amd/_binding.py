@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libgdntree.so")
 
 GDNTREE_OK, GDNTREE_ERR_ARG, GDNTREE_ERR_UNSUPPORTED, GDNTREE_ERR_DEVICE = 0, 1, 2, 3
 GDNTREE_F32, GDNTREE_BF16 = 0, 1
-EXPORTED = ("gdntree_build", "gdntree_verify", "gdntree_accept_commit", "gdntree_status_str")
+EXPORTED = ("gdntree_build", "gdntree_verify", "gdntree_accept_commit", "gdntree_accept", "gdntree_commit",
+            "gdntree_commit_build", "gdntree_status_str")
 
 
 class GdnTreeError(RuntimeError):
@@ -45,6 +46,13 @@ def _load() -> ctypes.CDLL:
     lib.gdntree_accept_commit.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp,
                                           vp, vp, vp, vp]
     lib.gdntree_accept_commit.restype = i
+    lib.gdntree_accept.argtypes = [CTree, i, i, i, vp, vp, vp, vp, vp]
+    lib.gdntree_accept.restype = i
+    lib.gdntree_commit.argtypes = [CTree, i, i, i, vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp]
+    lib.gdntree_commit.restype = i
+    lib.gdntree_commit_build.argtypes = [CTree, i, i, i, vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp,
+                                         vp, vp, vp, i, i, i, i, CTree, vp]
+    lib.gdntree_commit_build.restype = i
     lib.gdntree_status_str.argtypes = [i]
     lib.gdntree_status_str.restype = ctypes.c_char_p
     return lib
@@ -187,3 +195,71 @@ def gdntree_accept_commit(tree: Tree, target_argmax, k, v, alpha, beta, state, P
     _check(LIB.gdntree_accept_commit(tree.c(), B, R - 1, P, tp, L, H, D, D, _code(dt), *ptrs, sp,
                                      *ap, _stream(stream)))
     return acc_len, acc_tok, acc_node
+
+
+def _acc_buffers(B: int, P: int, device, acc=None):
+    if acc is None:
+        acc = (torch.empty(B, dtype=torch.int32, device=device),
+               torch.empty(B, P + 1, dtype=torch.int32, device=device),
+               torch.empty(B, P + 1, dtype=torch.int32, device=device))
+    return acc
+
+
+def gdntree_accept(tree: Tree, target_argmax, P: int, acc=None, stream=None):
+    """Greedy acceptance + bonus only (no state is touched).
+
+    Returns (acc_len [B], acc_tok [B][P+1], acc_node [B][P+1]) int32 device tensors.
+    """
+    B, R = target_argmax.shape
+    acc_len, acc_tok, acc_node = _acc_buffers(B, P, target_argmax.device, acc)
+    tp = _dev(target_argmax, "target_argmax", torch.int32, (B, R))
+    ap = (_dev(acc_len, "acc_len", torch.int32, (B,)),
+          _dev(acc_tok, "acc_tok", torch.int32, (B, P + 1)),
+          _dev(acc_node, "acc_node", torch.int32, (B, P + 1)))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match target_argmax")
+    _check(LIB.gdntree_accept(tree.c(), B, R - 1, P, tp, *ap, _stream(stream)))
+    return acc_len, acc_tok, acc_node
+
+
+def gdntree_commit(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state, P: int, stream=None):
+    """In-place commit of the state along an accepted path from gdntree_accept."""
+    L, B, R, H, D = k.shape
+    dt = k.dtype
+    lp = _dev(acc_len, "acc_len", torch.int32, (B,))
+    np_ = _dev(acc_node, "acc_node", torch.int32, (B, P + 1))
+    ptrs = [_dev(x, nm, dt, (L, B, R, H, D)) for x, nm in ((k, "k"), (v, "v"))]
+    ptrs += [_dev(x, nm, dt, (L, B, R, H)) for x, nm in ((alpha, "alpha"), (beta, "beta"))]
+    sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match the rows")
+    _check(LIB.gdntree_commit(tree.c(), B, R - 1, P, lp, np_, L, H, D, D, _code(dt), *ptrs, sp,
+                              _stream(stream)))
+
+
+def gdntree_commit_build(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state, P: int,
+                         next_lat_logp, next_lat_tok, next_root_tok, next_N: int, next_out: Tree,
+                         stream=None):
+    """gdntree_commit of this step and gdntree_build of the next step's tree into `next_out`,
+    in one launch (enqueue after this step's gdntree_accept)."""
+    L, B, R, H, D = k.shape
+    dt = k.dtype
+    lp = _dev(acc_len, "acc_len", torch.int32, (B,))
+    np_ = _dev(acc_node, "acc_node", torch.int32, (B, P + 1))
+    ptrs = [_dev(x, nm, dt, (L, B, R, H, D)) for x, nm in ((k, "k"), (v, "v"))]
+    ptrs += [_dev(x, nm, dt, (L, B, R, H)) for x, nm in ((alpha, "alpha"), (beta, "beta"))]
+    sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match the rows")
+    Bn, Pn, Kn = next_lat_logp.shape
+    nl = _dev(next_lat_logp, "next_lat_logp", torch.float32, (Bn, Pn, Kn))
+    nt = _dev(next_lat_tok, "next_lat_tok", torch.int32, (Bn, Pn, Kn))
+    nr = _dev(next_root_tok, "next_root_tok", torch.int32, (Bn,))
+    if next_out.B != Bn or next_out.N != next_N:
+        raise ValueError("next_out does not match the next lattice")
+    for f in ("parent", "depth", "rank", "token", "score", "anc"):
+        _dev(getattr(next_out, f), f, None, (Bn, next_N + 1))
+    _dev(next_out.n_nodes, "n_nodes", torch.int32, (Bn,))
+    _check(LIB.gdntree_commit_build(tree.c(), B, R - 1, P, lp, np_, L, H, D, D, _code(dt), *ptrs, sp,
+                                    nl, nt, nr, Bn, Pn, Kn, next_N, next_out.c(), _stream(stream)))
+    return next_out

@@ -51,7 +51,7 @@ struct VerifyParams {
 hipError_t launch_verify(const VerifyParams &p, hipStream_t stream);
 
 struct CommitParams {
-  const int32_t *parent, *token, *n_nodes, *target;
+  const int32_t *parent, *token, *n_nodes, *target;  // target: acceptance only
   const void *k, *v, *alpha, *beta;
   float *state;
   int32_t *acc_len, *acc_tok, *acc_node;
@@ -59,5 +59,10 @@ struct CommitParams {
   int in_bf16;
 };
 hipError_t launch_accept_commit(const CommitParams &p, hipStream_t stream);
+hipError_t launch_accept(const CommitParams &p, hipStream_t stream);  // acceptance only
+hipError_t launch_commit(const CommitParams &p, hipStream_t stream);  // commit of a given path
+struct BuildParams;
+// commit of a given path (p) fused with the build of nb other requests' trees (bp)
+hipError_t launch_commit_build(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream);
 
 }  // namespace gdntree

@@ -7,6 +7,8 @@
  *   gdntree_verify         gated-delta-rule outputs of every tree node, per GDN layer
  *   gdntree_accept_commit  greedy acceptance of the longest matching root path plus a
  *                          bonus token, then the accepted-path state commit
+ * gdntree_accept_commit also comes as two calls, gdntree_accept then gdntree_commit, and
+ * gdntree_commit_build runs a commit together with the next step's tree build in one launch.
  *
  * Sources: the SpecPilot paper summary (paper.rainbus.top, "SpecPilot: Autonomous
  * Algorithm Discovery and Systems Optimization for Speculative Decoding"), sections
@@ -140,6 +142,61 @@ gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, int N, int P,
                                      const void *v, const void *alpha, const void *beta,
                                      float *state, int32_t *acc_len, int32_t *acc_tok,
                                      int32_t *acc_node, void *stream);
+
+/*
+ * gdntree_accept - the acceptance half of gdntree_accept_commit on its own (one wave per
+ * request): the same acc_len, acc_tok and acc_node, and no state is touched.  With
+ * gdntree_commit it splits a step's end in two, so that work that needs only the accepted
+ * tokens (the next draft and tree build) can start on another stream while the states are
+ * being committed.  Reads tree.parent, tree.token, tree.n_nodes and target_argmax; a request
+ * with n_nodes outside [1, N+1] gets no output.
+ */
+gdntree_status gdntree_accept(gdntree_tree tree, int B, int N, int P,
+                              const int32_t *target_argmax, int32_t *acc_len, int32_t *acc_tok,
+                              int32_t *acc_node, void *stream);
+
+/*
+ * gdntree_commit - the commit half of gdntree_accept_commit for an accepted path given by a
+ * previous gdntree_accept on the same tree (same sources): for every layer and head,
+ * state[l][b][h] <- the state of node acc_node[b][acc_len[b] - 1], recomputed in fp32 from
+ * the committed state along acc_node[b][0..acc_len[b]) and written in place.
+ *
+ *   acc_len   i32 [B]        read only
+ *   acc_node  i32 [B][P+1]   read only
+ *   the rest as for gdntree_accept_commit.
+ * A request whose path is not a root path of its tree (acc_len outside [1, P+1], a first
+ * slot other than 0, a slot outside [1, n_nodes) or whose parent is not the previous slot)
+ * or whose n_nodes lies outside [1, N+1] keeps its state unchanged.  Reads tree.parent and
+ * tree.n_nodes.
+ */
+gdntree_status gdntree_commit(gdntree_tree tree, int B, int N, int P, const int32_t *acc_len,
+                              const int32_t *acc_node, int L, int H, int dk, int dv,
+                              gdntree_dtype in_dtype, const void *k, const void *v,
+                              const void *alpha, const void *beta, float *state, void *stream);
+
+/*
+ * gdntree_commit_build - gdntree_commit for this step's batch and gdntree_build for the next
+ * step's lattices in ONE launch (same sources as both).  The commit is bound by HBM traffic
+ * and the build is a latency-bound chain per request, so in one launch the build runs
+ * beside the commit instead of after it; results are exactly those of the two calls.
+ * Enqueue it after this step's gdntree_accept: the next draft, and so the next lattice,
+ * needs the accepted tokens.
+ *
+ *   tree ... state         as for gdntree_commit (this step)
+ *   next_lat_logp ... next_N, next_tree   as for gdntree_build (the next step)
+ * next_tree must not share memory with tree (the commit reads tree while the build writes
+ * next_tree); equal parent or n_nodes pointers give ERR_ARG.  Every check of the two calls
+ * applies; on any error nothing is enqueued.
+ */
+gdntree_status gdntree_commit_build(gdntree_tree tree, int B, int N, int P,
+                                    const int32_t *acc_len, const int32_t *acc_node, int L,
+                                    int H, int dk, int dv, gdntree_dtype in_dtype,
+                                    const void *k, const void *v, const void *alpha,
+                                    const void *beta, float *state,
+                                    const float *next_lat_logp, const int32_t *next_lat_tok,
+                                    const int32_t *next_root_tok, int next_B, int next_P,
+                                    int next_K, int next_N, gdntree_tree next_tree,
+                                    void *stream);
 
 /* Human-readable name of a status code ("unknown status" for other values). */
 const char *gdntree_status_str(int status);

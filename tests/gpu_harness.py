@@ -40,8 +40,9 @@ def device_inputs(w, dev="cuda"):
         state=g.state_from_math(w.h0).to(dev))
 
 
-def run_gpu(w, out_dtype=None, d=None):
-    """build -> verify -> (host: synthetic target from the built tree) -> accept_commit."""
+def run_gpu(w, out_dtype=None, d=None, split=False):
+    """build -> verify -> (host: synthetic target from the built tree) -> accept_commit, or
+    with split=True accept -> commit (the two-call form)."""
     import gdn_draft_tree_amd as g
     d = d or device_inputs(w)
     tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
@@ -50,8 +51,12 @@ def run_gpu(w, out_dtype=None, d=None):
     depth = tree.depth.cpu().numpy()
     n_nodes = tree.n_nodes.cpu().numpy()
     target = resolve_target(depth, n_nodes, w.lat_tok, w.tgt_choice, w.tgt_uniform)
-    acc = g.gdntree_accept_commit(tree, torch.from_numpy(target).cuda(), d["k"], d["v"], d["alpha"],
-                                  d["beta"], d["state"], w.cfg.P)
+    if split:
+        acc = g.gdntree_accept(tree, torch.from_numpy(target).cuda(), w.cfg.P)
+        g.gdntree_commit(tree, acc[0], acc[2], d["k"], d["v"], d["alpha"], d["beta"], d["state"], w.cfg.P)
+    else:
+        acc = g.gdntree_accept_commit(tree, torch.from_numpy(target).cuda(), d["k"], d["v"], d["alpha"],
+                                      d["beta"], d["state"], w.cfg.P)
     torch.cuda.synchronize()
     return dict(tree={f: getattr(tree, f).cpu().numpy() for f in
                       ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")},

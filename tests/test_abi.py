@@ -23,7 +23,8 @@ def _declared():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["gdntree_accept_commit", "gdntree_build", "gdntree_status_str", "gdntree_verify"]
+    assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_build", "gdntree_commit",
+                           "gdntree_commit_build", "gdntree_status_str", "gdntree_verify"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -124,6 +125,80 @@ def test_accept_commit_rejects(case, expect):
     st = g.LIB.gdntree_accept_commit(a["tree"], a["B"], a["N"], a["P"], a["tgt"], a["L"], a["H"], a["dk"],
                                      a["dv"], a["idt"], a["k"], a["v"], a["al"], a["be"], a["st"], a["al_"],
                                      a["at"], a["an"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_target", 1), ("null_acc_tok", 1), ("null_token", 1), ("B0", 1), ("N0", 1), ("P0", 1),
+    ("P17", 2), ("N65", 2),
+])
+def test_accept_rejects(case, expect):
+    g = _lib()
+    a = dict(tree=_tree(g), B=2, N=24, P=8, tgt=FAKE, al_=FAKE, at=FAKE, an=FAKE)
+    if case == "null_target": a["tgt"] = None
+    if case == "null_acc_tok": a["at"] = None
+    if case == "null_token": a["tree"] = _tree(g, token=1)
+    if case == "B0": a["B"] = 0
+    if case == "N0": a["N"] = 0
+    if case == "P0": a["P"] = 0
+    if case == "P17": a["P"] = 17
+    if case == "N65": a["N"] = 65
+    st = g.LIB.gdntree_accept(a["tree"], a["B"], a["N"], a["P"], a["tgt"], a["al_"], a["at"], a["an"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_acc_len", 1), ("null_acc_node", 1), ("null_state", 1), ("null_parent", 1), ("H0", 1),
+    ("P17", 2), ("N65", 2), ("d32", 2), ("dk_ne_dv", 2), ("dtype7", 1),
+])
+def test_commit_rejects(case, expect):
+    g = _lib()
+    a = dict(tree=_tree(g), B=2, N=24, P=8, al_=FAKE, an=FAKE, L=1, H=4, dk=128, dv=128, idt=1, k=FAKE,
+             v=FAKE, al=FAKE, be=FAKE, st=FAKE)
+    if case == "null_acc_len": a["al_"] = None
+    if case == "null_acc_node": a["an"] = None
+    if case == "null_state": a["st"] = None
+    if case == "null_parent": a["tree"] = _tree(g, parent=1)
+    if case == "H0": a["H"] = 0
+    if case == "P17": a["P"] = 17
+    if case == "N65": a["N"] = 65
+    if case == "d32": a["dk"] = a["dv"] = 32
+    if case == "dk_ne_dv": a["dv"] = 64
+    if case == "dtype7": a["idt"] = 7
+    st = g.LIB.gdntree_commit(a["tree"], a["B"], a["N"], a["P"], a["al_"], a["an"], a["L"], a["H"], a["dk"],
+                              a["dv"], a["idt"], a["k"], a["v"], a["al"], a["be"], a["st"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_acc_node", 1), ("null_state", 1), ("null_next_logp", 1), ("null_next_anc", 1), ("same_tree", 1),
+    ("next_B0", 1), ("next_K0", 1), ("H0", 1), ("next_P17", 2), ("next_K65", 2), ("next_N65", 2), ("N65", 2),
+    ("d32", 2), ("dtype7", 1),
+])
+def test_commit_build_rejects(case, expect):
+    g = _lib()
+    nxt = g.CTree(**{f: 0x2000 for f, _ in g.CTree._fields_})
+    a = dict(tree=_tree(g), B=2, N=24, P=8, al_=FAKE, an=FAKE, L=1, H=4, dk=128, dv=128, idt=1, k=FAKE,
+             v=FAKE, al=FAKE, be=FAKE, st=FAKE, nlp=FAKE, ntok=FAKE, nroot=FAKE, nB=2, nP=8, nK=16, nN=24,
+             nxt=nxt)
+    if case == "null_acc_node": a["an"] = None
+    if case == "null_state": a["st"] = None
+    if case == "null_next_logp": a["nlp"] = None
+    if case == "null_next_anc": a["nxt"] = g.CTree(**{f: (None if f == "anc" else 0x2000) for f, _ in g.CTree._fields_})
+    if case == "same_tree": a["nxt"] = _tree(g)
+    if case == "next_B0": a["nB"] = 0
+    if case == "next_K0": a["nK"] = 0
+    if case == "H0": a["H"] = 0
+    if case == "next_P17": a["nP"] = 17
+    if case == "next_K65": a["nK"] = 65
+    if case == "next_N65": a["nN"] = 65
+    if case == "N65": a["N"] = 65
+    if case == "d32": a["dk"] = a["dv"] = 32
+    if case == "dtype7": a["idt"] = 7
+    st = g.LIB.gdntree_commit_build(a["tree"], a["B"], a["N"], a["P"], a["al_"], a["an"], a["L"], a["H"],
+                                    a["dk"], a["dv"], a["idt"], a["k"], a["v"], a["al"], a["be"], a["st"],
+                                    a["nlp"], a["ntok"], a["nroot"], a["nB"], a["nP"], a["nK"], a["nN"],
+                                    a["nxt"], None)
     assert st == expect
 
 

@@ -183,3 +183,89 @@ def test_malformed_tree_is_contained():
     assert torch.isfinite(oc[:, 0]).all()
     assert torch.isnan(oc[:, 1]).all()
     assert (oc[:, 2] == 3.0).all()
+
+
+@pytest.mark.parametrize("name,seed,heads,reqs,layers", [
+    ("tiny", 0, None, None, None),
+    ("ragged", 1, 4, 8, None),
+    ("deep", 1, 2, None, 6),
+])
+def test_split_accept_then_commit(name, seed, heads, reqs, layers):
+    """gdntree_accept then gdntree_commit give exactly what gdntree_accept_commit gives (the
+    same fp32 arithmetic, bitwise), and so match the oracle."""
+    w = H.slice_workload(generate(name, seed=seed, B=reqs), H=heads, L=layers)
+    fused = H.run_gpu(w)
+    split = H.run_gpu(w, split=True)
+    for f in ("acc_len", "acc_tok", "acc_node"):
+        np.testing.assert_array_equal(split[f], fused[f])
+    assert np.array_equal(split["state"], fused["state"])
+    r = H.check_all(w, gpu=split)
+    _say(f"split {name}: state_err={r['state_err']:.2e} tau={split['acc_len'].tolist()}")
+
+
+def test_commit_keeps_state_on_a_bad_path():
+    """gdntree_commit leaves a request's state untouched when its path is not a root path of
+    its tree (a slot outside the node count, tau 0, a first slot other than the root, a slot
+    that is not a child of the previous one) and commits the others."""
+    import gdn_draft_tree_amd as g
+    from workloads import resolve_target
+    w = _custom(P=4, K=4, N=8, B=5, H_=2)
+    d = H.device_inputs(w)
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], 8)
+    torch.cuda.synchronize()
+    depth = tree.depth.cpu().numpy()
+    target = resolve_target(depth, tree.n_nodes.cpu().numpy(), w.lat_tok, w.tgt_choice, w.tgt_uniform)
+    tgt = torch.from_numpy(target).cuda()
+    s_ref = d["state"].clone()
+    acc_ref = g.gdntree_accept_commit(tree, tgt, d["k"], d["v"], d["alpha"], d["beta"], s_ref, 4)
+    acc_len, acc_tok, acc_node = g.gdntree_accept(tree, tgt, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(acc_len, acc_ref[0]) and torch.equal(acc_node, acc_ref[2])
+    acc_len, acc_node = acc_len.clone(), acc_node.clone()
+    acc_node[1, 1] = 99; acc_len[1] = 2                      # slot outside the node count
+    acc_len[2] = 0                                           # tau 0
+    acc_node[3, 0] = 1                                       # first slot not the root
+    deep = [t for t in range(1, 9) if depth[4, t] == 2]      # a slot that is not a child of the root
+    assert deep, "the seeded tree has a depth-2 node"
+    acc_node[4, 1] = deep[0]; acc_len[4] = 2
+    s0 = d["state"].clone()
+    g.gdntree_commit(tree, acc_len, acc_node, d["k"], d["v"], d["alpha"], d["beta"], d["state"], 4)
+    torch.cuda.synchronize()
+    assert torch.equal(d["state"][:, 0], s_ref[:, 0])
+    for b in (1, 2, 3, 4):
+        assert torch.equal(d["state"][:, b], s0[:, b]), b
+
+
+@pytest.mark.parametrize("cur,nxt", [
+    (dict(P=8, K=16, N=64, B=3, H_=4), dict(P=16, K=16, N=64, B=5, seed=7)),
+    (dict(P=4, K=4, N=8, B=2, H_=2, D=64, dtype="f32"), dict(P=8, K=8, N=24, B=1, seed=3)),
+])
+def test_commit_build_equals_the_two_calls(cur, nxt):
+    """One launch of commit + next build gives bitwise what gdntree_commit and gdntree_build
+    give separately (and the next tree equals the oracle's)."""
+    import gdn_draft_tree_amd as g
+    import oracle
+    from workloads import resolve_target
+    w = _custom(**cur)
+    wn = _custom(**nxt)
+    d = H.device_inputs(w)
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    torch.cuda.synchronize()
+    target = resolve_target(tree.depth.cpu().numpy(), tree.n_nodes.cpu().numpy(), w.lat_tok, w.tgt_choice,
+                            w.tgt_uniform)
+    acc = g.gdntree_accept(tree, torch.from_numpy(target).cuda(), w.cfg.P)
+    s_sep = d["state"].clone()
+    g.gdntree_commit(tree, acc[0], acc[2], d["k"], d["v"], d["alpha"], d["beta"], s_sep, w.cfg.P)
+    nl = (torch.from_numpy(wn.lat_logp).cuda(), torch.from_numpy(wn.lat_tok).cuda(), torch.from_numpy(wn.root_tok).cuda())
+    t_sep = g.gdntree_build(*nl, wn.cfg.N)
+    t_fused = g.Tree.empty(wn.cfg.B, wn.cfg.N, "cuda")
+    g.gdntree_commit_build(tree, acc[0], acc[2], d["k"], d["v"], d["alpha"], d["beta"], d["state"], w.cfg.P,
+                           *nl, wn.cfg.N, t_fused)
+    torch.cuda.synchronize()
+    assert torch.equal(d["state"], s_sep)
+    fields = ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")
+    fused = {f: getattr(t_fused, f).cpu().numpy() for f in fields}
+    sep = {f: getattr(t_sep, f).cpu().numpy() for f in fields}
+    sep["anc"] = sep["anc"].view(np.uint64)
+    H.assert_tree_equal(fused, sep)                          # used slots, scores bitwise
+    H.assert_tree_equal(fused, oracle.build_tree(wn.lat_logp, wn.lat_tok, wn.root_tok, wn.cfg.N))
