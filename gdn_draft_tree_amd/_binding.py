@@ -134,8 +134,33 @@ def _code(dtype: torch.dtype) -> int:
     raise ValueError(f"unsupported dtype {dtype}")
 
 
+class Prepared:
+    """One library call with its arguments validated and marshalled once: calling it enqueues
+    the same launch again (same tensors, same stream) with no Python-side checks.  It holds
+    references to the tensors it points at."""
+
+    def __init__(self, fn, args, result, keep):
+        self._fn = fn
+        # ctypes objects of the declared argument types, built once
+        self._args = tuple(a if isinstance(a, t) else t(a) for a, t in zip(args, fn.argtypes))
+        self.result = result
+        self._keep = keep
+
+    def __call__(self):
+        _check(self._fn(*self._args))
+        return self.result
+
+
+def _run(fn, args, prepare: bool, result, keep=()):
+    """Enqueue now, or (prepare=True) return a Prepared call for repeated launches."""
+    if prepare:
+        return Prepared(fn, args, result, keep)
+    _check(fn(*args))
+    return result
+
+
 def gdntree_build(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch.Tensor, N: int,
-                  out: Tree | None = None, stream=None) -> Tree:
+                  out: Tree | None = None, stream=None, prepare: bool = False) -> Tree:
     """Best-first tree from a [B][P][K] lattice (sorted along K); see gdntree.h."""
     B, P, K = lat_logp.shape
     out = out if out is not None else Tree.empty(B, N, lat_logp.device)
@@ -144,11 +169,12 @@ def gdntree_build(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch
             _dev(root_tok, "root_tok", torch.int32, (B,)))
     if out.B != B or out.N != N:
         raise ValueError("output tree has the wrong shape")
-    _check(LIB.gdntree_build(*args, B, P, K, N, out.c(), _stream(stream)))
-    return out
+    return _run(LIB.gdntree_build, (*args, B, P, K, N, out.c(), _stream(stream)), prepare, out,
+                (lat_logp, lat_tok, root_tok, out))
 
 
-def gdntree_verify(tree: Tree, q, k, v, alpha, beta, state, o=None, out_dtype=None, stream=None):
+def gdntree_verify(tree: Tree, q, k, v, alpha, beta, state, o=None, out_dtype=None, stream=None,
+                   prepare: bool = False):
     """Per-node GDN outputs o [L][B][N+1][H][d_v] for every tree slot < n_nodes.
 
     q, k, v: [L][B][N+1][H][d]; alpha, beta: [L][B][N+1][H] (bf16 or fp32, all the same);
@@ -165,13 +191,13 @@ def gdntree_verify(tree: Tree, q, k, v, alpha, beta, state, o=None, out_dtype=No
     op = _dev(o, "o", out_dtype, (L, B, R, H, D))
     if tree.B != B or tree.N != R - 1:
         raise ValueError("tree shape does not match the rows")
-    _check(LIB.gdntree_verify(tree.c(), B, R - 1, L, H, D, D, _code(dt), *ptrs, sp,
-                              _code(out_dtype), op, _stream(stream)))
-    return o
+    return _run(LIB.gdntree_verify, (tree.c(), B, R - 1, L, H, D, D, _code(dt), *ptrs, sp,
+                              _code(out_dtype), op, _stream(stream)), prepare, o,
+                (tree, q, k, v, alpha, beta, state, o))
 
 
 def gdntree_accept_commit(tree: Tree, target_argmax, k, v, alpha, beta, state, P: int,
-                          acc=None, stream=None):
+                          acc=None, stream=None, prepare: bool = False):
     """Greedy acceptance + bonus and in-place commit of the accepted-path state.
 
     Returns (acc_len [B], acc_tok [B][P+1], acc_node [B][P+1]) int32 device tensors.
@@ -192,9 +218,9 @@ def gdntree_accept_commit(tree: Tree, target_argmax, k, v, alpha, beta, state, P
           _dev(acc_node, "acc_node", torch.int32, (B, P + 1)))
     if tree.B != B or tree.N != R - 1:
         raise ValueError("tree shape does not match the rows")
-    _check(LIB.gdntree_accept_commit(tree.c(), B, R - 1, P, tp, L, H, D, D, _code(dt), *ptrs, sp,
-                                     *ap, _stream(stream)))
-    return acc_len, acc_tok, acc_node
+    return _run(LIB.gdntree_accept_commit, (tree.c(), B, R - 1, P, tp, L, H, D, D, _code(dt), *ptrs, sp,
+                                     *ap, _stream(stream)), prepare, (acc_len, acc_tok, acc_node),
+                (tree, target_argmax, k, v, alpha, beta, state, acc_len, acc_tok, acc_node))
 
 
 def _acc_buffers(B: int, P: int, device, acc=None):
@@ -205,7 +231,7 @@ def _acc_buffers(B: int, P: int, device, acc=None):
     return acc
 
 
-def gdntree_accept(tree: Tree, target_argmax, P: int, acc=None, stream=None):
+def gdntree_accept(tree: Tree, target_argmax, P: int, acc=None, stream=None, prepare: bool = False):
     """Greedy acceptance + bonus only (no state is touched).
 
     Returns (acc_len [B], acc_tok [B][P+1], acc_node [B][P+1]) int32 device tensors.
@@ -218,11 +244,12 @@ def gdntree_accept(tree: Tree, target_argmax, P: int, acc=None, stream=None):
           _dev(acc_node, "acc_node", torch.int32, (B, P + 1)))
     if tree.B != B or tree.N != R - 1:
         raise ValueError("tree shape does not match target_argmax")
-    _check(LIB.gdntree_accept(tree.c(), B, R - 1, P, tp, *ap, _stream(stream)))
-    return acc_len, acc_tok, acc_node
+    return _run(LIB.gdntree_accept, (tree.c(), B, R - 1, P, tp, *ap, _stream(stream)), prepare,
+                (acc_len, acc_tok, acc_node), (tree, target_argmax, acc_len, acc_tok, acc_node))
 
 
-def gdntree_commit(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state, P: int, stream=None):
+def gdntree_commit(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state, P: int, stream=None,
+                   prepare: bool = False):
     """In-place commit of the state along an accepted path from gdntree_accept."""
     L, B, R, H, D = k.shape
     dt = k.dtype
@@ -233,13 +260,14 @@ def gdntree_commit(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state, P: i
     sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
     if tree.B != B or tree.N != R - 1:
         raise ValueError("tree shape does not match the rows")
-    _check(LIB.gdntree_commit(tree.c(), B, R - 1, P, lp, np_, L, H, D, D, _code(dt), *ptrs, sp,
-                              _stream(stream)))
+    return _run(LIB.gdntree_commit, (tree.c(), B, R - 1, P, lp, np_, L, H, D, D, _code(dt), *ptrs, sp,
+                                     _stream(stream)), prepare, None,
+                (tree, acc_len, acc_node, k, v, alpha, beta, state))
 
 
 def gdntree_commit_build(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state, P: int,
                          next_lat_logp, next_lat_tok, next_root_tok, next_N: int, next_out: Tree,
-                         stream=None):
+                         stream=None, prepare: bool = False):
     """gdntree_commit of this step and gdntree_build of the next step's tree into `next_out`,
     in one launch (enqueue after this step's gdntree_accept)."""
     L, B, R, H, D = k.shape
@@ -260,6 +288,7 @@ def gdntree_commit_build(tree: Tree, acc_len, acc_node, k, v, alpha, beta, state
     for f in ("parent", "depth", "rank", "token", "score", "anc"):
         _dev(getattr(next_out, f), f, None, (Bn, next_N + 1))
     _dev(next_out.n_nodes, "n_nodes", torch.int32, (Bn,))
-    _check(LIB.gdntree_commit_build(tree.c(), B, R - 1, P, lp, np_, L, H, D, D, _code(dt), *ptrs, sp,
-                                    nl, nt, nr, Bn, Pn, Kn, next_N, next_out.c(), _stream(stream)))
-    return next_out
+    return _run(LIB.gdntree_commit_build, (tree.c(), B, R - 1, P, lp, np_, L, H, D, D, _code(dt), *ptrs, sp,
+                                           nl, nt, nr, Bn, Pn, Kn, next_N, next_out.c(), _stream(stream)),
+                prepare, next_out, (tree, acc_len, acc_node, k, v, alpha, beta, state, next_lat_logp,
+                                    next_lat_tok, next_root_tok, next_out))

@@ -269,3 +269,24 @@ def test_commit_build_equals_the_two_calls(cur, nxt):
     sep["anc"] = sep["anc"].view(np.uint64)
     H.assert_tree_equal(fused, sep)                          # used slots, scores bitwise
     H.assert_tree_equal(fused, oracle.build_tree(wn.lat_logp, wn.lat_tok, wn.root_tok, wn.cfg.N))
+
+
+def test_prepared_calls_equal_direct_calls():
+    """A call prepared once (binding's prepare=True) and enqueued twice gives bitwise what the
+    direct calls give."""
+    import gdn_draft_tree_amd as g
+    w = _custom(P=8, K=16, N=64, B=2, H_=3, seed=11)
+    d = H.device_inputs(w)
+    t_direct = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], 64)
+    o_direct = g.gdntree_verify(t_direct, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"])
+    t_prep = g.Tree.empty(2, 64, "cuda")
+    o_prep = torch.empty_like(o_direct)
+    pb = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], 64, out=t_prep, prepare=True)
+    pv = g.gdntree_verify(t_prep, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o=o_prep, prepare=True)
+    for _ in range(2):
+        o_prep.fill_(0)
+        pb()
+        pv()
+        torch.cuda.synchronize()
+        assert torch.equal(t_prep.parent, t_direct.parent) and torch.equal(t_prep.anc, t_direct.anc)
+        assert torch.equal(o_prep.view(torch.int16), o_direct.view(torch.int16))
