@@ -2,10 +2,10 @@
 
 A step is one pass of the whole path over one batch: tree build, verify, acceptance and
 state commit.  Steps are pipelined the way a decode loop can run them: gdntree_verify ->
-gdntree_accept -> gdntree_commit_build, where the last call commits this step's states and
-builds the next batch's tree in one launch (the next build needs only this step's
-acceptance: it stands for the next draft, which needs the accepted tokens); the next verify
-runs after it.  The same steps strictly in order
+gdntree_accept_commit_build, where the second call accepts, commits this step's states and
+builds the next batch's trees in one launch (each request's next build starts once that
+request's acceptance is known: it stands for the next draft, which needs the accepted
+tokens); the next verify runs after it.  The same steps strictly in order
 (build -> verify -> accept_commit) are reported beside it as `sequential`.  The default workload is the large ragged batch: 32 requests x one
 GDN layer (32 heads, d = 128), 16-position x top-16 lattices, N = 64 draft nodes per
 request, bf16 rows, fp32 state.  The synthetic target argmax (the stand-in for the target
@@ -210,9 +210,10 @@ def main():
         d["p_accept"] = g.gdntree_accept(d["tree"], d["target"], cfg.P, acc=d["acc"], stream=stream, prepare=True)
         d["p_commit"] = g.gdntree_commit(d["tree"], d["acc"][0], d["acc"][2], d["k"], d["v"], d["alpha"], d["beta"],
                                          d["state"], cfg.P, stream=stream, prepare=True)
-        d["p_commit_build"] = g.gdntree_commit_build(
-            d["tree"], d["acc"][0], d["acc"][2], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
-            dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, dn["tree"], stream=stream, prepare=True)
+        d["p_accept_commit_build"] = g.gdntree_accept_commit_build(
+            d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
+            dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, dn["tree"], acc=d["acc"], stream=stream,
+            prepare=True)
 
     def step(i, events=None):
         d = sets[i % nsets]
@@ -228,17 +229,16 @@ def main():
         if events:
             events[3].record(stream)
 
-    # Pipelined steps: the end of a step is split into acceptance and commit, and the commit
-    # runs in one launch with the next batch's tree build (which needs only this step's
-    # acceptance: it stands for the next draft, which needs the accepted tokens); the next
-    # verify runs after that launch.  One stream, no events.
+    # Pipelined steps: the end of a step (acceptance and commit) runs in one launch with the
+    # next batch's tree build; each request's next build starts in the workgroup that has just
+    # walked that request's acceptance (the build stands for the next draft, which needs the
+    # accepted tokens); the next verify runs after that launch.  One stream, no events.
     def run_pipelined(i0, k):
         sets[i0 % nsets]["p_build"]()
         for i in range(i0, i0 + k):
             d = sets[i % nsets]
             d["p_verify"]()
-            d["p_accept"]()
-            (d["p_commit_build"] if i + 1 < i0 + k else d["p_commit"])()
+            (d["p_accept_commit_build"] if i + 1 < i0 + k else d["p_accept_commit"])()
 
     for i in range(args.warmup):
         step(i)
@@ -329,8 +329,8 @@ def main():
                        "verify_back_to_back": t_verify},
         "sequential": {"ms_per_step": ms_seq, "value": nodes_per_step / (ms_seq * 1e-3),
                        "order": "build -> verify -> accept_commit, each step after the previous one"},
-        "pipelining": "build -> verify(i) -> accept(i) -> [commit(i) + build(i+1) in one launch] -> "
-                      "verify(i+1) ...; one stream",
+        "pipelining": "build -> verify(i) -> [accept(i), then per request build(i+1); commit(i) beside "
+                      "them; one launch] -> verify(i+1) ...; one stream",
         "host_enqueue_us_per_step": t_enqueued / args.steps * 1e6,
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
         "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),

@@ -67,10 +67,6 @@ __device__ __forceinline__ void write_acceptance(const CommitParams &p, int b, i
   p.acc_tok[ab + t] = t < len - 1 ? s_tok[s_path[t + 1]] : (t == len - 1 ? bonus : -1);
 }
 
-// WALK: wave 0 walks the tree and the (0, 0, 0) workgroup of each request writes the
-// acceptance; otherwise the path is read from acc_len / acc_node and checked (tau in
-// [1, P+1], slot 0 first, each next slot a child of the previous one within the node count;
-// a path that fails leaves the request's state untouched).
 template <int D>
 struct CommitSmem {
   float k[kMaxAnc][D];
@@ -81,9 +77,19 @@ struct CommitSmem {
   int len, bonus, bad;
 };
 
+// Where a commit workgroup takes its request's accepted path from.
+enum CommitPath {
+  kPathGiven = 0,      // read from acc_len / acc_node and checked (tau in [1, P+1], slot 0
+                       // first, each next slot a child of the previous one within the node
+                       // count; a path that fails leaves the request's state untouched)
+  kWalkAndWrite = 1,   // wave 0 walks the tree; the (0, 0, 0) workgroup of each request
+                       // writes the acceptance
+  kWalk = 2,           // wave 0 walks the tree; the acceptance is written elsewhere
+};
+
 // Commit of work unit `blk` (one 32-channel slice of one (layer, request, head)) by the 256
 // threads of a workgroup.
-template <int D, bool BF16IN, bool WALK>
+template <int D, bool BF16IN, int PATH>
 __device__ __forceinline__ void commit_unit(const CommitParams &p, int blk, int tid, CommitSmem<D> &sm) {
   typedef typename std::conditional<BF16IN, uint16_t, float>::type T;
   constexpr int SL = D / 32;       // workgroups (slices of 32 channels) per head
@@ -107,7 +113,7 @@ __device__ __forceinline__ void commit_unit(const CommitParams &p, int blk, int 
 #pragma unroll
   for (int m = 0; m < F4; ++m) st[m] = *reinterpret_cast<const float4 *>(col + 4 * (sub + 8 * m));
 
-  if constexpr (WALK) {
+  if constexpr (PATH != kPathGiven) {
     if (wave == 0) accept_walk(p, b, lane, s_path, s_tok, &s_len, &s_bonus);
     __syncthreads();
   } else {
@@ -129,7 +135,7 @@ __device__ __forceinline__ void commit_unit(const CommitParams &p, int blk, int 
   const int len = s_len;
   if (len == 0) return;  // malformed node count or path: nothing is written
 
-  if constexpr (WALK) {
+  if constexpr (PATH == kWalkAndWrite) {
     if (l == 0 && h == 0 && js == 0 && tid <= p.P) write_acceptance(p, b, tid, len, s_path, s_tok, s_bonus);
   }
 

@@ -173,6 +173,41 @@ GDNTREE_EXPORT gdntree_status gdntree_commit_build(
   return GDNTREE_OK;
 }
 
+GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
+    gdntree_tree tree, int B, int N, int P, const int32_t *target_argmax, int L, int H, int dk,
+    int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
+    const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
+    const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
+    int next_B, int next_P, int next_K, int next_N, gdntree_tree next_tree, void *stream) {
+  if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !k || !v || !alpha ||
+      !beta || !state || !acc_len || !acc_tok || !acc_node)
+    return GDNTREE_ERR_ARG;
+  if (!next_lat_logp || !next_lat_tok || !next_root_tok || !next_tree.parent || !next_tree.depth ||
+      !next_tree.rank || !next_tree.token || !next_tree.score || !next_tree.anc || !next_tree.n_nodes)
+    return GDNTREE_ERR_ARG;
+  // the acceptance and commit read the current tree while the build writes the next one
+  if (next_tree.parent == tree.parent || next_tree.n_nodes == tree.n_nodes || next_tree.token == tree.token)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || N <= 0 || P <= 0 || L <= 0 || H <= 0) return GDNTREE_ERR_ARG;
+  if (next_B <= 0 || next_P <= 0 || next_K <= 0 || next_N <= 0) return GDNTREE_ERR_ARG;
+  if (!dtype_ok(in_dtype)) return GDNTREE_ERR_ARG;
+  if (gdntree_status st = head_dims(dk, dv); st != GDNTREE_OK) return st;
+  if (N > kMaxN || P > kMaxP || next_P > kMaxP || next_K > kMaxK || next_N > kMaxN ||
+      !grid_fits((long long)L * B * H + (next_B > B ? next_B : B)))
+    return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  CommitParams p{};
+  p.parent = tree.parent; p.token = tree.token; p.n_nodes = tree.n_nodes; p.target = target_argmax;
+  p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state = state;
+  p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
+  p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
+  p.in_bf16 = in_dtype == GDNTREE_BF16;
+  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree};
+  if (launch_accept_commit_build(p, bp, next_B, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
 GDNTREE_EXPORT const char *gdntree_status_str(int status) {
   switch (status) {
     case GDNTREE_OK: return "ok";

@@ -64,5 +64,7 @@ hipError_t launch_commit(const CommitParams &p, hipStream_t stream);  // commit 
 struct BuildParams;
 // commit of a given path (p) fused with the build of nb other requests' trees (bp)
 hipError_t launch_commit_build(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream);
+// acceptance (written to p.acc_*), commit and the build of nb next trees in one launch
+hipError_t launch_accept_commit_build(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream);
 
 }  // namespace gdntree

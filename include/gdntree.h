@@ -8,7 +8,8 @@
  *   gdntree_accept_commit  greedy acceptance of the longest matching root path plus a
  *                          bonus token, then the accepted-path state commit
  * gdntree_accept_commit also comes as two calls, gdntree_accept then gdntree_commit, and
- * gdntree_commit_build runs a commit together with the next step's tree build in one launch.
+ * gdntree_commit_build / gdntree_accept_commit_build run a commit (with or without the
+ * acceptance) together with the next step's tree build in one launch.
  *
  * Sources: the SpecPilot paper summary (paper.rainbus.top, "SpecPilot: Autonomous
  * Algorithm Discovery and Systems Optimization for Speculative Decoding"), sections
@@ -197,6 +198,30 @@ gdntree_status gdntree_commit_build(gdntree_tree tree, int B, int N, int P,
                                     const int32_t *next_root_tok, int next_B, int next_P,
                                     int next_K, int next_N, gdntree_tree next_tree,
                                     void *stream);
+
+/*
+ * gdntree_accept_commit_build - gdntree_accept_commit for this step and gdntree_build for
+ * the next step's lattices in ONE launch (same sources as both).  Request b's next tree is
+ * built by the workgroup that has just walked request b's acceptance, so each next build
+ * starts after its own request's acceptance, as the next draft requires; the commit runs
+ * beside the builds.  Results are exactly those of gdntree_accept_commit followed by
+ * gdntree_build.
+ *
+ *   tree ... acc_node      as for gdntree_accept_commit (this step)
+ *   next_lat_logp ... next_N, next_tree   as for gdntree_build (the next step)
+ * next_tree must not share memory with tree; equal parent, token or n_nodes pointers give
+ * ERR_ARG.  Every check of the two calls applies; on any error nothing is enqueued.
+ */
+gdntree_status gdntree_accept_commit_build(gdntree_tree tree, int B, int N, int P,
+                                           const int32_t *target_argmax, int L, int H, int dk,
+                                           int dv, gdntree_dtype in_dtype, const void *k,
+                                           const void *v, const void *alpha, const void *beta,
+                                           float *state, int32_t *acc_len, int32_t *acc_tok,
+                                           int32_t *acc_node, const float *next_lat_logp,
+                                           const int32_t *next_lat_tok,
+                                           const int32_t *next_root_tok, int next_B, int next_P,
+                                           int next_K, int next_N, gdntree_tree next_tree,
+                                           void *stream);
 
 /* Human-readable name of a status code ("unknown status" for other values). */
 const char *gdntree_status_str(int status);

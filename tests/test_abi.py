@@ -23,8 +23,9 @@ def _declared():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_build", "gdntree_commit",
-                           "gdntree_commit_build", "gdntree_status_str", "gdntree_verify"]
+    assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_accept_commit_build",
+                           "gdntree_build", "gdntree_commit", "gdntree_commit_build", "gdntree_status_str",
+                           "gdntree_verify"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -199,6 +200,34 @@ def test_commit_build_rejects(case, expect):
                                     a["dk"], a["dv"], a["idt"], a["k"], a["v"], a["al"], a["be"], a["st"],
                                     a["nlp"], a["ntok"], a["nroot"], a["nB"], a["nP"], a["nK"], a["nN"],
                                     a["nxt"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_target", 1), ("null_acc_tok", 1), ("null_token", 1), ("null_next_root", 1), ("same_token", 1),
+    ("next_N0", 1), ("L0", 1), ("P17", 2), ("next_K65", 2), ("d96", 2), ("dtype5", 1),
+])
+def test_accept_commit_build_rejects(case, expect):
+    g = _lib()
+    nxt = g.CTree(**{f: 0x2000 for f, _ in g.CTree._fields_})
+    a = dict(tree=_tree(g), B=2, N=24, P=8, tgt=FAKE, L=1, H=4, dk=128, dv=128, idt=1, k=FAKE, v=FAKE,
+             al=FAKE, be=FAKE, st=FAKE, al_=FAKE, at=FAKE, an=FAKE, nlp=FAKE, ntok=FAKE, nroot=FAKE, nB=2, nP=8,
+             nK=16, nN=24, nxt=nxt)
+    if case == "null_target": a["tgt"] = None
+    if case == "null_acc_tok": a["at"] = None
+    if case == "null_token": a["tree"] = _tree(g, token=1)
+    if case == "null_next_root": a["nroot"] = None
+    if case == "same_token": a["nxt"] = g.CTree(**{f: (FAKE if f == "token" else 0x2000) for f, _ in g.CTree._fields_})
+    if case == "next_N0": a["nN"] = 0
+    if case == "L0": a["L"] = 0
+    if case == "P17": a["P"] = 17
+    if case == "next_K65": a["nK"] = 65
+    if case == "d96": a["dk"] = a["dv"] = 96
+    if case == "dtype5": a["idt"] = 5
+    st = g.LIB.gdntree_accept_commit_build(a["tree"], a["B"], a["N"], a["P"], a["tgt"], a["L"], a["H"], a["dk"],
+                                           a["dv"], a["idt"], a["k"], a["v"], a["al"], a["be"], a["st"],
+                                           a["al_"], a["at"], a["an"], a["nlp"], a["ntok"], a["nroot"], a["nB"],
+                                           a["nP"], a["nK"], a["nN"], a["nxt"], None)
     assert st == expect
 
 

@@ -290,3 +290,39 @@ def test_prepared_calls_equal_direct_calls():
         torch.cuda.synchronize()
         assert torch.equal(t_prep.parent, t_direct.parent) and torch.equal(t_prep.anc, t_direct.anc)
         assert torch.equal(o_prep.view(torch.int16), o_direct.view(torch.int16))
+
+
+@pytest.mark.parametrize("cur,nxt", [
+    (dict(P=8, K=16, N=64, B=3, H_=4), dict(P=16, K=16, N=64, B=5, seed=7)),   # more next requests
+    (dict(P=16, K=16, N=64, B=6, H_=2), dict(P=8, K=16, N=24, B=2, seed=9)),   # fewer next requests
+    (dict(P=4, K=4, N=8, B=2, H_=2, D=64, dtype="f32"), dict(P=8, K=8, N=24, B=2, seed=3)),
+])
+def test_accept_commit_build_equals_the_two_calls(cur, nxt):
+    """Acceptance, commit and the next build in one launch give bitwise what
+    gdntree_accept_commit and gdntree_build give separately."""
+    import gdn_draft_tree_amd as g
+    from workloads import resolve_target
+    w = _custom(**cur)
+    wn = _custom(**nxt)
+    d = H.device_inputs(w)
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    torch.cuda.synchronize()
+    target = torch.from_numpy(resolve_target(tree.depth.cpu().numpy(), tree.n_nodes.cpu().numpy(), w.lat_tok,
+                                             w.tgt_choice, w.tgt_uniform)).cuda()
+    s_sep = d["state"].clone()
+    acc_sep = g.gdntree_accept_commit(tree, target, d["k"], d["v"], d["alpha"], d["beta"], s_sep, w.cfg.P)
+    nl = (torch.from_numpy(wn.lat_logp).cuda(), torch.from_numpy(wn.lat_tok).cuda(), torch.from_numpy(wn.root_tok).cuda())
+    t_sep = g.gdntree_build(*nl, wn.cfg.N)
+    t_fused = g.Tree.empty(wn.cfg.B, wn.cfg.N, "cuda")
+    acc = tuple(torch.full_like(x, -7) for x in acc_sep)
+    g.gdntree_accept_commit_build(tree, target, d["k"], d["v"], d["alpha"], d["beta"], d["state"], w.cfg.P,
+                                  *nl, wn.cfg.N, t_fused, acc=acc)
+    torch.cuda.synchronize()
+    assert torch.equal(d["state"], s_sep)
+    for x, y in zip(acc, acc_sep):
+        assert torch.equal(x, y)
+    fields = ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")
+    fused = {f: getattr(t_fused, f).cpu().numpy() for f in fields}
+    sep = {f: getattr(t_sep, f).cpu().numpy() for f in fields}
+    sep["anc"] = sep["anc"].view(np.uint64)
+    H.assert_tree_equal(fused, sep)
