@@ -714,6 +714,12 @@ void verify_kernel(VerifyParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) kt[mt >> 1][4 * (mt & 1) + i] = (_Float16)c[i];
     }
+    // Scheduling fences: this channel tile's K^T fragments are packed before its products,
+    // and the next tile's only after this tile's E rows (which read the last products'
+    // results).  An interleaved schedule, in which VALU packing of the next tile's fragments
+    // rewrote the B operand registers of an MFMA still waiting on the previous MFMA's
+    // accumulator, gave wrong E entries in workgroups sharing a CU.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
       const int t = 16 * mt + l16;
@@ -731,6 +737,7 @@ void verify_kernel(VerifyParams p) {
       // rows n..RM-1 are unused scratch; rows past RM do not exist
       if (mt < NT - 1 || t < RM) *reinterpret_cast<f16x4 *>(erow + swz<D, 8>(t, 16 * ct + 4 * g4)) = ev;
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): E is written
   __builtin_amdgcn_s_barrier();        // (2) the product waves may read E

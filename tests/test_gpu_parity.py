@@ -326,3 +326,27 @@ def test_accept_commit_build_equals_the_two_calls(cur, nxt):
     sep = {f: getattr(t_sep, f).cpu().numpy() for f in fields}
     sep["anc"] = sep["anc"].view(np.uint64)
     H.assert_tree_equal(fused, sep)
+
+
+@pytest.mark.parametrize("name,B", [("ragged", 24), ("batched", 24)])
+def test_repeated_launches_with_shared_cus(name, B):
+    """Several launches over more units than resident workgroups (two or three share each
+    CU, and a second round follows) give bitwise-identical outputs, every unit within the
+    bar against the oracle.  Guards against schedule-dependent corruption that shows only
+    when workgroups run side by side."""
+    import gdn_draft_tree_amd as g
+    w = generate(name, seed=3, B=B)
+    ref = H.run_oracle(w)
+    d = H.device_inputs(w)
+    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    outs = []
+    for _ in range(3):
+        o = g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"])
+        torch.cuda.synchronize()
+        outs.append(o)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    oe = H.output_errors(outs[0].float().cpu().numpy().astype(np.float64), ref["o"], ref["hnorm"],
+                         ref["tree"]["n_nodes"])
+    assert oe <= H.TOL, f"output error {oe:.3e}"
+    _say(f"{name} B={B}: 3 launches identical, out_err={oe:.2e}")
