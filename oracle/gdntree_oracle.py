@@ -31,6 +31,9 @@ Readings where the pages leave a step open (each listed in the design notes):
     node index is the insertion order.
   * If the trie holds fewer than N nodes the build stops early.
   * If several children of the current node match the target, the smallest index wins.
+  * With a budget shared by the batch, G counts draft nodes over all requests (roots not
+    counted), N stays the per-request cap, and ties across requests go to the smaller
+    request index.
   * Outputs carry no 1/sqrt(d_k) scale: o = h^T q exactly.
 
 Every function is a direct transcription of the definition; nothing is blocked, fused or
@@ -98,6 +101,70 @@ def build_tree(lat_logp: np.ndarray, lat_tok: np.ndarray, root_tok: np.ndarray, 
         out["token"][b, :n] = token
         out["score"][b, :n] = score
         out["anc"][b, :n] = np.array(anc, dtype=np.uint64)
+        out["n_nodes"][b] = n
+    return out
+
+
+def build_tree_shared(lat_logp: np.ndarray, lat_tok: np.ndarray, root_tok: np.ndarray, N: int,
+                      G: int, positions=None) -> dict:
+    """Best-first draft trees for a whole batch under one shared node budget.
+
+    SpecPilot summary, Technical novelty (batching: the node budget is shared across the
+    batch, and each request gets its own number of draft positions).  One best-first pass
+    runs over the union of every request's frontier: it adds the candidate with the
+    largest path log-prob until the batch holds G draft nodes or no candidate is left.  A
+    request that holds N draft nodes offers no more candidates (its tree keeps N+1 slots),
+    and request b draws children only from its first positions[b] lattice positions
+    (all P when positions is None; values are clipped to [0, P]).
+
+    Ties: the smaller request index, then the smaller parent slot, then the smaller rank.
+    Node indices within a request are its insertion order.  Returns the arrays of
+    build_tree, with every request's tree in its own [N+1] slots.
+    """
+    B, P, K = lat_logp.shape
+    pos = np.full(B, P) if positions is None else np.clip(np.asarray(positions), 0, P)
+    out = {
+        "parent": np.full((B, N + 1), -1, np.int64),
+        "depth": np.full((B, N + 1), -1, np.int64),
+        "rank": np.full((B, N + 1), -1, np.int64),
+        "token": np.full((B, N + 1), -1, np.int64),
+        "score": np.full((B, N + 1), np.nan),
+        "anc": np.zeros((B, N + 1), np.uint64),
+        "n_nodes": np.zeros(B, np.int64),
+    }
+    trees = [{"parent": [-1], "depth": [0], "rank": [-1], "token": [int(root_tok[b])],
+              "score": [0.0], "anc": [0]} for b in range(B)]
+    # the full frontier of the batch: (request, parent slot, rank)
+    frontier = [(b, 0, r) for b in range(B) if pos[b] > 0 and N > 0 for r in range(K)]
+    total = 0
+    while total < G and frontier:
+        def key(c):
+            b, p, r = c
+            t = trees[b]
+            s = t["score"][p] + float(np.float64(lat_logp[b, t["depth"][p], r]))
+            return (-s, b, p, r)
+        best = min(frontier, key=key)
+        frontier.remove(best)
+        b, p, r = best
+        t = trees[b]
+        i = len(t["parent"])
+        d = t["depth"][p] + 1
+        t["parent"].append(p)
+        t["depth"].append(d)
+        t["rank"].append(r)
+        t["token"].append(int(lat_tok[b, d - 1, r]))
+        t["score"].append(t["score"][p] + float(np.float64(lat_logp[b, d - 1, r])))
+        t["anc"].append(t["anc"][p] | (1 << (i - 1)))
+        total += 1
+        if d < pos[b]:
+            frontier.extend((b, i, rr) for rr in range(K))
+        if i == N:  # the request is full: withdraw its remaining candidates
+            frontier = [c for c in frontier if c[0] != b]
+    for b, t in enumerate(trees):
+        n = len(t["parent"])
+        for name in ("parent", "depth", "rank", "token", "score"):
+            out[name][b, :n] = t[name]
+        out["anc"][b, :n] = np.array(t["anc"], dtype=np.uint64)
         out["n_nodes"][b] = n
     return out
 

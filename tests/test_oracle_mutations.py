@@ -16,6 +16,7 @@ from oracle import gdntree_oracle as real
 
 from . import test_oracle_accept as T_acc
 from . import test_oracle_build as T_build
+from . import test_oracle_shared as T_shared
 from . import test_oracle_verify as T_ver
 
 MUTATIONS = {
@@ -33,16 +34,19 @@ MUTATIONS = {
     "no_bonus": ("+ [int(target[b, u])]", ""),
     "accept_highest_index": ("u = min(nxt)", "u = max(nxt)"),
     "tau_off_by_one": ("acc_len[b] = len(path)", "acc_len[b] = len(path) - 1"),
+    "shared_tie_request_desc": ("return (-s, b, p, r)", "return (-s, -b, p, r)"),
+    "shared_no_cap": ("if i == N:  # the request is full", "if i == -1:  # the request is full"),
+    "shared_budget_off_by_one": ("while total < G and frontier:", "while total <= G and frontier:"),
     "commit_skips_root": ("for i in acc_node[b, :int(acc_len[b])]:",
                           "for i in acc_node[b, 1:int(acc_len[b])]:"),
 }
 
-EXPORTS = ["build_tree", "gdn_update", "gdn_readout", "gdn_step", "verify_request", "verify",
+EXPORTS = ["build_tree", "build_tree_shared", "gdn_update", "gdn_readout", "gdn_step", "verify_request", "verify",
            "accept", "commit", "pipeline"]
 
 
 def _pins():
-    for mod in (T_build, T_ver, T_acc):
+    for mod in (T_build, T_shared, T_ver, T_acc):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
