@@ -89,9 +89,13 @@ def _oracle_on_requests(job):
     def target_fn(tree):
         return resolve_target(tree["depth"], tree["n_nodes"], lat_tok, tch, tun)
 
+    shared = {}
+    if w.cfg.G is not None:  # the batch budget couples the requests: a task is the whole batch
+        shared = dict(G=w.cfg.G, positions=w.cfg.positions_for(b1 - b0))
     with threadpool_limits(limits=1):
         r = oracle.pipeline(w.lat_logp[sl], lat_tok, w.root_tok[sl], w.cfg.N, x["q"][ll, sl], x["k"][ll, sl],
-                            x["v"][ll, sl], x["alpha"][ll, sl], x["beta"][ll, sl], x["h0"][ll, sl], target_fn)
+                            x["v"][ll, sl], x["alpha"][ll, sl], x["beta"][ll, sl], x["h0"][ll, sl], target_fn,
+                            **shared)
     return int(np.asarray(r["tree"]["n_nodes"]).sum()) * (l1 - l0)
 
 
@@ -110,7 +114,10 @@ def cpu_baseline(name: str, reqs: int, seeds: int, workers: int) -> dict:
     t0 = time.perf_counter()
     nodes1 = _oracle_on_requests((0, 0, reqs, 0, L))
     dt1 = time.perf_counter() - t0
-    jobs = [(s, b, b + 1, l, l + 1) for s in range(seeds) for b in range(reqs) for l in range(L)]
+    if _CPU_WORK[0][0].cfg.G is None:
+        jobs = [(s, b, b + 1, l, l + 1) for s in range(seeds) for b in range(reqs) for l in range(L)]
+    else:
+        jobs = [(s, 0, reqs, l, l + 1) for s in range(seeds) for l in range(L)]
     workers = min(workers, len(jobs))
     with mp.get_context("fork").Pool(workers) as pool:
         pool.map(abs, range(workers))  # workers started before the clock
@@ -122,11 +129,13 @@ def cpu_baseline(name: str, reqs: int, seeds: int, workers: int) -> dict:
         model = next(x.split(":", 1)[1].strip() for x in open("/proc/cpuinfo") if x.startswith("model name"))
     except (OSError, StopIteration):
         pass
+    unit = "request" if _CPU_WORK[0][0].cfg.G is None else "whole batch"
     _CPU_WORK.clear()
     return {"value": nodes / dt, "unit": "nodes/s", "cores": workers, "kind": "oracle",
             "sample": f"{name} workload, seeds 0..{seeds - 1}, the first {reqs} requests of each "
                       f"({seeds * reqs} requests x {L} layers): the oracle's full build+verify+accept+commit "
-                      f"pipeline in fp64 numpy, one (request, layer) per task over {workers} worker "
+                      f"pipeline in fp64 numpy, one ({unit}, "
+                      f"layer) per task over {workers} worker "
                       f"processes (BLAS 1 thread each), {dt:.1f} s wall",
             "value_1core": nodes1 / dt1, "sample_1core": f"seed 0, {reqs} requests x {L} layers in one process, {dt1:.1f} s",
             "cpu_model": model}
@@ -179,7 +188,13 @@ def main():
         d = dict(lat_logp=torch.from_numpy(w.lat_logp).to(dev), lat_tok=torch.from_numpy(w.lat_tok).to(dev),
                  root_tok=torch.from_numpy(w.root_tok).to(dev), q=w.q.to(dev), k=w.k.to(dev), v=w.v.to(dev),
                  alpha=w.alpha.to(dev), beta=w.beta.to(dev), state=g.state_from_math(w.h0).to(dev))
-        d["tree"] = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N)
+        if cfg.G is None:
+            d["tree"] = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N)
+        else:
+            d["positions"] = None if cfg.positions is None else torch.tensor(cfg.positions_for(), dtype=torch.int32,
+                                                                               device=dev)
+            d["tree"] = g.gdntree_build_shared(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N, cfg.G,
+                                               d["positions"])
         torch.cuda.synchronize()
         tgt = resolve_target(d["tree"].depth.cpu().numpy(), d["tree"].n_nodes.cpu().numpy(), w.lat_tok,
                              w.tgt_choice, w.tgt_uniform)
@@ -201,8 +216,12 @@ def main():
     # the timed loops only enqueue them, so Python's argument checks stay out of the step time.
     for i, d in enumerate(sets):
         dn = sets[(i + 1) % nsets]
-        d["p_build"] = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N, out=d["tree"],
-                                       stream=stream, prepare=True)
+        if cfg.G is None:
+            d["p_build"] = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N, out=d["tree"],
+                                           stream=stream, prepare=True)
+        else:
+            d["p_build"] = g.gdntree_build_shared(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N, cfg.G,
+                                                  d["positions"], out=d["tree"], stream=stream, prepare=True)
         d["p_verify"] = g.gdntree_verify(d["tree"], d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"],
                                          o=d["o"], stream=stream, prepare=True)
         d["p_accept_commit"] = g.gdntree_accept_commit(d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"],
@@ -234,6 +253,10 @@ def main():
     # walked that request's acceptance (the build stands for the next draft, which needs the
     # accepted tokens); the next verify runs after that launch.  One stream, no events.
     def run_pipelined(i0, k):
+        if cfg.G is not None:  # a batch-budget build is two launches: no fused end of step
+            for i in range(i0, i0 + k):
+                step(i)
+            return
         sets[i0 % nsets]["p_build"]()
         for i in range(i0, i0 + k):
             d = sets[i % nsets]
@@ -320,7 +343,8 @@ def main():
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp32", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.notes}", "B": cfg.B, "L": cfg.L, "H": cfg.H, "d": cfg.D,
-                   "P": cfg.P, "K": cfg.K, "N": cfg.N, "io_dtype": cfg.dtype, "input_sets": nsets},
+                   "P": cfg.P, "K": cfg.K, "N": cfg.N, "io_dtype": cfg.dtype, "input_sets": nsets,
+                   **({} if cfg.G is None else {"G": cfg.G, "positions": list(cfg.positions or ())})},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload), "kernel": "verify_kernel",
                      "algorithmic_bytes": vbytes, "mean_us": t_verify,
@@ -329,8 +353,10 @@ def main():
                        "verify_back_to_back": t_verify},
         "sequential": {"ms_per_step": ms_seq, "value": nodes_per_step / (ms_seq * 1e-3),
                        "order": "build -> verify -> accept_commit, each step after the previous one"},
-        "pipelining": "build -> verify(i) -> [accept(i), then per request build(i+1); commit(i) beside "
-                      "them; one launch] -> verify(i+1) ...; one stream",
+        "pipelining": ("build -> verify(i) -> [accept(i), then per request build(i+1); commit(i) beside "
+                       "them; one launch] -> verify(i+1) ...; one stream") if cfg.G is None else
+                      "none: batch-budget build (per-request builds, then the budget cut) -> verify -> "
+                      "accept_commit, in order; one stream",
         "host_enqueue_us_per_step": t_enqueued / args.steps * 1e6,
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
         "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),

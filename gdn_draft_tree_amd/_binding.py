@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libgdntree.so")
 
 GDNTREE_OK, GDNTREE_ERR_ARG, GDNTREE_ERR_UNSUPPORTED, GDNTREE_ERR_DEVICE = 0, 1, 2, 3
 GDNTREE_F32, GDNTREE_BF16 = 0, 1
-EXPORTED = ("gdntree_build", "gdntree_verify", "gdntree_accept_commit", "gdntree_accept", "gdntree_commit",
+EXPORTED = ("gdntree_build", "gdntree_build_shared", "gdntree_verify", "gdntree_accept_commit", "gdntree_accept", "gdntree_commit",
             "gdntree_commit_build", "gdntree_accept_commit_build", "gdntree_status_str")
 
 
@@ -41,6 +41,8 @@ def _load() -> ctypes.CDLL:
     vp, i = ctypes.c_void_p, ctypes.c_int
     lib.gdntree_build.argtypes = [vp, vp, vp, i, i, i, i, CTree, vp]
     lib.gdntree_build.restype = i
+    lib.gdntree_build_shared.argtypes = [vp, vp, vp, vp, i, i, i, i, i, CTree, vp]
+    lib.gdntree_build_shared.restype = i
     lib.gdntree_verify.argtypes = [CTree, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, i, vp, vp]
     lib.gdntree_verify.restype = i
     lib.gdntree_accept_commit.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp,
@@ -174,6 +176,23 @@ def gdntree_build(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch
         raise ValueError("output tree has the wrong shape")
     return _run(LIB.gdntree_build, (*args, B, P, K, N, out.c(), _stream(stream)), prepare, out,
                 (lat_logp, lat_tok, root_tok, out))
+
+
+def gdntree_build_shared(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch.Tensor, N: int,
+                         G: int, positions: torch.Tensor | None = None, out: Tree | None = None,
+                         stream=None, prepare: bool = False) -> Tree:
+    """Best-first trees of a whole batch under one budget of G draft nodes; request b draws
+    from its first positions[b] lattice positions (all P when None); see gdntree.h."""
+    B, P, K = lat_logp.shape
+    out = out if out is not None else Tree.empty(B, N, lat_logp.device)
+    args = (_dev(lat_logp, "lat_logp", torch.float32, (B, P, K)),
+            _dev(lat_tok, "lat_tok", torch.int32, (B, P, K)),
+            _dev(root_tok, "root_tok", torch.int32, (B,)),
+            None if positions is None else _dev(positions, "positions", torch.int32, (B,)))
+    if out.B != B or out.N != N:
+        raise ValueError("output tree has the wrong shape")
+    return _run(LIB.gdntree_build_shared, (*args, B, P, K, N, int(G), out.c(), _stream(stream)), prepare,
+                out, (lat_logp, lat_tok, root_tok, positions, out))
 
 
 def gdntree_verify(tree: Tree, q, k, v, alpha, beta, state, o=None, out_dtype=None, stream=None,

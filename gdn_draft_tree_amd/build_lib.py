@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdntree.so")
-SOURCES = ["gdntree_api.hip", "build_tree.hip", "verify_tree.hip", "accept_commit.hip", "commit_build.hip"]
+SOURCES = ["gdntree_api.hip", "build_tree.hip", "verify_tree.hip", "accept_commit.hip", "commit_build.hip", "shared_budget.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-fvisibility=hidden",

@@ -27,6 +27,8 @@ struct BuildParams {
   const int32_t *lat_tok, *root_tok;
   int P, K, N;
   gdntree_tree out;
+  // draft positions per request [B], clipped to [0, P]; null: all P for every request
+  const int32_t *positions = nullptr;
 };
 
 template <int CTRL, int ROWMASK>
@@ -88,6 +90,8 @@ __device__ __forceinline__ double wave_max_f64(double x) {
 // the first wave alone runs the pops and writes the tree.
 __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int tid, int nth, float *s_logp) {
   const int P = bp.P, K = bp.K, N = bp.N;
+  // children are offered only at depths below this request's own position count
+  const int Pb = bp.positions ? min(max(bp.positions[b], 0), P) : P;
   const gdntree_tree &out = bp.out;
   const int PK = P * K;
   const float *lp = bp.lat_logp + (size_t)b * PK;
@@ -108,8 +112,8 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
   // LDS index of the fetched-ahead log-prob; every lane reloads its entry after each pop
   // (one unconditional read, so the value lands straight in its register)
   int nlp_at = 0;
-  if (lane == 0) {  // the root: P >= 1 and K >= 1
-    cand = 0.0 + (double)s_logp[0];
+  if (lane == 0) {  // the root (P >= 1 and K >= 1); no children when the request has no positions
+    cand = Pb > 0 ? 0.0 + (double)s_logp[0] : kNone;
     nlp_at = min(1, K - 1);
   }
   float nlp = s_logp[nlp_at];
@@ -153,7 +157,7 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
       if (lane == n) {
         my_parent = p; my_depth = d; my_rank = r; my_score = m; my_anc = a;
         my_next = 0;
-        cand = (d < P) ? m + (double)first : kNone;
+        cand = (d < Pb) ? m + (double)first : kNone;
         nlp_at = min(d, P - 1) * K + min(1, K - 1);
       }
     } else {

@@ -48,6 +48,25 @@ GDNTREE_EXPORT gdntree_status gdntree_build(const float *lat_logp, const int32_t
   return GDNTREE_OK;
 }
 
+GDNTREE_EXPORT gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_tok,
+                                                   const int32_t *root_tok, const int32_t *positions,
+                                                   int B, int P, int K, int N, int G, gdntree_tree out,
+                                                   void *stream) {
+  if (!lat_logp || !lat_tok || !root_tok || !out.parent || !out.depth || !out.rank ||
+      !out.token || !out.score || !out.anc || !out.n_nodes)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || P <= 0 || K <= 0 || N <= 0 || G < 0) return GDNTREE_ERR_ARG;
+  if (P > kMaxP || K > kMaxK || N > kMaxN || B > kSharedMaxB) return GDNTREE_ERR_UNSUPPORTED;
+  // the budget cut holds B (rounded up to a power of two) lists of min(N, G) keys in LDS
+  if (G > 0 && (long long)G < (long long)B * N &&
+      (long long)shared_budget_lists(B) * (N < G ? N : G) > kSharedMaxSlots)
+    return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  const BuildParams bp{lat_logp, lat_tok, root_tok, P, K, N, out, positions};
+  if (launch_build_shared(bp, B, G, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
 GDNTREE_EXPORT gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, int L, int H, int dk,
                                              int dv, gdntree_dtype in_dtype, const void *q,
                                              const void *k, const void *v, const void *alpha,
@@ -168,7 +187,7 @@ GDNTREE_EXPORT gdntree_status gdntree_commit_build(
   p.acc_len = const_cast<int32_t *>(acc_len); p.acc_node = const_cast<int32_t *>(acc_node);
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
-  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree};
+  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, nullptr};
   if (launch_commit_build(p, bp, next_B, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
@@ -203,7 +222,7 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
   p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
-  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree};
+  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, nullptr};
   if (launch_accept_commit_build(p, bp, next_B, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }

@@ -13,6 +13,8 @@ constexpr int kMaxSlots = kMaxN + 1;
 constexpr int kMaxP = 16;          // positions, hence tree depth
 constexpr int kMaxK = 64;          // candidates per position
 constexpr int kMaxAnc = kMaxP + 1; // ancestors-or-self of a node (depth 0..16)
+constexpr int kSharedMaxSlots = 4096;  // keys the budget cut holds: pow2(B) * min(N, G)
+constexpr int kSharedMaxB = 1024;      // requests of a build under a shared budget
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
@@ -62,6 +64,10 @@ hipError_t launch_accept_commit(const CommitParams &p, hipStream_t stream);
 hipError_t launch_accept(const CommitParams &p, hipStream_t stream);  // acceptance only
 hipError_t launch_commit(const CommitParams &p, hipStream_t stream);  // commit of a given path
 struct BuildParams;
+hipError_t launch_build_params(const BuildParams &bp, int B, hipStream_t stream);
+// per-request builds, then the cut of every request's node count to a batch budget of G drafts
+hipError_t launch_build_shared(const BuildParams &bp, int B, int G, hipStream_t stream);
+int shared_budget_lists(int B);  // B rounded up to a power of two
 // commit of a given path (p) fused with the build of nb other requests' trees (bp)
 hipError_t launch_commit_build(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream);
 // acceptance (written to p.acc_*), commit and the build of nb next trees in one launch

@@ -7,6 +7,7 @@
  *   gdntree_verify         gated-delta-rule outputs of every tree node, per GDN layer
  *   gdntree_accept_commit  greedy acceptance of the longest matching root path plus a
  *                          bonus token, then the accepted-path state commit
+ * gdntree_build_shared builds the trees of a whole batch under one shared node budget.
  * gdntree_accept_commit also comes as two calls, gdntree_accept then gdntree_commit, and
  * gdntree_commit_build / gdntree_accept_commit_build run a commit (with or without the
  * acceptance) together with the next step's tree build in one launch.
@@ -83,6 +84,34 @@ typedef struct {
 gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
                              const int32_t *root_tok, int B, int P, int K, int N,
                              gdntree_tree out, void *stream);
+
+/*
+ * gdntree_build_shared - best-first trees for a whole batch under one shared node budget.
+ *
+ * One best-first pass over the union of every request's frontier: it inserts the batch's
+ * candidate with the largest cumulative path log-prob until the batch holds G draft nodes
+ * (roots not counted) or no candidate is left.  A request holding N draft nodes offers no
+ * more, and request b takes children only from its first positions[b] lattice positions.
+ * Ties go to the smaller request index, then the smaller parent slot, then the smaller
+ * rank.  Each request's tree is then exactly the prefix of its own gdntree_build tree (over
+ * its positions) that the budget leaves it.  (SpecPilot summary, Technical novelty,
+ * batching: a node budget shared by the batch, draft positions chosen per request.)
+ *
+ *   lat_logp, lat_tok, root_tok  as for gdntree_build
+ *   positions i32 [B] or NULL    draft positions per request, clipped to [0, P] (0: the
+ *                                request gets its root only); NULL: P for every request
+ *   G                            the batch's draft-node budget, G >= 0 (0: roots only)
+ *   out                          every field written for slots < n_nodes[b]; slots at or
+ *                                past n_nodes[b] may hold nodes the budget cut off
+ * Limits: B <= 1024 and, when 0 < G < B * N, B' * min(N, G) <= 4096 with B' = B rounded up
+ * to a power of two (else ERR_UNSUPPORTED).  lat_logp must hold log-probabilities (<= 0), so
+ * that a child never outscores its parent.  Two kernels: the per-request builds, then (when
+ * G < B * N) one workgroup that merges the requests' score lists under (score desc, request,
+ * slot), keeping the first G keys, and cuts every n_nodes[b] to its slots among them.
+ */
+gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_tok,
+                                    const int32_t *root_tok, const int32_t *positions, int B,
+                                    int P, int K, int N, int G, gdntree_tree out, void *stream);
 
 /*
  * gdntree_verify - per-node gated delta rule over the tree, one or more layers.

@@ -293,14 +293,19 @@ def commit(acc_node: np.ndarray, acc_len: np.ndarray, k, v, alpha, beta, h0):
     return out
 
 
-def pipeline(lat_logp, lat_tok, root_tok, N, q, k, v, alpha, beta, h0, target_fn):
+def pipeline(lat_logp, lat_tok, root_tok, N, q, k, v, alpha, beta, h0, target_fn, G=None,
+             positions=None):
     """build -> verify -> accept -> commit for one batch.
 
     ``target_fn(tree)`` returns the per-slot target argmax [B][N+1] for the built tree (the
-    target model's LM head is outside the method; the caller supplies it).
+    target model's LM head is outside the method; the caller supplies it).  With ``G`` set,
+    the trees come from build_tree_shared (batch budget G, per-request ``positions``).
     """
     P = lat_logp.shape[1]
-    tree = build_tree(lat_logp, lat_tok, root_tok, N)
+    if G is None:
+        tree = build_tree(lat_logp, lat_tok, root_tok, N)
+    else:
+        tree = build_tree_shared(lat_logp, lat_tok, root_tok, N, G, positions)
     o, hnorm = verify(tree, q, k, v, alpha, beta, h0)
     target = target_fn(tree)
     acc_len, acc_tok, acc_node = accept(tree, target, P)

@@ -40,12 +40,18 @@ def device_inputs(w, dev="cuda"):
         state=g.state_from_math(w.h0).to(dev))
 
 
-def run_gpu(w, out_dtype=None, d=None, split=False):
+def run_gpu(w, out_dtype=None, d=None, split=False, shared=None):
     """build -> verify -> (host: synthetic target from the built tree) -> accept_commit, or
-    with split=True accept -> commit (the two-call form)."""
+    with split=True accept -> commit (the two-call form).  shared=(G, positions or None)
+    builds the trees under a batch budget of G draft nodes."""
     import gdn_draft_tree_amd as g
     d = d or device_inputs(w)
-    tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    if shared is None:
+        tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N)
+    else:
+        G, positions = shared
+        pos = None if positions is None else torch.tensor(np.asarray(positions, np.int32)).cuda()
+        tree = g.gdntree_build_shared(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N, G, pos)
     o = g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], out_dtype=out_dtype)
     torch.cuda.synchronize()
     depth = tree.depth.cpu().numpy()
@@ -65,11 +71,13 @@ def run_gpu(w, out_dtype=None, d=None, split=False):
                 state=g.state_to_math(d["state"]).cpu().numpy().astype(np.float64))
 
 
-def run_oracle(w):
+def run_oracle(w, shared=None):
     def target_fn(tree):
         return resolve_target(tree["depth"], tree["n_nodes"], w.lat_tok, w.tgt_choice, w.tgt_uniform)
+    G, positions = shared if shared is not None else (None, None)
     return oracle.pipeline(w.lat_logp, w.lat_tok, w.root_tok, w.cfg.N, w.f64("q"), w.f64("k"), w.f64("v"),
-                           w.f64("alpha"), w.f64("beta"), w.h0.double().numpy(), target_fn)
+                           w.f64("alpha"), w.f64("beta"), w.h0.double().numpy(), target_fn, G=G,
+                           positions=positions)
 
 
 def assert_tree_equal(gt, ot):
@@ -104,9 +112,9 @@ def state_errors(g_s, s_ref):
     return worst([num / den])
 
 
-def check_all(w, out_dtype=None, gpu=None, ref=None):
-    gpu = gpu or run_gpu(w, out_dtype=out_dtype)
-    ref = ref or run_oracle(w)
+def check_all(w, out_dtype=None, gpu=None, ref=None, shared=None):
+    gpu = gpu or run_gpu(w, out_dtype=out_dtype, shared=shared)
+    ref = ref or run_oracle(w, shared=shared)
     assert_tree_equal(gpu["tree"], ref["tree"])
     np.testing.assert_array_equal(gpu["target"], ref["target"])
     oe = output_errors(gpu["o"], ref["o"], ref["hnorm"], ref["tree"]["n_nodes"])

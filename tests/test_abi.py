@@ -24,7 +24,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_accept_commit_build",
-                           "gdntree_build", "gdntree_commit", "gdntree_commit_build", "gdntree_status_str",
+                           "gdntree_build", "gdntree_build_shared", "gdntree_commit", "gdntree_commit_build", "gdntree_status_str",
                            "gdntree_verify"]
 
 
@@ -79,6 +79,30 @@ def test_build_rejects(case, expect):
     if case == "N65": args["N"] = 65
     st = g.LIB.gdntree_build(args["logp"], args["tok"], args["root"], args["B"], args["P"], args["K"],
                              args["N"], args["tree"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_logp", 1), ("null_root", 1), ("null_tree_field", 1), ("B0", 1), ("N0", 1), ("Gneg", 1),
+    ("P17", 2), ("K65", 2), ("N65", 2), ("B1025", 2), ("BN4097", 2),
+])
+def test_build_shared_rejects(case, expect):
+    """Rejected on the host before any device work (a null positions array is allowed)."""
+    g = _lib()
+    a = dict(logp=FAKE, tok=FAKE, root=FAKE, B=2, P=8, K=16, N=24, G=30, tree=_tree(g))
+    if case == "null_logp": a["logp"] = None
+    if case == "null_root": a["root"] = None
+    if case == "null_tree_field": a["tree"] = _tree(g, n_nodes=1)
+    if case == "B0": a["B"] = 0
+    if case == "N0": a["N"] = 0
+    if case == "Gneg": a["G"] = -1
+    if case == "P17": a["P"] = 17
+    if case == "K65": a["K"] = 65
+    if case == "N65": a["N"] = 65
+    if case == "B1025": a.update(B=1025, N=1)
+    if case == "BN4097": a.update(B=65, N=64, G=100)   # 128 lists x 64 keys
+    st = g.LIB.gdntree_build_shared(a["logp"], a["tok"], a["root"], None, a["B"], a["P"], a["K"], a["N"],
+                                    a["G"], a["tree"], None)
     assert st == expect
 
 

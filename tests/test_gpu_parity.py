@@ -350,3 +350,37 @@ def test_repeated_launches_with_shared_cus(name, B):
                          ref["tree"]["n_nodes"])
     assert oe <= H.TOL, f"output error {oe:.3e}"
     _say(f"{name} B={B}: 3 launches identical, out_err={oe:.2e}")
+
+
+@pytest.mark.parametrize("name,B,heads,G,positions", [
+    ("ragged", 32, 2, 192, "16/12/8"),   # the batch budget of draft rows, positions per request
+    ("ragged", 32, 2, 1500, None),       # a budget that leaves some requests at the cap
+    ("batched", 24, 2, 200, None),
+    ("batched", 24, 1, 0, None),         # roots only
+    ("batched", 24, 1, 10 ** 6, "0/8/3"),  # no cut (no selection launch); zero positions
+    ("ragged", 64, 1, 1000, None),       # 64 lists x 64 keys, the largest cut
+    ("batched", 1, 1, 10, None),         # one request: no merge
+    ("batched", 100, 1, 300, "8/5"),     # 100 requests (128 lists)
+])
+def test_build_shared_full_pipeline(name, B, heads, G, positions):
+    """Shared-budget trees bit-exact against the oracle's batch-wide best-first pass; then
+    verify, acceptance and commit over those trees against the oracle."""
+    w = H.slice_workload(generate(replace(CONFIGS[name], B=B), seed=3), H=heads)
+    pos = None
+    if positions is not None:
+        cyc = [int(x) for x in positions.split("/")]
+        pos = [cyc[b % len(cyc)] for b in range(B)]
+    _say(f"shared build: {name} B={B} H={heads} G={G} positions={positions}")
+    r = H.check_all(w, shared=(G, pos))
+    n = r["gpu"]["tree"]["n_nodes"]
+    _say(f"  drafts per request {n.min() - 1}..{n.max() - 1}, total {int(n.sum()) - B}, "
+         f"out_err={r['out_err']:.2e} state_err={r['state_err']:.2e}")
+
+
+def test_build_shared_uniform_ties():
+    """Every candidate tied in every request: the cross-request rule (smaller request first)
+    and the in-request rule decide the whole allocation."""
+    w = _custom(P=4, K=4, N=40, B=6)
+    w.lat_logp[:] = np.float32(-math.log(4))
+    for G in (5, 23, 100, 239):
+        H.check_all(w, shared=(G, [4, 2, 3, 4, 1, 4]))

@@ -1,4 +1,4 @@
-"""The five workload presets.
+"""The five workload presets, and the ragged batch under a shared node budget.
 
 Shapes follow the SpecPilot summary (paper.rainbus.top/paper/2611.02501): parallel drafters
 propose 8 or 16 masked positions with a top-16 candidate lattice (section "Prerequisites >
@@ -30,7 +30,15 @@ class Config:
     p_top1_range: tuple | None = None
     # include the geometric rank-r tail (rank r>=1 with prob (1-p)*(2/3)*0.5**r)
     rank_tail: bool = True
+    # when set, the trees are built under one batch budget of G draft nodes (N stays the
+    # per-request cap), and request b uses positions[b % len(positions)] lattice positions
+    G: int | None = None
+    positions: tuple | None = None
     notes: str = field(default="", compare=False)
+
+    def positions_for(self, B: int | None = None):
+        B = self.B if B is None else B
+        return None if self.positions is None else [self.positions[b % len(self.positions)] for b in range(B)]
 
     @property
     def rows(self) -> int:
@@ -53,4 +61,11 @@ CONFIGS: dict[str, Config] = {
                      V=151936, N=64, p_top1_range=(0.6, 0.95),
                      notes="32 requests x one GDN layer, 16x16 lattices, N=64, "
                            "per-request top-1 agreement ~ U(0.6, 0.95)"),
+    # the ragged batch under a node budget shared by the batch (SpecPilot summary, Technical
+    # novelty, batching: a 192-node budget, draft positions 16/12/8 chosen per request)
+    "shared": Config("shared", B=32, L=1, H=32, D=128, dtype="bf16", P=16, K=16, V=151936,
+                     N=64, p_top1_range=(0.6, 0.95), G=192, positions=(16, 12, 8),
+                     notes="32 requests x one GDN layer, 16x16 lattices, one batch budget of 192 "
+                           "draft nodes (at most 64 per request), draft positions 16/12/8 by "
+                           "request, per-request top-1 agreement ~ U(0.6, 0.95)"),
 }
