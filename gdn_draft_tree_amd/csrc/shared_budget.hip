@@ -26,33 +26,41 @@ namespace {
 
 constexpr int kSelThreads = 1024;
 
-// "x before y" in the batch order: the larger score first, then the smaller index (the
-// request-major draft index b * N + slot - 1; a sentinel carries -inf and an index past
-// every real one)
-__device__ __forceinline__ bool before(double xs, int xi, double ys, int yi) {
-  return xs > ys || (xs == ys && xi < yi);
-}
-
 // Bp: B rounded up to a power of two; 1 <= G < B * N; Bp * min(N, G) <= kSharedMaxSlots.
+// Keys are the scores alone: every merge joins a list A of lower requests with a list C of
+// higher ones, so on equal scores A's key comes first, and within one list equal scores keep
+// slot order; each key carries its request (-1 for a sentinel, a slot that holds no node).
 __global__ __launch_bounds__(kSelThreads) void select_budget_kernel(const double *score, int32_t *n_nodes,
                                                                     int B, int Bp, int N, int G) {
   __shared__ double s_key[2][kSharedMaxSlots];
-  __shared__ int s_idx[2][kSharedMaxSlots];
+  __shared__ short s_req[2][kSharedMaxSlots];
   __shared__ int s_cnt[kSharedMaxB];
   const int tid = threadIdx.x;
-  // level 0: Bp lists (the requests, then empty ones) of their first len0 draft slots; a slot
-  // that holds no node is a sentinel
+  // level 0: Bp lists (the requests, then empty ones) of their first len0 draft slots.  Every
+  // load is issued before any is used (a slot's score is read whether or not it holds a node:
+  // it lies inside the [B][N+1] tree either way), so level 0 waits for one memory latency.
   const int len0 = N < G ? N : G;
-  for (int e = tid; e < Bp * len0; e += kSelThreads) {
-    const int j = e / len0, i = e % len0;
-    double sc = -__builtin_inf();
-    int ix = (1 << 30) + e;
-    if (j < B && i + 1 < n_nodes[j]) {
-      sc = score[(size_t)j * (N + 1) + i + 1];
-      ix = j * N + i;
+  constexpr int kPer = kSharedMaxSlots / kSelThreads;
+  double sv[kPer];
+  int room[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = tid + r * kSelThreads, j = e / len0, i = e % len0;
+    sv[r] = -__builtin_inf();
+    room[r] = 0;
+    if (e < Bp * len0 && j < B) {
+      sv[r] = score[(size_t)j * (N + 1) + i + 1];
+      room[r] = n_nodes[j] - 1 - i;  // > 0 iff slot i + 1 holds a node
     }
-    s_key[0][e] = sc;
-    s_idx[0][e] = ix;
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = tid + r * kSelThreads;
+    if (e < Bp * len0) {
+      const bool real = room[r] > 0;
+      s_key[0][e] = real ? sv[r] : -__builtin_inf();
+      s_req[0][e] = (short)(real ? e / len0 : -1);
+    }
   }
   for (int b = tid; b < B; b += kSelThreads) s_cnt[b] = 0;
   __syncthreads();
@@ -61,23 +69,21 @@ __global__ __launch_bounds__(kSelThreads) void select_budget_kernel(const double
   while (nl > 1) {
     const int nlen = 2 * len < G ? 2 * len : G;
     const double *ks = s_key[cur];
-    const int *is = s_idx[cur];
     for (int t = tid; t < (nl / 2) * nlen; t += kSelThreads) {
       const int m = t / nlen, k = t % nlen;
-      const int a0 = 2 * m * len, b0 = a0 + len;  // lists A = [a0, a0 + len) and C = [b0, b0 + len)
-      // i = how many of the first k merged keys come from A: the first i whose A[i] is not
-      // before C[k - 1 - i]
+      const int a0 = 2 * m * len, c0 = a0 + len;  // lists A = [a0, a0 + len) and C = [c0, c0 + len)
+      // i = how many of the first k merged keys come from A: the first i whose A[i] does not
+      // come before C[k - 1 - i]
       int lo = k > len ? k - len : 0, hi = k < len ? k : len;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (before(ks[a0 + mid], is[a0 + mid], ks[b0 + k - 1 - mid], is[b0 + k - 1 - mid])) lo = mid + 1;
+        if (ks[a0 + mid] >= ks[c0 + k - 1 - mid]) lo = mid + 1;
         else hi = mid;
       }
       const int i = lo, j = k - lo;
-      const bool from_a = i < len && (j >= len || before(ks[a0 + i], is[a0 + i], ks[b0 + j], is[b0 + j]));
-      const int src = from_a ? a0 + i : b0 + j;
-      s_key[cur ^ 1][m * nlen + k] = ks[src];
-      s_idx[cur ^ 1][m * nlen + k] = is[src];
+      const int src = (i < len && (j >= len || ks[a0 + i] >= ks[c0 + j])) ? a0 + i : c0 + j;
+      s_key[cur ^ 1][t] = ks[src];
+      s_req[cur ^ 1][t] = s_req[cur][src];
     }
     __syncthreads();
     cur ^= 1;
@@ -88,7 +94,7 @@ __global__ __launch_bounds__(kSelThreads) void select_budget_kernel(const double
   // every real key among the first G joins its request's count
   const int take = G < len ? G : len;
   for (int e = tid; e < take; e += kSelThreads)
-    if (s_key[cur][e] != -__builtin_inf()) atomicAdd(&s_cnt[s_idx[cur][e] / N], 1);
+    if (s_req[cur][e] >= 0) atomicAdd(&s_cnt[s_req[cur][e]], 1);
   __syncthreads();
   for (int b = tid; b < B; b += kSelThreads) n_nodes[b] = 1 + s_cnt[b];
 }
