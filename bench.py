@@ -141,6 +141,64 @@ def cpu_baseline(name: str, reqs: int, seeds: int, workers: int) -> dict:
             "cpu_model": model}
 
 
+def tau_curve(name: str, seeds: int, budgets=(4, 8, 16, 24, 32, 48, 64)) -> None:
+    """Exact replay of tau(N): for each node budget N, the library's build and acceptance (one
+    launch each, on the GPU) over the workload's seeded lattices and synthetic targets, with the
+    mean accepted length tau(N) (accepted drafts + bonus) and each launch's time.  Beside it, the
+    lattice-limited tau: the expected tau of a tree holding the whole P x K lattice, where
+    acceptance stops only when the target's token is not among a position's K candidates
+    (closed form 1 + sum_{d=1..P} (1 - u_b)^d with u_b request b's uniform-token mass), and
+    its ratio to tau(N) (the headroom a larger tree could still take).  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import gdn_draft_tree_amd as g
+    from workloads import CONFIGS, generate, resolve_target
+    from workloads.generate import target_probs
+
+    cfg = CONFIGS[name]
+    dev = torch.device("cuda:0")
+    ws = [generate(cfg, seed=s) for s in range(seeds)]
+    u = np.concatenate([[target_probs(cfg, float(p))[cfg.K] for p in w.p_top1] for w in ws])
+    tau_lat = float(np.mean([1.0 + sum((1.0 - x) ** d for d in range(1, cfg.P + 1)) for x in u]))
+    rows = []
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for N in budgets:
+        if N > cfg.N:
+            continue
+        taus, t_build, t_acc = [], [], []
+        for w in ws:
+            lp, lt, rt = (torch.from_numpy(x).to(dev) for x in (w.lat_logp, w.lat_tok, w.root_tok))
+            tree = g.gdntree_build(lp, lt, rt, N)
+            torch.cuda.synchronize()
+            tgt = resolve_target(tree.depth.cpu().numpy(), tree.n_nodes.cpu().numpy(), w.lat_tok,
+                                 w.tgt_choice[:, :N + 1], w.tgt_uniform[:, :N + 1])
+            tgt_d = torch.from_numpy(np.ascontiguousarray(tgt)).to(dev)
+            acc = g.gdntree_accept(tree, tgt_d, cfg.P)
+            p_build = g.gdntree_build(lp, lt, rt, N, out=tree, prepare=True)
+            p_acc = g.gdntree_accept(tree, tgt_d, cfg.P, acc=acc, prepare=True)
+            for _ in range(3):  # warm
+                p_build()
+                p_acc()
+            e0.record()
+            p_build()
+            e1.record()
+            p_acc()
+            e2.record()
+            torch.cuda.synchronize()
+            t_build.append(e0.elapsed_time(e1) * 1e3)
+            t_acc.append(e1.elapsed_time(e2) * 1e3)
+            taus.append(acc[0].cpu().numpy())
+        tau = np.concatenate(taus)
+        rows.append({"N": N, "tau_mean": float(tau.mean()), "tau_hist": np.bincount(tau).tolist(),
+                     "lattice_tau_over_tau": tau_lat / float(tau.mean()),
+                     "build_us": float(np.median(t_build)), "accept_us": float(np.median(t_acc))})
+    print(json.dumps({"metric": "tau(N): mean accepted length per step (accepted drafts + bonus)",
+                      "workload": f"{cfg.name}: {cfg.notes}", "requests": cfg.B * seeds,
+                      "seeds": seeds, "lattice_tau": tau_lat, "curve": rows,
+                      "data": "synthetic lattices and targets (seeded); build and acceptance on the GPU"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,12 +214,20 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB copy kernel (dst = src * 1), the reference "
                          "dispatch for scaling hardware byte counters")
+    ap.add_argument("--tau-curve", action="store_true",
+                    help="instead of the step benchmark: replay build + acceptance on the GPU over "
+                         "the workload's seeded lattices for a sweep of node budgets N and print tau(N)")
+    ap.add_argument("--tau-seeds", type=int, default=8, help="input seeds of the tau(N) replay")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
               "multi-GPU mode (the verify step shards by request or head with no exchange).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.tau_curve:
+        tau_curve(args.workload, args.tau_seeds)
+        return
 
     cpu = None
     if not args.no_cpu_baseline:

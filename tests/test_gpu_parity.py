@@ -384,3 +384,30 @@ def test_build_shared_uniform_ties():
     w.lat_logp[:] = np.float32(-math.log(4))
     for G in (5, 23, 100, 239):
         H.check_all(w, shared=(G, [4, 2, 3, 4, 1, 4]))
+
+
+@pytest.mark.parametrize("name,N", [("ragged", 8), ("ragged", 32), ("batched", 16)])
+def test_tau_replay_at_smaller_budgets(name, N):
+    """The tau(N) replay (build and acceptance alone, a budget below the workload's N, the
+    first N + 1 per-slot target draws) against the oracle: trees and acceptance bit-exact."""
+    import oracle
+    from workloads import resolve_target
+    import gdn_draft_tree_amd as g
+    w = generate(name, seed=5)
+    lp, lt, rt = (torch.from_numpy(x).cuda() for x in (w.lat_logp, w.lat_tok, w.root_tok))
+    tree = g.gdntree_build(lp, lt, rt, N)
+    torch.cuda.synchronize()
+    tgt = resolve_target(tree.depth.cpu().numpy(), tree.n_nodes.cpu().numpy(), w.lat_tok,
+                         w.tgt_choice[:, :N + 1], w.tgt_uniform[:, :N + 1])
+    acc = g.gdntree_accept(tree, torch.from_numpy(np.ascontiguousarray(tgt)).cuda(), w.cfg.P)
+    torch.cuda.synchronize()
+    ref = oracle.build_tree(w.lat_logp, w.lat_tok, w.root_tok, N)
+    H.assert_tree_equal({f: getattr(tree, f).cpu().numpy() for f in
+                         ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")}, ref)
+    tgt_ref = resolve_target(ref["depth"], ref["n_nodes"], w.lat_tok, w.tgt_choice[:, :N + 1],
+                             w.tgt_uniform[:, :N + 1])
+    a_len, a_tok, a_node = oracle.accept(ref, tgt_ref, w.cfg.P)
+    np.testing.assert_array_equal(acc[0].cpu().numpy(), a_len)
+    np.testing.assert_array_equal(acc[1].cpu().numpy(), a_tok)
+    np.testing.assert_array_equal(acc[2].cpu().numpy(), a_node)
+    _say(f"{name} N={N}: mean tau {a_len.mean():.3f}")
