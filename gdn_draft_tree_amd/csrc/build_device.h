@@ -85,20 +85,37 @@ __device__ __forceinline__ double wave_max_f64(double x) {
   return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
 }
 
-// Builds request b's tree.  Every thread of the workgroup (tid < nth) helps stage the
-// lattice's log-probs in s_logp (P * K floats of LDS) and meets the workgroup barrier; then
-// the first wave alone runs the pops and writes the tree.
-__device__ __forceinline__ void build_request(const BuildParams &bp, int b, int tid, int nth, float *s_logp) {
+// Threads t = 0..nth-1 (of some part of the workgroup) copy request b's lattice into LDS:
+// log-probs to s_logp and token ids to s_ltok (P * K entries each).
+__device__ __forceinline__ void stage_lattice(const BuildParams &bp, int b, int t, int nth, float *s_logp,
+                                              int *s_ltok) {
+  const int PK = bp.P * bp.K;
+  const float *lp = bp.lat_logp + (size_t)b * PK;
+  const int32_t *lt = bp.lat_tok + (size_t)b * PK;
+  for (int e = t; e < PK; e += nth) {
+    s_logp[e] = lp[e];
+    s_ltok[e] = lt[e];
+  }
+}
+
+// Builds request b's tree.  Unless `staged` (the caller has staged the lattice with
+// stage_lattice and met a workgroup barrier since), every thread of the workgroup (tid < nth)
+// helps stage the lattice and meets the workgroup barrier; then the first wave alone runs the
+// pops and writes the tree.
+__device__ __forceinline__ void build_request(const BuildParams &bp, int b, int tid, int nth, float *s_logp,
+                                              int *s_ltok, bool staged = false) {
   const int P = bp.P, K = bp.K, N = bp.N;
   // children are offered only at depths below this request's own position count
   const int Pb = bp.positions ? min(max(bp.positions[b], 0), P) : P;
   const gdntree_tree &out = bp.out;
   const int PK = P * K;
-  const float *lp = bp.lat_logp + (size_t)b * PK;
-  for (int e = tid; e < PK; e += nth) s_logp[e] = lp[e];
-  __syncthreads();
+  if (!staged) {
+    stage_lattice(bp, b, tid, nth, s_logp, s_ltok);
+    __syncthreads();
+  }
   if (tid >= 64) return;  // one wave builds
   const int lane = tid;
+  const int root_token = bp.root_tok[b];  // loaded now, used after the pops
   // first-child log-prob of a node at depth d (children sit at lattice position d): lane d
   const float lp_first = s_logp[min(lane, P - 1) * K];
 
@@ -168,13 +185,13 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
   }
 
   // tokens, after the build: the candidate of the node's rank at its lattice position
-  const int32_t *lt = bp.lat_tok + (size_t)b * PK;
+  const int *lt = s_ltok;
   const size_t base = (size_t)b * (N + 1);
   if (lane < n) {
     out.parent[base + lane] = my_parent;
     out.depth[base + lane] = my_depth;
     out.rank[base + lane] = my_rank;
-    out.token[base + lane] = lane == 0 ? bp.root_tok[b] : lt[(my_depth - 1) * K + my_rank];
+    out.token[base + lane] = lane == 0 ? root_token : lt[(my_depth - 1) * K + my_rank];
     out.score[base + lane] = my_score;
     out.anc[base + lane] = my_anc;
   }

@@ -8,7 +8,8 @@ namespace {
 
 __global__ __launch_bounds__(64) void build_tree_kernel(BuildParams bp) {
   __shared__ float s_logp[kMaxP * kMaxK];
-  build_request(bp, blockIdx.x, threadIdx.x, 64, s_logp);
+  __shared__ int s_ltok[kMaxP * kMaxK];
+  build_request(bp, blockIdx.x, threadIdx.x, 64, s_logp, s_ltok);
 }
 
 }  // namespace

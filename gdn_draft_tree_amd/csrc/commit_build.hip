@@ -18,9 +18,10 @@ template <int D, bool BF16IN>
 __global__ __launch_bounds__(256) void commit_build_kernel(CommitParams p, BuildParams bp, int nb) {
   __shared__ CommitSmem<D> sm;
   __shared__ float s_logp[kMaxP * kMaxK];
+  __shared__ int s_ltok[kMaxP * kMaxK];
   if ((int)blockIdx.x < nb) {
     __builtin_amdgcn_s_setprio(2);
-    build_request(bp, blockIdx.x, threadIdx.x, 256, s_logp);
+    build_request(bp, blockIdx.x, threadIdx.x, 256, s_logp, s_ltok);
     return;
   }
   commit_unit<D, BF16IN, kPathGiven>(p, blockIdx.x - nb, threadIdx.x, sm);
@@ -34,13 +35,17 @@ template <int D, bool BF16IN>
 __global__ __launch_bounds__(256) void accept_commit_build_kernel(CommitParams p, BuildParams bp, int nb, int na) {
   __shared__ CommitSmem<D> sm;
   __shared__ float s_logp[kMaxP * kMaxK];
+  __shared__ int s_ltok[kMaxP * kMaxK];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (b < na) {
     __builtin_amdgcn_s_setprio(2);
+    // waves 1-3 fetch the next lattice (an input of this launch) while wave 0 walks, so the
+    // build after the walk starts with its log-probs already in LDS
+    if (b < nb && tid >= 64) stage_lattice(bp, b, tid - 64, 192, s_logp, s_ltok);
     if (b < p.B && tid < 64) accept_walk(p, b, tid, sm.path, sm.tok, &sm.len, &sm.bonus);
     __syncthreads();
     if (b < p.B && tid <= p.P && sm.len != 0) write_acceptance(p, b, tid, sm.len, sm.path, sm.tok, sm.bonus);
-    if (b < nb) build_request(bp, b, tid, 256, s_logp);
+    if (b < nb) build_request(bp, b, tid, 256, s_logp, s_ltok, true);
     return;
   }
   commit_unit<D, BF16IN, kWalk>(p, b - na, tid, sm);
