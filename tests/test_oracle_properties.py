@@ -9,6 +9,8 @@ Each property is fixed by a definition or by mathematics, not by the oracle's ow
     verification): the accepted path matches the target on every edge, cannot be
     extended, takes the smallest matching slot at every step, and with distinct sibling
     tokens is the deepest matching root path found by enumeration;
+  * the shared node budget (same page, Technical novelty, batching): the batch holds its
+    first G trie nodes by score, each request capped at N and at its own positions;
   * the gated delta rule along the tree (same page, Prerequisites > hybrid recurrent
     architecture): a node's output equals the WY / UT closed form solved with a library
     linear solve, the tree verify of a node equals the chain verify over its root path
@@ -195,3 +197,33 @@ def test_commit_is_state_of_deepest_accepted(L, B, n, H, d, seed):
     for l, b in itertools.product(range(L), range(B)):
         np.testing.assert_allclose(np.sqrt((new[l, b] ** 2).sum(axis=(-2, -1))),
                                    hnorm[l, b, int(deepest[b])], rtol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# batch-wide best-first build under a shared budget
+# --------------------------------------------------------------------------------------
+@SETTINGS
+@given(B=st.integers(1, 5), P=st.integers(1, 3), K=st.integers(2, 4), N=st.integers(1, 20),
+       G=st.integers(0, 60), seed=st.integers(0, 2**31 - 1), data=st.data())
+def test_shared_build_is_top_g_of_the_batch(B, P, K, N, G, seed, data):
+    """Distinct scores: the batch's trees hold exactly its first G trie nodes in descending
+    score order (a request stops at N), each request in its own insertion order."""
+    positions = data.draw(st.lists(st.integers(0, P), min_size=B, max_size=B))
+    rng = np.random.default_rng(seed)
+    logp, tok = _lattice(rng, B, P, K)
+    every = []
+    for b in range(B):
+        for path, s in _all_trie_nodes(logp[b], positions[b], K):
+            every.append((s, b, path))
+    every.sort(key=lambda x: -x[0])
+    got_b = [[] for _ in range(B)]
+    total = 0
+    for s, b, path in every:
+        if total == G:
+            break
+        if len(got_b[b]) < N:
+            got_b[b].append(path)
+            total += 1
+    tree = oracle.build_tree_shared(logp, tok, np.arange(B), N, G, positions)
+    for b in range(B):
+        assert _rank_paths(tree, b)[1:] == got_b[b]
