@@ -246,7 +246,9 @@ def main():
     torch.cuda.set_device(dev)
     e = 2 if cfg.dtype == "bf16" else 4
     set_bytes = (5 * cfg.L * cfg.B * cfg.rows * cfg.H * cfg.D * e + cfg.L * cfg.B * cfg.H * cfg.D * cfg.D * 4)
-    nsets = args.sets or max(2, int(np.ceil(600e6 / set_bytes)))
+    # enough sets to exceed the 256 MB last-level cache; at most 256 (small workloads are
+    # latency-bound, and every set is generated and built up front)
+    nsets = args.sets or min(256, max(2, int(np.ceil(600e6 / set_bytes))))
 
     sets = []
     for s in range(nsets):
@@ -393,9 +395,12 @@ def main():
 
     depth = np.concatenate([d["tree"].depth.cpu().numpy()[b, :int(n)] for d in sets
                             for b, n in enumerate(d["tree"].n_nodes.cpu().numpy())])
-    tau_all = np.concatenate([d["acc"][0].cpu().numpy() for d in sets])
-    n_nodes = [int(d["tree"].n_nodes.sum()) for d in sets]
-    taus = [int(d["acc"][0].sum()) for d in sets]
+    # acceptance results exist for the sets the timed and warm-up steps ran on
+    used = sets[:min(nsets, args.warmup + args.steps)]
+    tau_all = np.concatenate([d["acc"][0].cpu().numpy() for d in used])
+    # node counts of the sets the timed steps (and the back-to-back verify launches) ran on
+    n_nodes = [int(sets[(args.warmup + i) % nsets]["tree"].n_nodes.sum()) for i in range(args.steps)]
+    taus = [int(d["acc"][0].sum()) for d in used]
     nodes_per_step = float(np.mean(n_nodes)) * cfg.L
     ms = elapsed / args.steps * 1e3
     ms_seq = elapsed_seq / args.steps * 1e3
