@@ -297,10 +297,16 @@ def main():
         d["p_accept"] = g.gdntree_accept(d["tree"], d["target"], cfg.P, acc=d["acc"], stream=stream, prepare=True)
         d["p_commit"] = g.gdntree_commit(d["tree"], d["acc"][0], d["acc"][2], d["k"], d["v"], d["alpha"], d["beta"],
                                          d["state"], cfg.P, stream=stream, prepare=True)
-        d["p_accept_commit_build"] = g.gdntree_accept_commit_build(
-            d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
-            dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, dn["tree"], acc=d["acc"], stream=stream,
-            prepare=True)
+        if cfg.G is None:
+            d["p_accept_commit_build"] = g.gdntree_accept_commit_build(
+                d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
+                dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, dn["tree"], acc=d["acc"], stream=stream,
+                prepare=True)
+        else:
+            d["p_accept_commit_build"] = g.gdntree_accept_commit_build_shared(
+                d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
+                dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, cfg.G, dn["tree"],
+                next_positions=dn["positions"], acc=d["acc"], stream=stream, prepare=True)
 
     def step(i, events=None):
         d = sets[i % nsets]
@@ -321,10 +327,6 @@ def main():
     # walked that request's acceptance (the build stands for the next draft, which needs the
     # accepted tokens); the next verify runs after that launch.  One stream, no events.
     def run_pipelined(i0, k):
-        if cfg.G is not None:  # a batch-budget build is two launches: no fused end of step
-            for i in range(i0, i0 + k):
-                step(i)
-            return
         sets[i0 % nsets]["p_build"]()
         for i in range(i0, i0 + k):
             d = sets[i % nsets]
@@ -426,8 +428,8 @@ def main():
                        "order": "build -> verify -> accept_commit, each step after the previous one"},
         "pipelining": ("build -> verify(i) -> [accept(i), then per request build(i+1); commit(i) beside "
                        "them; one launch] -> verify(i+1) ...; one stream") if cfg.G is None else
-                      "none: batch-budget build (per-request builds, then the budget cut) -> verify -> "
-                      "accept_commit, in order; one stream",
+                      "build_shared -> verify(i) -> [accept(i), then per request build(i+1); commit(i) "
+                      "beside them; one launch] -> budget cut of the trees (i+1) -> verify(i+1) ...; one stream",
         "host_enqueue_us_per_step": t_enqueued / args.steps * 1e6,
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
         "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),

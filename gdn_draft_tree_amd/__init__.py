@@ -11,6 +11,7 @@ Importing this package loads libgdntree.so and raises if it has not been built.
 from ._binding import (EXPORTED, GDNTREE_BF16, GDNTREE_ERR_ARG, GDNTREE_ERR_DEVICE,  # noqa: F401
                        GDNTREE_ERR_UNSUPPORTED, GDNTREE_F32, GDNTREE_OK, LIB, LIB_PATH, CTree,
                        GdnTreeError, Tree, gdntree_accept, gdntree_accept_commit,
-                       gdntree_accept_commit_build, gdntree_build, gdntree_build_shared,
+                       gdntree_accept_commit_build, gdntree_accept_commit_build_shared, gdntree_build,
+                       gdntree_build_shared,
                        gdntree_commit, gdntree_commit_build, gdntree_status_str, gdntree_verify)
 from .layout import state_from_math, state_to_math  # noqa: F401

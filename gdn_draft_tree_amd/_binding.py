@@ -19,7 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libgdntree.so")
 GDNTREE_OK, GDNTREE_ERR_ARG, GDNTREE_ERR_UNSUPPORTED, GDNTREE_ERR_DEVICE = 0, 1, 2, 3
 GDNTREE_F32, GDNTREE_BF16 = 0, 1
 EXPORTED = ("gdntree_build", "gdntree_build_shared", "gdntree_verify", "gdntree_accept_commit", "gdntree_accept", "gdntree_commit",
-            "gdntree_commit_build", "gdntree_accept_commit_build", "gdntree_status_str")
+            "gdntree_commit_build", "gdntree_accept_commit_build", "gdntree_accept_commit_build_shared",
+            "gdntree_status_str")
 
 
 class GdnTreeError(RuntimeError):
@@ -58,6 +59,9 @@ def _load() -> ctypes.CDLL:
     lib.gdntree_accept_commit_build.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, vp, i, i, i, i, CTree, vp]
     lib.gdntree_accept_commit_build.restype = i
+    lib.gdntree_accept_commit_build_shared.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp,
+                                                       vp, vp, vp, vp, vp, vp, i, i, i, i, i, CTree, vp]
+    lib.gdntree_accept_commit_build_shared.restype = i
     lib.gdntree_status_str.argtypes = [i]
     lib.gdntree_status_str.restype = ctypes.c_char_p
     return lib
@@ -349,3 +353,31 @@ def gdntree_accept_commit_build(tree: Tree, target_argmax, k, v, alpha, beta, st
                 prepare, (acc_len, acc_tok, acc_node),
                 (tree, target_argmax, k, v, alpha, beta, state, acc_len, acc_tok, acc_node, next_lat_logp,
                  next_lat_tok, next_root_tok, next_out))
+
+
+def gdntree_accept_commit_build_shared(tree: Tree, target_argmax, k, v, alpha, beta, state, P: int,
+                                       next_lat_logp, next_lat_tok, next_root_tok, next_N: int, next_G: int,
+                                       next_out: Tree, next_positions=None, acc=None, stream=None,
+                                       prepare: bool = False):
+    """gdntree_accept_commit_build with the next trees built under one budget of next_G draft
+    nodes (request b over its next_positions[b] positions).  Returns (acc_len, acc_tok, acc_node)."""
+    L, B, R, H, D = k.shape
+    dt = k.dtype
+    acc_len, acc_tok, acc_node = _acc_buffers(B, P, k.device, acc)
+    tp = _dev(target_argmax, "target_argmax", torch.int32, (B, R))
+    ptrs = [_dev(x, nm, dt, (L, B, R, H, D)) for x, nm in ((k, "k"), (v, "v"))]
+    ptrs += [_dev(x, nm, dt, (L, B, R, H)) for x, nm in ((alpha, "alpha"), (beta, "beta"))]
+    sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
+    ap = (_dev(acc_len, "acc_len", torch.int32, (B,)),
+          _dev(acc_tok, "acc_tok", torch.int32, (B, P + 1)),
+          _dev(acc_node, "acc_node", torch.int32, (B, P + 1)))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match the rows")
+    lp, lt, rt, Bn, Pn, Kn, Nn, nc = _next_lattice(next_lat_logp, next_lat_tok, next_root_tok, next_N, next_out)
+    pp = None if next_positions is None else _dev(next_positions, "next_positions", torch.int32, (Bn,))
+    return _run(LIB.gdntree_accept_commit_build_shared,
+                (tree.c(), B, R - 1, P, tp, L, H, D, D, _code(dt), *ptrs, sp, *ap, lp, lt, rt, pp, Bn, Pn, Kn, Nn,
+                 int(next_G), nc, _stream(stream)),
+                prepare, (acc_len, acc_tok, acc_node),
+                (tree, target_argmax, k, v, alpha, beta, state, acc_len, acc_tok, acc_node, next_lat_logp,
+                 next_lat_tok, next_root_tok, next_positions, next_out))

@@ -192,12 +192,17 @@ GDNTREE_EXPORT gdntree_status gdntree_commit_build(
   return GDNTREE_OK;
 }
 
-GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
+namespace {
+
+// The fused acceptance + commit + next build, optionally followed by the cut of the next
+// trees to a batch budget of next_G draft nodes (next_G < 0: no budget).
+gdntree_status accept_commit_build_impl(
     gdntree_tree tree, int B, int N, int P, const int32_t *target_argmax, int L, int H, int dk,
     int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
     const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
     const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
-    int next_B, int next_P, int next_K, int next_N, gdntree_tree next_tree, void *stream) {
+    const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
+    gdntree_tree next_tree, void *stream) {
   if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !k || !v || !alpha ||
       !beta || !state || !acc_len || !acc_tok || !acc_node)
     return GDNTREE_ERR_ARG;
@@ -214,6 +219,12 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
   if (N > kMaxN || P > kMaxP || next_P > kMaxP || next_K > kMaxK || next_N > kMaxN ||
       !grid_fits((long long)L * B * H + (next_B > B ? next_B : B)))
     return GDNTREE_ERR_UNSUPPORTED;
+  if (next_G >= 0) {
+    if (next_B > kSharedMaxB) return GDNTREE_ERR_UNSUPPORTED;
+    if (next_G > 0 && (long long)next_G < (long long)next_B * next_N &&
+        (long long)shared_budget_lists(next_B) * (next_N < next_G ? next_N : next_G) > kSharedMaxSlots)
+      return GDNTREE_ERR_UNSUPPORTED;
+  }
   if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
   CommitParams p{};
   p.parent = tree.parent; p.token = tree.token; p.n_nodes = tree.n_nodes; p.target = target_argmax;
@@ -222,9 +233,37 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
   p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
-  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, nullptr};
+  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, next_positions};
   if (launch_accept_commit_build(p, bp, next_B, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (next_G >= 0 && launch_budget_cut(next_tree, next_B, next_N, next_G, (hipStream_t)stream) != hipSuccess)
+    return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
+}
+
+}  // namespace
+
+GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
+    gdntree_tree tree, int B, int N, int P, const int32_t *target_argmax, int L, int H, int dk,
+    int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
+    const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
+    const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
+    int next_B, int next_P, int next_K, int next_N, gdntree_tree next_tree, void *stream) {
+  return accept_commit_build_impl(tree, B, N, P, target_argmax, L, H, dk, dv, in_dtype, k, v, alpha, beta, state,
+                                  acc_len, acc_tok, acc_node, next_lat_logp, next_lat_tok, next_root_tok, nullptr,
+                                  next_B, next_P, next_K, next_N, -1, next_tree, stream);
+}
+
+GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build_shared(
+    gdntree_tree tree, int B, int N, int P, const int32_t *target_argmax, int L, int H, int dk,
+    int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
+    const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
+    const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
+    const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
+    gdntree_tree next_tree, void *stream) {
+  if (next_G < 0) return GDNTREE_ERR_ARG;
+  return accept_commit_build_impl(tree, B, N, P, target_argmax, L, H, dk, dv, in_dtype, k, v, alpha, beta, state,
+                                  acc_len, acc_tok, acc_node, next_lat_logp, next_lat_tok, next_root_tok,
+                                  next_positions, next_B, next_P, next_K, next_N, next_G, next_tree, stream);
 }
 
 GDNTREE_EXPORT const char *gdntree_status_str(int status) {

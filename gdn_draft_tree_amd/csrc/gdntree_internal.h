@@ -68,6 +68,8 @@ hipError_t launch_build_params(const BuildParams &bp, int B, hipStream_t stream)
 // per-request builds, then the cut of every request's node count to a batch budget of G drafts
 hipError_t launch_build_shared(const BuildParams &bp, int B, int G, hipStream_t stream);
 int shared_budget_lists(int B);  // B rounded up to a power of two
+// the cut alone, for trees already built per request (capped at N)
+hipError_t launch_budget_cut(const gdntree_tree &out, int B, int N, int G, hipStream_t stream);
 // commit of a given path (p) fused with the build of nb other requests' trees (bp)
 hipError_t launch_commit_build(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream);
 // acceptance (written to p.acc_*), commit and the build of nb next trees in one launch

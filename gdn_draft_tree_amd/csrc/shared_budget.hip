@@ -113,17 +113,21 @@ int shared_budget_lists(int B) {
   return Bp;
 }
 
+hipError_t launch_budget_cut(const gdntree_tree &out, int B, int N, int G, hipStream_t stream) {
+  if (G >= B * N) return hipSuccess;  // no request is cut: the independent builds are the answer
+  if (G == 0) {
+    hipLaunchKernelGGL(roots_only_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, out.n_nodes, B);
+  } else {
+    hipLaunchKernelGGL(select_budget_kernel, dim3(1), dim3(kSelThreads), 0, stream, (const double *)out.score,
+                       out.n_nodes, B, shared_budget_lists(B), N, G);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_build_shared(const BuildParams &bp, int B, int G, hipStream_t stream) {
   hipError_t e = launch_build_params(bp, B, stream);
   if (e != hipSuccess) return e;
-  if (G >= B * bp.N) return hipSuccess;  // no request is cut: the independent builds are the answer
-  if (G == 0) {
-    hipLaunchKernelGGL(roots_only_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, bp.out.n_nodes, B);
-  } else {
-    hipLaunchKernelGGL(select_budget_kernel, dim3(1), dim3(kSelThreads), 0, stream,
-                       (const double *)bp.out.score, bp.out.n_nodes, B, shared_budget_lists(B), bp.N, G);
-  }
-  return hipGetLastError();
+  return launch_budget_cut(bp.out, B, bp.N, G, stream);
 }
 
 }  // namespace gdntree

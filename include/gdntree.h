@@ -7,7 +7,8 @@
  *   gdntree_verify         gated-delta-rule outputs of every tree node, per GDN layer
  *   gdntree_accept_commit  greedy acceptance of the longest matching root path plus a
  *                          bonus token, then the accepted-path state commit
- * gdntree_build_shared builds the trees of a whole batch under one shared node budget.
+ * gdntree_build_shared builds the trees of a whole batch under one shared node budget, and
+ * gdntree_accept_commit_build_shared fuses that build into the end of the previous step.
  * gdntree_accept_commit also comes as two calls, gdntree_accept then gdntree_commit, and
  * gdntree_commit_build / gdntree_accept_commit_build run a commit (with or without the
  * acceptance) together with the next step's tree build in one launch.
@@ -251,6 +252,27 @@ gdntree_status gdntree_accept_commit_build(gdntree_tree tree, int B, int N, int 
                                            const int32_t *next_root_tok, int next_B, int next_P,
                                            int next_K, int next_N, gdntree_tree next_tree,
                                            void *stream);
+
+/*
+ * gdntree_accept_commit_build_shared - gdntree_accept_commit_build with the next step's trees
+ * built under one batch budget: the same launch (acceptance, commit, per-request builds, here
+ * over each request's next_positions[b] positions), then the cut of every next_tree.n_nodes[b]
+ * to the request's drafts among the batch's first next_G (as gdntree_build_shared).  For
+ * callers that build under a shared budget every step (SpecPilot summary, Technical novelty,
+ * batching).  Bitwise the same results as gdntree_accept_commit followed by
+ * gdntree_build_shared.
+ *
+ *   next_positions i32 [next_B] or NULL, next_G >= 0   as for gdntree_build_shared
+ *   the rest as for gdntree_accept_commit_build; the limits of gdntree_build_shared apply to
+ *   next_B, next_N and next_G.
+ */
+gdntree_status gdntree_accept_commit_build_shared(
+    gdntree_tree tree, int B, int N, int P, const int32_t *target_argmax, int L, int H, int dk,
+    int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
+    const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
+    const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
+    const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
+    gdntree_tree next_tree, void *stream);
 
 /* Human-readable name of a status code ("unknown status" for other values). */
 const char *gdntree_status_str(int status);

@@ -24,7 +24,7 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_accept_commit_build",
-                           "gdntree_build", "gdntree_build_shared", "gdntree_commit", "gdntree_commit_build", "gdntree_status_str",
+                           "gdntree_accept_commit_build_shared", "gdntree_build", "gdntree_build_shared", "gdntree_commit", "gdntree_commit_build", "gdntree_status_str",
                            "gdntree_verify"]
 
 
@@ -274,3 +274,21 @@ def test_binding_checks_devices_and_dtypes():
         g.gdntree_build(torch.zeros(1, 4, 4), torch.zeros(1, 4, 4, dtype=torch.int32),
                         torch.zeros(1, dtype=torch.int32), 8,
                         out=g.Tree(*[torch.zeros(1, 9)] * 6, torch.zeros(1)))
+
+
+@pytest.mark.parametrize("case,expect", [("Gneg", 1), ("null_state", 1), ("same_tree", 1), ("nB1025", 2),
+                                         ("cut_too_big", 2), ("N65", 2)])
+def test_accept_commit_build_shared_rejects(case, expect):
+    g = _lib()
+    a = dict(tree=_tree(g), nt=g.CTree(**{f: FAKE + 8 for f, _ in g.CTree._fields_}), st=FAKE, nB=2, nN=24, G=30,
+             N=24)
+    if case == "Gneg": a["G"] = -1
+    if case == "null_state": a["st"] = None
+    if case == "same_tree": a["nt"] = _tree(g)
+    if case == "nB1025": a.update(nB=1025, nN=1, G=10)
+    if case == "cut_too_big": a.update(nB=65, nN=64, G=100)
+    if case == "N65": a["N"] = 65
+    st = g.LIB.gdntree_accept_commit_build_shared(a["tree"], 2, a["N"], 8, FAKE, 1, 4, 128, 128, 1, FAKE, FAKE,
+                                                  FAKE, FAKE, a["st"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                                  a["nB"], 8, 16, a["nN"], a["G"], a["nt"], None)
+    assert st == expect

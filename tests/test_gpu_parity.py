@@ -411,3 +411,45 @@ def test_tau_replay_at_smaller_budgets(name, N):
     np.testing.assert_array_equal(acc[1].cpu().numpy(), a_tok)
     np.testing.assert_array_equal(acc[2].cpu().numpy(), a_node)
     _say(f"{name} N={N}: mean tau {a_len.mean():.3f}")
+
+
+
+@pytest.mark.parametrize("G,positions", [(192, "16/12/8"), (0, None), (10 ** 6, "4/16")])
+def test_accept_commit_build_shared_equals_the_two_calls(G, positions):
+    """Acceptance + commit + the next trees under a batch budget in one call equal
+    gdntree_accept_commit then gdntree_build_shared, bitwise; the next trees equal the oracle's."""
+    import oracle
+    import gdn_draft_tree_amd as g
+    cur = H.slice_workload(generate("ragged", seed=7), B=32, H=2)
+    nxt = generate("ragged", seed=8)
+    pos = None if positions is None else [int(x) for x in positions.split("/")]
+    pos = None if pos is None else [pos[b % len(pos)] for b in range(32)]
+    runs = []
+    for fused in (True, False):
+        d = H.device_inputs(cur)
+        tree = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cur.cfg.N)
+        torch.cuda.synchronize()
+        from workloads import resolve_target
+        tgt = torch.from_numpy(resolve_target(tree.depth.cpu().numpy(), tree.n_nodes.cpu().numpy(), cur.lat_tok,
+                                              cur.tgt_choice, cur.tgt_uniform)).cuda()
+        nl = [torch.from_numpy(x).cuda() for x in (nxt.lat_logp, nxt.lat_tok, nxt.root_tok)]
+        npos = None if pos is None else torch.tensor(pos, dtype=torch.int32).cuda()
+        nout = g.Tree.empty(32, nxt.cfg.N, "cuda")
+        if fused:
+            acc = g.gdntree_accept_commit_build_shared(tree, tgt, d["k"], d["v"], d["alpha"], d["beta"], d["state"],
+                                                       cur.cfg.P, *nl, nxt.cfg.N, G, nout, next_positions=npos)
+        else:
+            acc = g.gdntree_accept_commit(tree, tgt, d["k"], d["v"], d["alpha"], d["beta"], d["state"], cur.cfg.P)
+            g.gdntree_build_shared(*nl, nxt.cfg.N, G, npos, out=nout)
+        torch.cuda.synchronize()
+        runs.append(dict(acc=[a.cpu().numpy() for a in acc], state=d["state"].cpu().numpy(),
+                         tree={f: getattr(nout, f).cpu().numpy() for f in
+                               ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")}))
+    a, b = runs
+    for x, y in zip(a["acc"], b["acc"]):
+        np.testing.assert_array_equal(x, y)
+    assert a["state"].tobytes() == b["state"].tobytes()
+    ref = oracle.build_tree_shared(nxt.lat_logp, nxt.lat_tok, nxt.root_tok, nxt.cfg.N, G, pos)
+    H.assert_tree_equal(a["tree"], ref)
+    H.assert_tree_equal(b["tree"], ref)
+    _say(f"fused shared build G={G}: drafts {int(ref['n_nodes'].sum()) - 32}")
