@@ -5,6 +5,10 @@ target, as hand-written gfx950 (MI355X) HIP kernels behind a C ABI (include/gdnt
     o    = gdntree_verify(tree, q, k, v, alpha, beta, state)          # per GDN layer
     acc  = gdntree_accept_commit(tree, target_argmax, k, v, alpha, beta, state, P)
     # or, split: acc = gdntree_accept(tree, target_argmax, P); gdntree_commit(tree, acc[0], acc[2], ...)
+    # a whole batch under one budget of G draft nodes (request b over positions[b] positions):
+    tree = gdntree_build_shared(lat_logp, lat_tok, root_tok, N, G, positions)
+    # the end of a step fused with the next step's build (optionally under a batch budget):
+    acc  = gdntree_accept_commit_build(tree, target_argmax, k, v, alpha, beta, state, P, *next_lattice, N, next_tree)
 
 Importing this package loads libgdntree.so and raises if it has not been built.
 """
