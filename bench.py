@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BASELINE_METRIC = "GDN tree-verify nodes/s per layer + achieved HBM GB/s vs ~8 TB/s peak"
 COPY_BYTES = 256 << 20
 VERIFY_SRC = os.path.join(ROOT, "gdn_draft_tree_amd", "csrc", "verify_tree.hip")
 COUNTERS_MD = os.path.join(ROOT, "profiles", "verify_kernel_ragged_counters.md")
@@ -141,6 +142,49 @@ def cpu_baseline(name: str, reqs: int, seeds: int, workers: int) -> dict:
             "cpu_model": model}
 
 
+def stream_ceiling(cfg, units: int, rows_per_unit: float, reps: int = 100) -> dict:
+    """What this part streams for the verify launch's traffic with none of its work: the probe
+    kernel (gdn_draft_tree_amd/csrc/stream_probe.hip) with one workgroup per (layer, request,
+    head) reading that unit's state and rows and writing its output rows; the same reads alone;
+    and one plain 1 GiB read.  Buffers rotate over more than 512 MB (so the 256 MB last-level
+    cache cannot serve the reads); median over `reps` launches, each timed with HIP events."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    probe = ctypes.CDLL(os.path.join(ROOT, "gdn_draft_tree_amd", "libgdntree_probe.so"))
+    probe.gdntree_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_int, ctypes.c_void_p]
+    e = 2 if cfg.dtype == "bf16" else 4
+    rd = int(units * (4 * cfg.D * cfg.D + rows_per_unit * (3 * cfg.D * e + 2 * e))) // 16 * 16
+    wr = int(units * rows_per_unit * cfg.D * e) // 16 * 16
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, rbytes, wbytes, blocks in (("verify_mix", rd, wr, units), ("verify_reads_only", rd, 0, units),
+                                         ("read_1GiB", 1 << 30, 0, 4096)):
+        nbuf = max(2, -(-(600 << 20) // rbytes))
+        src = torch.empty(nbuf * rbytes, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty(max(16, nbuf * wbytes), dtype=torch.uint8, device="cuda")
+        ts = []
+        for i in range(reps + 5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            st = probe.gdntree_probe_stream(src.data_ptr() + (i % nbuf) * rbytes, rbytes,
+                                            dst.data_ptr() + (i % nbuf) * wbytes, wbytes, blocks, stream.cuda_stream)
+            b.record(stream)
+            if st != 0:
+                raise RuntimeError(f"stream probe failed: {st}")
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ts[5:]])) * 1e3
+        out[name] = {"read_bytes": rbytes, "write_bytes": wbytes, "blocks": blocks, "median_us": us,
+                     "GBps": (rbytes + wbytes) / (us * 1e-6) / 1e9,
+                     "frac_of_peak": (rbytes + wbytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del src, dst
+    return out
+
+
 def tau_curve(name: str, seeds: int, budgets=(4, 8, 16, 24, 32, 48, 64)) -> None:
     """Exact replay of tau(N): for each node budget N, the library's build and acceptance (one
     launch each, on the GPU) over the workload's seeded lattices and synthetic targets, with the
@@ -218,6 +262,10 @@ def main():
                     help="instead of the step benchmark: replay build + acceptance on the GPU over "
                          "the workload's seeded lattices for a sweep of node budgets N and print tau(N)")
     ap.add_argument("--tau-seeds", type=int, default=8, help="input seeds of the tau(N) replay")
+    ap.add_argument("--reps", type=int, default=200,
+                    help="verify (and commit) launches timed one by one for the medians (>= 100)")
+    ap.add_argument("--no-stream-ceiling", action="store_true",
+                    help="skip the streaming probe that measures what this part streams for the verify's bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
@@ -255,7 +303,7 @@ def main():
         w = generate(cfg, seed=s)
         d = dict(lat_logp=torch.from_numpy(w.lat_logp).to(dev), lat_tok=torch.from_numpy(w.lat_tok).to(dev),
                  root_tok=torch.from_numpy(w.root_tok).to(dev), q=w.q.to(dev), k=w.k.to(dev), v=w.v.to(dev),
-                 alpha=w.alpha.to(dev), beta=w.beta.to(dev), state=g.state_from_math(w.h0).to(dev))
+                 alpha=w.alpha.to(dev), beta=w.beta.to(dev), state=w.h0.to(dev))
         if cfg.G is None:
             d["tree"] = g.gdntree_build(d["lat_logp"], d["lat_tok"], d["root_tok"], cfg.N)
         else:
@@ -376,6 +424,26 @@ def main():
     torch.cuda.synchronize()
     t_verify = e0.elapsed_time(e1) * 1e3 / args.steps
 
+    # the verify and the commit one launch at a time, each between its own pair of events, over
+    # `reps` launches (rotating input sets): medians
+    reps = max(100, args.reps)
+    vev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (a, b) in enumerate(vev):
+        a.record(stream)
+        sets[i % nsets]["p_verify"]()
+        b.record(stream)
+    torch.cuda.synchronize()
+    vus = np.array([a.elapsed_time(b) for a, b in vev]) * 1e3
+    vnodes = np.array([int(sets[i % nsets]["tree"].n_nodes.sum()) for i in range(reps)]) * cfg.L
+    for i, (a, b) in enumerate(vev):
+        d = sets[i % nsets]
+        d["p_build"]()   # a fresh tree: the commit below runs on the same (deterministic) tree
+        a.record(stream)
+        d["p_accept_commit"]()
+        b.record(stream)
+    torch.cuda.synchronize()
+    cus = np.array([a.elapsed_time(b) for a, b in vev]) * 1e3
+
     # a real model calls verify once per layer: for stacked layers, the same work as L launches
     # of one layer each (back to back, rotating input sets)
     t_verify_layers = None
@@ -410,18 +478,27 @@ def main():
     cbytes = float(np.mean([commit_bytes(cfg, t) for t in taus]))
     achieved = vbytes / (t_verify * 1e-6) / 1e9
 
+    vmed = float(np.median(vus))
     out = {
-        "metric": "GDN tree-verify nodes/s per layer", "value": nodes_per_step / (ms * 1e-3),
+        "metric": BASELINE_METRIC, "value": nodes_per_step / (ms * 1e-3),
         "unit": "nodes/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp32", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.notes}", "B": cfg.B, "L": cfg.L, "H": cfg.H, "d": cfg.D,
                    "P": cfg.P, "K": cfg.K, "N": cfg.N, "io_dtype": cfg.dtype, "input_sets": nsets,
                    **({} if cfg.G is None else {"G": cfg.G, "positions": list(cfg.positions or ())})},
+        "value_is": ("verified (node, layer) pairs per second over whole pipelined steps (build, verify, "
+                     "acceptance and commit of every request); the per-layer verify rate by the verify "
+                     "kernel's own time is verify_nodes_per_s"),
+        "verify_nodes_per_s": float(np.median(vnodes / (vus * 1e-6))),
+        "verify_us": {"median": vmed, "p10": float(np.percentile(vus, 10)), "p90": float(np.percentile(vus, 90)),
+                      "reps": reps, "mean_back_to_back": t_verify, "mean_in_step": t_verify_step},
+        "commit_us": {"median": float(np.median(cus)), "reps": reps,
+                      "what": "acceptance + accepted-path commit (one launch), after a build"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload), "kernel": "verify_kernel",
                      "algorithmic_bytes": vbytes, "mean_us": t_verify,
-                     "mean_us_in_step": t_verify_step},
+                     "frac_at_median": vbytes / (vmed * 1e-6) / 1e9 / HBM_PEAK_GBS},
         "kernels_us": {"build": t_build, "verify": t_verify_step, "accept_commit": t_commit,
                        "verify_back_to_back": t_verify},
         "sequential": {"ms_per_step": ms_seq, "value": nodes_per_step / (ms_seq * 1e-3),
@@ -430,19 +507,26 @@ def main():
                        "them; one launch] -> verify(i+1) ...; one stream") if cfg.G is None else
                       "build_shared -> verify(i) -> [accept(i), then per request build(i+1); commit(i) "
                       "beside them; one launch] -> budget cut of the trees (i+1) -> verify(i+1) ...; one stream",
+        "pipelining_leaves_out": ("the drafter: in a decode loop the next lattice comes from a drafter run on "
+                                  "the accepted tokens, between acceptance and build; here the lattices are "
+                                  "inputs, so the pipelined step hides the build behind the commit as a "
+                                  "drafter would hide the commit; the in-order figure is `sequential`"),
         "host_enqueue_us_per_step": t_enqueued / args.steps * 1e6,
         "commit_GBps": cbytes / (t_commit * 1e-6) / 1e9,
-        "verify_nodes_per_s": nodes_per_step / (t_verify * 1e-6),
-        "verify_draft_nodes_per_s": (nodes_per_step - cfg.B * cfg.L) / (t_verify * 1e-6),
+        "verify_draft_nodes_per_s": (nodes_per_step - cfg.B * cfg.L) / (vmed * 1e-6),
         "verify_per_layer_launches_us": t_verify_layers,
         "tree": {"depth_max": int(depth.max()), "depth_mean": float(depth.mean()),
                  "depth_hist": np.bincount(depth).tolist(),
                  "tau_hist": np.bincount(tau_all, minlength=2)[1:].tolist()},
         "tau_mean": float(np.mean(taus)) / cfg.B,
-        "precision": "bf16 rows and outputs; fp32 state, gates, path solve and accumulation; MFMA "
-                     "operands in fp16 (state and v columns scaled by a power of two per 16-channel "
-                     "slice); fp64 tree scores",
+        "precision": "state products fp32-exact: every fp32 state entry split into three bf16 parts (its "
+                     "24-bit significand exactly) times the bf16 rows on MFMA, fp32 accumulation; Gram "
+                     "entries exact products accumulated in fp32; path solves, gates and the per-node "
+                     "ancestor sums in fp32; commit in fp32; bf16 rows and outputs; fp64 tree scores",
     }
+    if not args.no_stream_ceiling:
+        out["stream_ceiling"] = stream_ceiling(cfg, cfg.L * cfg.B * cfg.H,
+                                               nodes_per_step / (cfg.L * cfg.B))
     if cpu is not None:
         out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)

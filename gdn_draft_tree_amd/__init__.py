@@ -18,4 +18,3 @@ from ._binding import (EXPORTED, GDNTREE_BF16, GDNTREE_ERR_ARG, GDNTREE_ERR_DEVI
                        gdntree_accept_commit_build, gdntree_accept_commit_build_shared, gdntree_build,
                        gdntree_build_shared,
                        gdntree_commit, gdntree_commit_build, gdntree_status_str, gdntree_verify)
-from .layout import state_from_math, state_to_math  # noqa: F401

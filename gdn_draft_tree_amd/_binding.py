@@ -204,7 +204,7 @@ def gdntree_verify(tree: Tree, q, k, v, alpha, beta, state, o=None, out_dtype=No
     """Per-node GDN outputs o [L][B][N+1][H][d_v] for every tree slot < n_nodes.
 
     q, k, v: [L][B][N+1][H][d]; alpha, beta: [L][B][N+1][H] (bf16 or fp32, all the same);
-    state: fp32 [L][B][H][d_v][d_k] (the transpose of the d_k x d_v state), read only.
+    state: fp32 [L][B][H][d_k][d_v] (the d_k x d_v state S of every head), read only.
     """
     L, B, R, H, D = q.shape
     dt = q.dtype

@@ -12,6 +12,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdntree.so")
 SOURCES = ["gdntree_api.hip", "build_tree.hip", "verify_tree.hip", "accept_commit.hip", "commit_build.hip", "shared_budget.hip"]
+# the benchmark's streaming probe, in a library of its own (not part of the path's ABI)
+PROBE_SOURCES = ["stream_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libgdntree_probe.so")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-fvisibility=hidden",
@@ -21,9 +24,14 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+    _build_one(PROBE_LIB, PROBE_SOURCES, verbose, extra)
+    return _build_one(LIB, SOURCES, verbose, extra)
+
+
+def _build_one(lib: str, sources: list[str], verbose: bool, extra: list[str] | None) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *FLAGS, *(extra or []), *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    tmp = lib + ".tmp"
+    cmd = [hipcc, *FLAGS, *(extra or []), *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -33,8 +41,8 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

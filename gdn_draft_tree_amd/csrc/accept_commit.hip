@@ -25,7 +25,7 @@ __global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
 
 template <int D, bool BF16IN, int PATH>
 hipError_t launch_d(const CommitParams &p, hipStream_t stream) {
-  const long long blocks = (long long)p.L * p.B * p.H * (D / 32);
+  const long long blocks = (long long)p.L * p.B * p.H;
   hipLaunchKernelGGL((commit_kernel<D, BF16IN, PATH>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

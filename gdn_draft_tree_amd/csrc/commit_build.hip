@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void accept_commit_build_kernel(CommitParams p
 template <int D, bool BF16IN>
 hipError_t launch_acb(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream) {
   const int na = nb > p.B ? nb : p.B;
-  const long long blocks = (long long)na + (long long)p.L * p.B * p.H * (D / 32);
+  const long long blocks = (long long)na + (long long)p.L * p.B * p.H;
   hipLaunchKernelGGL((accept_commit_build_kernel<D, BF16IN>), dim3((unsigned)blocks), dim3(256), 0, stream, p, bp,
                      nb, na);
   return hipGetLastError();
@@ -62,7 +62,7 @@ hipError_t launch_acb(const CommitParams &p, const BuildParams &bp, int nb, hipS
 
 template <int D, bool BF16IN>
 hipError_t launch_cb(const CommitParams &p, const BuildParams &bp, int nb, hipStream_t stream) {
-  const long long blocks = (long long)nb + (long long)p.L * p.B * p.H * (D / 32);
+  const long long blocks = (long long)nb + (long long)p.L * p.B * p.H;
   hipLaunchKernelGGL((commit_build_kernel<D, BF16IN>), dim3((unsigned)blocks), dim3(256), 0, stream, p, bp, nb);
   return hipGetLastError();
 }

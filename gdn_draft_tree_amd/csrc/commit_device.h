@@ -10,12 +10,14 @@
 // accepted node, recomputed from the committed state through the tau accepted rows with
 // the gated delta rule and written back in place.
 //
-// Commit kernel: one workgroup of 256 lanes owns 32 value channels j of one (layer, request,
-// head): eight lanes per channel, each holding 16 (d_k = 128) or 8 (d_k = 64) entries of
-// column j of the state, which is one contiguous row of the [d_v][d_k] layout.  Either wave 0
-// of every workgroup walks its request's tree itself (at most 17 ballot steps over 65 slots),
-// so that acceptance and commit are one launch, or the workgroup takes the accepted path
-// that the acceptance kernel (one wave per request) wrote before.
+// Commit kernel: one workgroup of 256 lanes per (layer, request, head), in the [d_k][d_v]
+// state layout: lane (w, l) of the first 2 d lanes owns value channel j = 32 w + (l & 31) and
+// the half l >> 5 of its column (d/2 entries), so each load or store instruction moves two
+// 128-byte runs of consecutive channels, and the column's dot product k . S_j is the sum of
+// the two halves, one lane-exchange away.  Either wave 0 walks its request's tree itself (at
+// most 17 ballot steps over 65 slots), so that acceptance and commit are one launch, or the
+// workgroup takes the accepted path that the acceptance kernel (one wave per request) wrote
+// before.
 
 #pragma once
 
@@ -70,7 +72,7 @@ __device__ __forceinline__ void write_acceptance(const CommitParams &p, int b, i
 template <int D>
 struct CommitSmem {
   float k[kMaxAnc][D];
-  float v[kMaxAnc][32];
+  float v[kMaxAnc][D];
   float a[kMaxAnc], b[kMaxAnc];
   int path[kMaxAnc];
   int tok[kMaxSlots];
@@ -82,36 +84,37 @@ enum CommitPath {
   kPathGiven = 0,      // read from acc_len / acc_node and checked (tau in [1, P+1], slot 0
                        // first, each next slot a child of the previous one within the node
                        // count; a path that fails leaves the request's state untouched)
-  kWalkAndWrite = 1,   // wave 0 walks the tree; the (0, 0, 0) workgroup of each request
-                       // writes the acceptance
+  kWalkAndWrite = 1,   // wave 0 walks the tree; the (0, 0) workgroup of each request writes
+                       // the acceptance
   kWalk = 2,           // wave 0 walks the tree; the acceptance is written elsewhere
 };
 
-// Commit of work unit `blk` (one 32-channel slice of one (layer, request, head)) by the 256
-// threads of a workgroup.
+// Commit of work unit `hh` (one (layer, request, head)) by the 256 threads of a workgroup.
 template <int D, bool BF16IN, int PATH>
-__device__ __forceinline__ void commit_unit(const CommitParams &p, int blk, int tid, CommitSmem<D> &sm) {
+__device__ __forceinline__ void commit_unit(const CommitParams &p, int hh, int tid, CommitSmem<D> &sm) {
   typedef typename std::conditional<BF16IN, uint16_t, float>::type T;
-  constexpr int SL = D / 32;       // workgroups (slices of 32 channels) per head
-  constexpr int EPL = D / 8;       // state entries per lane
-  constexpr int F4 = EPL / 4;      // float4 per lane
+  constexpr int EPL = D / 2;       // state entries per lane: half a column
+  static_assert(2 * D <= 256, "one lane per half column");
   float(&s_k)[kMaxAnc][D] = sm.k;
-  float(&s_v)[kMaxAnc][32] = sm.v;
+  float(&s_v)[kMaxAnc][D] = sm.v;
   float *s_a = sm.a, *s_b = sm.b;
   int *s_path = sm.path, *s_tok = sm.tok;
   int &s_len = sm.len, &s_bonus = sm.bonus, &s_bad = sm.bad;
 
   const int lane = tid & 63, wave = tid >> 6;
-  const int hh = blk / SL, js = blk % SL;
   const int h = hh % p.H, lb = hh / p.H, b = lb % p.B, l = lb / p.B;
-  const int c = tid >> 3, sub = tid & 7;
-  const int j = js * 32 + c;
+  const bool act = tid < 2 * D;
+  const int j = 32 * wave + (lane & 31), i0 = (lane >> 5) * EPL;
 
-  // state column j, entries i = 4 * (sub + 8 m) + 0..3
-  float *col = p.state + ((size_t)hh * D + j) * D;
-  float4 st[F4];
+  // entries i0 .. i0 + EPL - 1 of column j: S[i][j] at i * D + j
+  float *S = p.state + (size_t)hh * D * D;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(S, 0, D * D * 4, 0x00020000);
+  const int voff = (i0 * D + j) * 4;
+  float st[EPL];
+  if (act) {
 #pragma unroll
-  for (int m = 0; m < F4; ++m) st[m] = *reinterpret_cast<const float4 *>(col + 4 * (sub + 8 * m));
+    for (int m = 0; m < EPL; ++m) st[m] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, m * D * 4, 0));
+  }
 
   if constexpr (PATH != kPathGiven) {
     if (wave == 0) accept_walk(p, b, lane, s_path, s_tok, &s_len, &s_bonus);
@@ -136,20 +139,20 @@ __device__ __forceinline__ void commit_unit(const CommitParams &p, int blk, int 
   if (len == 0) return;  // malformed node count or path: nothing is written
 
   if constexpr (PATH == kWalkAndWrite) {
-    if (l == 0 && h == 0 && js == 0 && tid <= p.P) write_acceptance(p, b, tid, len, s_path, s_tok, s_bonus);
+    if (l == 0 && h == 0 && tid <= p.P) write_acceptance(p, b, tid, len, s_path, s_tok, s_bonus);
   }
 
-  // rows of the accepted path: k (all d_k), v (this slice's 32 channels), alpha, beta
+  // rows of the accepted path: k and v (all channels), alpha, beta
   const T *gk = static_cast<const T *>(p.k);
   const T *gv = static_cast<const T *>(p.v);
   const T *ga = static_cast<const T *>(p.alpha);
   const T *gb = static_cast<const T *>(p.beta);
   const size_t rowbase = (size_t)lb * p.R;
-  for (int e = tid; e < len * (D + 32); e += 256) {
-    const int x = e / (D + 32), r = e % (D + 32);
+  for (int e = tid; e < len * 2 * D; e += 256) {
+    const int x = e / (2 * D), r = e % (2 * D);
     const size_t ro = ((rowbase + s_path[x]) * p.H + h) * (size_t)D;
     if (r < D) s_k[x][r] = load_elem(gk, ro + r);
-    else s_v[x][r - D] = load_elem(gv, ro + js * 32 + (r - D));
+    else s_v[x][r - D] = load_elem(gv, ro + (r - D));
   }
   for (int x = tid; x < len; x += 256) {
     const size_t gi = (rowbase + s_path[x]) * p.H + h;
@@ -157,35 +160,34 @@ __device__ __forceinline__ void commit_unit(const CommitParams &p, int blk, int 
     s_b[x] = load_elem(gb, gi);
   }
   __syncthreads();
+  if (!act) return;
 
   for (int x = 0; x < len; ++x) {
     float dot = 0.f;
 #pragma unroll
-    for (int m = 0; m < F4; ++m) {
-      const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][4 * (sub + 8 * m)]);
-      dot += kk.x * st[m].x + kk.y * st[m].y + kk.z * st[m].z + kk.w * st[m].w;
+    for (int m = 0; m < EPL; m += 4) {
+      const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][i0 + m]);
+      dot += kk.x * st[m] + kk.y * st[m + 1] + kk.z * st[m + 2] + kk.w * st[m + 3];
     }
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    dot += __shfl_xor(dot, 4);
+    dot += __shfl_xor(dot, 32);  // the other half of column j
+    // read k again below instead of keeping d/2 values of it in registers across the exchange
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const float a = s_a[x];
-    const float coef = s_b[x] * (s_v[x][c] - a * dot);  // S <- a S + k (b (v - a k.S))
+    const float coef = s_b[x] * (s_v[x][j] - a * dot);  // S <- a S + k (b (v - a k.S))
 #pragma unroll
-    for (int m = 0; m < F4; ++m) {
-      const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][4 * (sub + 8 * m)]);
-      st[m].x = a * st[m].x + kk.x * coef;
-      st[m].y = a * st[m].y + kk.y * coef;
-      st[m].z = a * st[m].z + kk.z * coef;
-      st[m].w = a * st[m].w + kk.w * coef;
+    for (int m = 0; m < EPL; m += 4) {
+      const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][i0 + m]);
+      st[m] = a * st[m] + kk.x * coef;
+      st[m + 1] = a * st[m + 1] + kk.y * coef;
+      st[m + 2] = a * st[m + 2] + kk.z * coef;
+      st[m + 3] = a * st[m + 3] + kk.w * coef;
     }
   }
   // Non-temporal stores: the committed state is next read by the following step's verify, long
   // after this batch's other traffic, so it is written through instead of lingering dirty in
-  // the caches (measured: the next verify runs 1.3-1.4 us faster, the commit no slower).
+  // the caches.
 #pragma unroll
-  for (int m = 0; m < F4; ++m)
-    __builtin_nontemporal_store(f32x4{st[m].x, st[m].y, st[m].z, st[m].w},
-                                reinterpret_cast<f32x4 *>(col + 4 * (sub + 8 * m)));
+  for (int m = 0; m < EPL; ++m) __builtin_nontemporal_store(st[m], S + (size_t)(i0 + m) * D + j);
 }
 
 }  // namespace gdntree

@@ -36,14 +36,14 @@ bool grid_fits(long long units) { return units > 0 && units * 4 < 0x7fffffffLL; 
 
 GDNTREE_EXPORT gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
                                             const int32_t *root_tok, int B, int P, int K, int N,
-                                            gdntree_tree out, void *stream) {
+                                            gdntree_tree out, hipStream_t stream) {
   if (!lat_logp || !lat_tok || !root_tok || !out.parent || !out.depth || !out.rank ||
       !out.token || !out.score || !out.anc || !out.n_nodes)
     return GDNTREE_ERR_ARG;
   if (B <= 0 || P <= 0 || K <= 0 || N <= 0) return GDNTREE_ERR_ARG;
   if (P > kMaxP || K > kMaxK || N > kMaxN || !grid_fits(B)) return GDNTREE_ERR_UNSUPPORTED;
   if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
-  if (launch_build(lat_logp, lat_tok, root_tok, B, P, K, N, out, (hipStream_t)stream) != hipSuccess)
+  if (launch_build(lat_logp, lat_tok, root_tok, B, P, K, N, out, stream) != hipSuccess)
     return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
@@ -51,7 +51,7 @@ GDNTREE_EXPORT gdntree_status gdntree_build(const float *lat_logp, const int32_t
 GDNTREE_EXPORT gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_tok,
                                                    const int32_t *root_tok, const int32_t *positions,
                                                    int B, int P, int K, int N, int G, gdntree_tree out,
-                                                   void *stream) {
+                                                   hipStream_t stream) {
   if (!lat_logp || !lat_tok || !root_tok || !out.parent || !out.depth || !out.rank ||
       !out.token || !out.score || !out.anc || !out.n_nodes)
     return GDNTREE_ERR_ARG;
@@ -63,7 +63,7 @@ GDNTREE_EXPORT gdntree_status gdntree_build_shared(const float *lat_logp, const 
     return GDNTREE_ERR_UNSUPPORTED;
   if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
   const BuildParams bp{lat_logp, lat_tok, root_tok, P, K, N, out, positions};
-  if (launch_build_shared(bp, B, G, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (launch_build_shared(bp, B, G, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
 
@@ -71,7 +71,7 @@ GDNTREE_EXPORT gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, in
                                              int dv, gdntree_dtype in_dtype, const void *q,
                                              const void *k, const void *v, const void *alpha,
                                              const void *beta, const float *state,
-                                             gdntree_dtype out_dtype, void *o, void *stream) {
+                                             gdntree_dtype out_dtype, void *o, hipStream_t stream) {
   if (!tree.parent || !tree.anc || !tree.n_nodes || !q || !k || !v || !alpha || !beta || !state || !o)
     return GDNTREE_ERR_ARG;
   if (B <= 0 || N <= 0 || L <= 0 || H <= 0) return GDNTREE_ERR_ARG;
@@ -89,7 +89,7 @@ GDNTREE_EXPORT gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, in
   p.B = B; p.R = N + 1; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
   p.out_bf16 = out_dtype == GDNTREE_BF16;
-  if (launch_verify(p, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (launch_verify(p, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
 
@@ -99,7 +99,7 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, in
                                                     const void *k, const void *v, const void *alpha,
                                                     const void *beta, float *state, int32_t *acc_len,
                                                     int32_t *acc_tok, int32_t *acc_node,
-                                                    void *stream) {
+                                                    hipStream_t stream) {
   if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !k || !v || !alpha ||
       !beta || !state || !acc_len || !acc_tok || !acc_node)
     return GDNTREE_ERR_ARG;
@@ -115,13 +115,13 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, in
   p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
-  if (launch_accept_commit(p, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (launch_accept_commit(p, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
 
 GDNTREE_EXPORT gdntree_status gdntree_accept(gdntree_tree tree, int B, int N, int P,
                                              const int32_t *target_argmax, int32_t *acc_len,
-                                             int32_t *acc_tok, int32_t *acc_node, void *stream) {
+                                             int32_t *acc_tok, int32_t *acc_node, hipStream_t stream) {
   if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !acc_len || !acc_tok || !acc_node)
     return GDNTREE_ERR_ARG;
   if (B <= 0 || N <= 0 || P <= 0) return GDNTREE_ERR_ARG;
@@ -131,7 +131,7 @@ GDNTREE_EXPORT gdntree_status gdntree_accept(gdntree_tree tree, int B, int N, in
   p.parent = tree.parent; p.token = tree.token; p.n_nodes = tree.n_nodes; p.target = target_argmax;
   p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
   p.B = B; p.R = N + 1; p.P = P; p.L = 1; p.H = 1; p.D = 128;
-  if (launch_accept(p, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (launch_accept(p, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
 
@@ -139,7 +139,7 @@ GDNTREE_EXPORT gdntree_status gdntree_commit(gdntree_tree tree, int B, int N, in
                                              const int32_t *acc_len, const int32_t *acc_node, int L,
                                              int H, int dk, int dv, gdntree_dtype in_dtype,
                                              const void *k, const void *v, const void *alpha,
-                                             const void *beta, float *state, void *stream) {
+                                             const void *beta, float *state, hipStream_t stream) {
   if (!tree.parent || !tree.n_nodes || !acc_len || !acc_node || !k || !v || !alpha || !beta || !state)
     return GDNTREE_ERR_ARG;
   if (B <= 0 || N <= 0 || P <= 0 || L <= 0 || H <= 0) return GDNTREE_ERR_ARG;
@@ -155,7 +155,7 @@ GDNTREE_EXPORT gdntree_status gdntree_commit(gdntree_tree tree, int B, int N, in
   p.acc_len = const_cast<int32_t *>(acc_len); p.acc_node = const_cast<int32_t *>(acc_node);
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
-  if (launch_commit(p, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (launch_commit(p, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
 
@@ -164,7 +164,7 @@ GDNTREE_EXPORT gdntree_status gdntree_commit_build(
     int H, int dk, int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
     const void *beta, float *state, const float *next_lat_logp, const int32_t *next_lat_tok,
     const int32_t *next_root_tok, int next_B, int next_P, int next_K, int next_N,
-    gdntree_tree next_tree, void *stream) {
+    gdntree_tree next_tree, hipStream_t stream) {
   if (!tree.parent || !tree.n_nodes || !acc_len || !acc_node || !k || !v || !alpha || !beta || !state)
     return GDNTREE_ERR_ARG;
   if (!next_lat_logp || !next_lat_tok || !next_root_tok || !next_tree.parent || !next_tree.depth ||
@@ -188,7 +188,7 @@ GDNTREE_EXPORT gdntree_status gdntree_commit_build(
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
   const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, nullptr};
-  if (launch_commit_build(p, bp, next_B, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (launch_commit_build(p, bp, next_B, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
 
@@ -202,7 +202,7 @@ gdntree_status accept_commit_build_impl(
     const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
     const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
     const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
-    gdntree_tree next_tree, void *stream) {
+    gdntree_tree next_tree, hipStream_t stream) {
   if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !k || !v || !alpha ||
       !beta || !state || !acc_len || !acc_tok || !acc_node)
     return GDNTREE_ERR_ARG;
@@ -234,8 +234,8 @@ gdntree_status accept_commit_build_impl(
   p.B = B; p.R = N + 1; p.P = P; p.L = L; p.H = H; p.D = dk;
   p.in_bf16 = in_dtype == GDNTREE_BF16;
   const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, next_positions};
-  if (launch_accept_commit_build(p, bp, next_B, (hipStream_t)stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
-  if (next_G >= 0 && launch_budget_cut(next_tree, next_B, next_N, next_G, (hipStream_t)stream) != hipSuccess)
+  if (launch_accept_commit_build(p, bp, next_B, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  if (next_G >= 0 && launch_budget_cut(next_tree, next_B, next_N, next_G, stream) != hipSuccess)
     return GDNTREE_ERR_DEVICE;
   return GDNTREE_OK;
 }
@@ -247,7 +247,7 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build(
     int dv, gdntree_dtype in_dtype, const void *k, const void *v, const void *alpha,
     const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
     const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
-    int next_B, int next_P, int next_K, int next_N, gdntree_tree next_tree, void *stream) {
+    int next_B, int next_P, int next_K, int next_N, gdntree_tree next_tree, hipStream_t stream) {
   return accept_commit_build_impl(tree, B, N, P, target_argmax, L, H, dk, dv, in_dtype, k, v, alpha, beta, state,
                                   acc_len, acc_tok, acc_node, next_lat_logp, next_lat_tok, next_root_tok, nullptr,
                                   next_B, next_P, next_K, next_N, -1, next_tree, stream);
@@ -259,14 +259,14 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build_shared(
     const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
     const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
     const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
-    gdntree_tree next_tree, void *stream) {
+    gdntree_tree next_tree, hipStream_t stream) {
   if (next_G < 0) return GDNTREE_ERR_ARG;
   return accept_commit_build_impl(tree, B, N, P, target_argmax, L, H, dk, dv, in_dtype, k, v, alpha, beta, state,
                                   acc_len, acc_tok, acc_node, next_lat_logp, next_lat_tok, next_root_tok,
                                   next_positions, next_B, next_P, next_K, next_N, next_G, next_tree, stream);
 }
 
-GDNTREE_EXPORT const char *gdntree_status_str(int status) {
+GDNTREE_EXPORT const char *gdntree_status_str(gdntree_status status) {
   switch (status) {
     case GDNTREE_OK: return "ok";
     case GDNTREE_ERR_ARG: return "invalid argument (null pointer, non-positive size or unknown dtype)";

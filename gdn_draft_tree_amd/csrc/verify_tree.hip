@@ -8,41 +8,44 @@
 // a WY-form kernel for it (Technical novelty).  This kernel never forms any node state.
 //
 // Tree form of the WY / UT transform.  Let g_t be the product of the gates a over the path
-// root..t.  Unrolling the recurrence along t's path gives S_t = g_t S0 + sum_s (g_t/g_s)
-// k_s u_s^T over the ancestors-or-self s of t, with pseudo-values u that solve a system
-// triangular along root paths.  Scaling the unknowns by the path gates removes every gate
-// from that system: for node t with ancestors-or-self anc e at depths e = 0..d_t, let z
-// solve (deepest first)
-//     z[e] + sum_{e2 > e} z[e2] b_{anc e2} (k_{anc e2} . k_{anc e}) = q_t . k_{anc e}.
-// With Y[t, anc e] = b_{anc e} z[e] and W1[t, anc e] = (g_t / g_{anc e}) Y[t, anc e],
-//     o_t = S0^T E_t + sum_s W1[t, s] v_s,     E_t = g_t (q_t - sum_s Y[t, s] k_s).
-// So the committed state S0, the only large operand (d_k x d_v fp32), enters through ONE
-// dense product S0^T E, and the tree enters through small work that needs q, k, a and b
-// only: Gram entries of ancestor pairs, one path solve per node, and the "effective
-// queries" E.  Y and W1 are bounded by one in magnitude when |q| = |k| = 1 and a, b lie in
-// [0, 1] (W1[t, s] is the coefficient of v_s in o_t, and z does not depend on the gates).
+// root..t.  Unrolling the recurrence along t's path gives S_t = g_t S0 + sum_s (g_t/g_s) b_s
+// k_s w_s^T over the ancestors-or-self s of t, with pseudo-values w that solve a system
+// triangular along root paths.  Collecting the coefficients of each row: for node t with
+// ancestors-or-self anc e at depths e = 0..d_t, let z solve (deepest first)
+//     z[e] + sum_{e2 > e} z[e2] b_{anc e2} (k_{anc e2} . k_{anc e}) = q_t . k_{anc e};
+// with Y[t, e] = b_{anc e} z[e] and W1[t, e] = (g_t / g_{anc e}) Y[t, e],
+//     o_t = g_t (S0^T q_t - sum_e Y[t, e] S0^T k_{anc e}) + sum_e W1[t, e] v_{anc e}.
+// So the committed state S0 (d_k x d_v fp32), the only large operand, enters through the
+// dense products A_q = Q S0 and A_k = K S0 over the rows as they are, which need neither
+// the tree nor the gates; the tree enters through small work on q, k, a, b only (Gram
+// entries of ancestor pairs, one path solve per node), and the two meet in a sparse sum over
+// each node's ancestors.
+//
+// Precision.  The products A_q and A_k are fp32-exact: each fp32 state entry is split into
+// three bf16 parts hi + mid + lo that hold its 24-bit significand exactly (hi = RN(x),
+// mid = RN(x - hi), lo = x - hi - mid, every difference exact in fp32), and every part
+// multiplies the bf16 rows exactly on MFMA with fp32 accumulation.  fp32 rows are split the
+// same way (six of the nine part products; the three dropped ones are below 2^-24 of the
+// term).  The Gram entries are exact products accumulated in fp32 (split likewise for fp32
+// rows), and the path solves, gates and the sparse sums run in fp32.
 //
 // Work decomposition: one workgroup per (layer, request, head) with two kinds of waves.
-//  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they only stream
-//    this head's committed state and v rows into registers, form V^T W1^T once W1 is in
-//    LDS, convert the state to fp16 as it lands, and once E is in LDS add S0^T E^T.
+//  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they gather this
+//    head's state columns from the [d_k][d_v] layout (lane (g, c) holds S0[32 ks + 8 g + e]
+//    [16 w + c], the B operand of a 16x16x32 product), split it as it lands, and form A_k and
+//    A_q for their channels with the row tiles read from LDS; then the sparse sums.
 //  * four tree waves: wave 0 loads the per-node inputs and does the per-node prologue; waves
-//    1..3 stream the q and k rows into LDS (buffer loads to LDS).  Together they compute the
-//    Gram tiles [Q; K] K^T of the lower node triangle, then wave 0 does the per-node path
-//    solves (one lane per node) that give Y and W1, and all four form E on MFMA.  They order
-//    their phases through an LDS counter.
-// A first workgroup barrier orders the loads (below); three more hand over W1, then E, then
-// the finished output rows, which are staged in LDS and stored as whole rows by every wave.
-// A product wave that issues its
-// state loads stalls until the memory pipeline accepts them, so the waves that carry the
-// latency-bound tree work issue only the small row loads, ahead of the state (and run at
-// raised priority).  When the state lands, only one dense product and the stores remain.
+//    1..3 stream the q, k and v rows into LDS (buffer loads to LDS).  Together they compute
+//    the Gram tiles [Q; K] K^T of the lower node triangle, then wave 0 does the per-node path
+//    solves (one lane per node), which give each node's coefficient rows.
+// Rows 0..63 go through 16-row MFMA tiles; a 65th row (a tree of 64 drafts) is done on VALU
+// from the fp32 state fragments, so that a single row never costs a whole tile.
 //
-// Precision: MFMA operands are fp16 with fp32 accumulation.  Rows in bf16 convert to fp16
-// exactly; the state and v columns of a product wave are scaled by one power of two (from
-// their largest magnitude) before the conversion and the outputs are scaled back, so the
-// fp16 range holds for any state scale.  The Gram entries are exact for bf16 rows (fp32
-// inputs enter the Gram as hi + lo bf16 pairs), and the path solve runs in fp32.
+// MFMA operand registers are refilled only after the products that read them have completed:
+// every chain of products is fenced off from the code that refills its operands, and before a
+// product wave splits the next state fragment into the registers the previous products read,
+// it reads each accumulator those products wrote (a VALU read of an MFMA result, which the
+// compiler delays by the required wait states, so the products have finished).
 
 #include <type_traits>
 
@@ -51,8 +54,9 @@
 namespace gdntree {
 namespace {
 
-constexpr int kAR = 20;  // compact row: ancestor depths 0..16, padded to five 16-byte vectors
+constexpr int kAR = 20;  // compact coefficient row: depths 0..16, padded to five 16-byte vectors
 constexpr int kLdsBytes = 160 * 1024;
+constexpr int kTreeWaves = 4;
 
 template <bool BF16IN>
 struct InT;
@@ -61,42 +65,38 @@ struct InT<true> { typedef uint16_t T; };
 template <>
 struct InT<false> { typedef float T; };
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-template <int D, bool BF16IN, int NT>
+// NT 16-row tiles of rows (rows 0 .. 16 NT - 1) plus, with X65, the 65th row.
+template <int D, bool BF16IN, int NT, bool X65>
 struct VerifySmem {
   typedef typename InT<BF16IN>::T T;
-  static constexpr int RM = (16 * NT < kMaxSlots) ? 16 * NT : kMaxSlots;  // node rows held
+  static constexpr int RM = 16 * NT + (X65 ? 1 : 0);                       // rows held
   static constexpr int ROWB = (RM * D * (int)sizeof(T) + 1023) / 1024 * 1024;  // whole 1 KiB loads
-  static constexpr int SP = (16 * NT + 31) / 32 * 32;  // node (contraction) axis of Y K and W1 V
-  // Y / W1 row stride in fp16 elements: 16 rows read at one column start hit distinct banks
-  static constexpr int SPW = SP + 8;
-  // fp16 rows of E: in place of the q rows for bf16 inputs, a region of their own for fp32
-  static constexpr int EB = BF16IN ? 16 : (RM * D * 2 + 15) / 16 * 16;
-  alignas(16) unsigned char qk[2 * ROWB];  // q rows (then E for bf16 inputs), k rows
-  alignas(16) unsigned char e16[EB];
-  alignas(16) _Float16 y[RM * SPW];        // Y rows, the node axis in the MFMA k order
-  alignas(16) _Float16 w1[RM * SPW];       // W1 rows, same layout
-  alignas(16) float lc[RM * kAR];          // b_t k_t . k_s for s a strict ancestor of t, at depth(s)
-  alignas(16) float mc[RM * kAR];          // q_t . k_s for s an ancestor-or-self of t, at depth(s)
+  // Dense coefficient rows for the sums on MFMA: -g_t Y and W1 at [t][s] for s < 16 NT, zero
+  // off t's ancestors-or-self; rows padded by 16 bytes, so that 16 consecutive rows read at one
+  // column hit distinct banks.
+  static constexpr int SPD = 16 * NT + 4;
+  static constexpr int DENSEB = 2 * RM * SPD * 4;
+  static constexpr int QKB = 2 * ROWB > DENSEB ? 2 * ROWB : (DENSEB + 15) / 16 * 16;
+  // q rows then k rows; after the products, the dense coefficient rows; after the sums, the
+  // output rows when they are wider than the v rows
+  alignas(16) unsigned char qk[QKB];
+  alignas(16) unsigned char vr[ROWB];      // v rows
+  alignas(16) float cy[RM * kAR];          // Gram b_t k_t.k_s (strict ancestors s), then -g_t Y[t, e]
+  alignas(16) float cw[RM * kAR];          // Gram q_t.k_s (ancestors-or-self s), then W1[t, e]
   alignas(16) unsigned long long mask[RM];
-  alignas(16) float gamma[16 * NT];        // path gate
+  float gamma[RM];                         // path gate g_t
   float beta[RM];                          // b per node
   float cwl[kMaxAnc][64];                  // W1 weights b_{anc e} g_t / g_{anc e}, per depth and lane
   int bad;
   int sync;                                // tree-wave phase counter
 };
 
-constexpr int kTreeWaves = 4;
-
-template <int D, bool BF16IN, int NT>
+template <int D, bool BF16IN, int NT, bool X65>
 struct VerifyShape {
-  static constexpr int NW = D / 16;        // product waves
-  static constexpr int WAVES = NW + kTreeWaves;
+  static constexpr int NPW = D / 16;       // product waves
+  static constexpr int WAVES = NPW + kTreeWaves;
   static constexpr int NTH = 64 * WAVES;
-  static constexpr int LDS = (int)sizeof(VerifySmem<D, BF16IN, NT>);
+  static constexpr int LDS = (int)sizeof(VerifySmem<D, BF16IN, NT, X65>);
   static constexpr int WG_PER_CU0 = kLdsBytes / LDS < 1 ? 1 : kLdsBytes / LDS;
   static constexpr int WG_PER_CU = WG_PER_CU0 < 2 ? WG_PER_CU0 : 2;
   // A workgroup's waves are dealt over the CU's four SIMDs, so the register budget must let
@@ -114,70 +114,136 @@ __device__ __forceinline__ int swz(int r, int i) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// Workgroup barrier that is also a compiler barrier for memory operations: the s_barrier
+// builtin alone does not order memory accesses at the IR level, so loads of LDS data that
+// other waves write before the barrier could otherwise be moved above it.
+__device__ __forceinline__ void wg_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ bf16x8 frag16(const void *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
 }
-__device__ __forceinline__ f16x8 hfrag(const void *p) {
-  return __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4 *>(p));
+
+// x = hi + mid + lo exactly, each part bf16 (round to nearest even): x - hi and x - hi - mid
+// are exact in fp32 and the last difference fits bf16's significand.  Two elements at a time,
+// one packed conversion per part.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split3(const float *x, bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
+#pragma unroll
+  for (int i = 0; i < 8; i += 2) {
+    const f32x2 v = {x[i], x[i + 1]};
+    const bf16x2 h = __builtin_convertvector(v, bf16x2);
+    const f32x2 r = v - __builtin_convertvector(h, f32x2);
+    const bf16x2 m = __builtin_convertvector(r, bf16x2);
+    const bf16x2 l = __builtin_convertvector(r - __builtin_convertvector(m, f32x2), bf16x2);
+    hi[i] = h[0]; hi[i + 1] = h[1];
+    mid[i] = m[0]; mid[i + 1] = m[1];
+    lo[i] = l[0]; lo[i + 1] = l[1];
+  }
 }
 
-// x = hi + lo with hi, lo bf16 (round to nearest even); x - hi is exact in fp32.
-__device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Four fp32 values split exactly in three bf16 parts (as bf16 bit patterns): the same split as
+// split3, into bf16 vectors reinterpreted whole (no per-element casts of vector elements).
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split4(const f32x4 &x, s16x4 &hi, s16x4 &mid, s16x4 &lo) {
+  bf16x4 h4, m4, l4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const __bf16 h = (__bf16)x[i];
-    hi[i] = h;
-    lo[i] = (__bf16)(x[i] - (float)h);
+  for (int i = 0; i < 4; i += 2) {
+    const f32x2 v = {x[i], x[i + 1]};
+    const bf16x2 h = __builtin_convertvector(v, bf16x2);
+    const f32x2 r = v - __builtin_convertvector(h, f32x2);
+    const bf16x2 m = __builtin_convertvector(r, bf16x2);
+    const bf16x2 l = __builtin_convertvector(r - __builtin_convertvector(m, f32x2), bf16x2);
+    h4[i] = h[0]; h4[i + 1] = h[1];
+    m4[i] = m[0]; m4[i + 1] = m[1];
+    l4[i] = l[0]; l4[i + 1] = l[1];
   }
+  hi = __builtin_bit_cast(s16x4, h4);
+  mid = __builtin_bit_cast(s16x4, m4);
+  lo = __builtin_bit_cast(s16x4, l4);
+}
+
+// 16 x 16 x 16 bf16 product: lane (g, c) holds A[c][4 g + 0..3] and B[4 g + 0..3][c], and gets
+// C[4 g + 0..3][c] -- so the C tile of one product is the B operand of the next.
+__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+
+// Product of an exactly split fp32 operand (three parts) with a bf16 operand (exact).
+__device__ __forceinline__ f32x4 mfma_x3(bf16x8 a, const bf16x8 &bh, const bf16x8 &bm, const bf16x8 &bl, f32x4 c) {
+  c = mfma_bf16(a, bl, c);
+  c = mfma_bf16(a, bm, c);
+  return mfma_bf16(a, bh, c);
 }
-// 16 x 16 x 16: lane l holds A[l % 16][4 (l / 16) + 0..3] and B[4 (l / 16) + 0..3][l % 16].
-__device__ __forceinline__ f32x4 mfma16_f16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+// Product of two exactly split fp32 operands: the six part products down to 2^-16 relative.
+__device__ __forceinline__ f32x4 mfma_x6(const bf16x8 &ah, const bf16x8 &am, const bf16x8 &al, const bf16x8 &bh,
+                                         const bf16x8 &bm, const bf16x8 &bl, f32x4 c) {
+  c = mfma_bf16(ah, bl, c);
+  c = mfma_bf16(am, bm, c);
+  c = mfma_bf16(al, bh, c);
+  c = mfma_bf16(ah, bm, c);
+  c = mfma_bf16(am, bh, c);
+  return mfma_bf16(ah, bh, c);
 }
 
-// Eight consecutive elements of one LDS row (a 16-byte chunk for bf16, two for fp32): the
-// operand fragment of a Gram product that contracts over d.
+// Eight consecutive elements of one LDS row (a 16-byte chunk for bf16, two for fp32), as the
+// operand fragment of a product that contracts over d: the bf16 row itself, or an fp32 row
+// split in three.
 template <int D, bool BF16IN>
 __device__ __forceinline__ void row_frag(const typename InT<BF16IN>::T *rows, int r, int col, bf16x8 &hi,
-                                         bf16x8 &lo) {
+                                         bf16x8 &mid, bf16x8 &lo) {
   if constexpr (BF16IN) {
     hi = frag16(rows + swz<D, 8>(r, col));
   } else {
     const float4 a = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
     const float4 b = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col + 4));
     const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    split8(f, hi, lo);
+    split3(f, hi, mid, lo);
   }
 }
 
 // Four consecutive elements of one LDS row as fp32 (col is a multiple of 4).
 template <int D, bool BF16IN>
-__device__ __forceinline__ f32x4 row4(const typename InT<BF16IN>::T *rows, int r, int col) {
+__device__ __forceinline__ void row4(const typename InT<BF16IN>::T *rows, int r, int col, float *x) {
   if constexpr (BF16IN) {
-    const uint2 x = *reinterpret_cast<const uint2 *>(rows + swz<D, 8>(r, col));
-    return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
-                 __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+    const uint2 w = *reinterpret_cast<const uint2 *>(rows + swz<D, 8>(r, col));
+    x[0] = __uint_as_float(w.x << 16);
+    x[1] = __uint_as_float(w.x & 0xffff0000u);
+    x[2] = __uint_as_float(w.y << 16);
+    x[3] = __uint_as_float(w.y & 0xffff0000u);
   } else {
-    const float4 x = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
-    return f32x4{x.x, x.y, x.z, x.w};
+    const float4 a = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   }
 }
 
-// Position of node s inside its 32-node chunk of a Y / W1 row.  The A operand of Y K and
-// V^T W1^T holds, in lane (g, c), nodes 4 g + 0..3 of the chunk's first 16-node tile and
-// 16 + 4 g + 0..3 of its second (the C layout of two products with the identity), so the k
-// index 8 g + e of the product stands for node 4 g + e (e < 4) or 16 + 4 g + e - 4 (e >= 4);
-// the rows are stored in that k order.
-__device__ __forceinline__ int w1_pos(int s) {
-  const int sl = s & 31;
-  return (s & ~31) + 8 * ((sl & 15) >> 2) + ((sl >> 4) << 2) + (sl & 3);
+// Eight consecutive elements of one LDS row as fp32 (col is a multiple of 8).
+template <int D, bool BF16IN>
+__device__ __forceinline__ void row8(const typename InT<BF16IN>::T *rows, int r, int col, float *x) {
+  if constexpr (BF16IN) {
+    const uint4 w = *reinterpret_cast<const uint4 *>(rows + swz<D, 8>(r, col));
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(ww[i] << 16);
+      x[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
+    const float4 b = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col + 4));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
 }
 
 __device__ __forceinline__ int wave_max_i32(int x) {
@@ -190,11 +256,20 @@ __device__ __forceinline__ int wave_max_i32(int x) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
 __device__ __forceinline__ float bperm_f32(int lane_src, float x) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(lane_src << 2, __float_as_int(x)));
 }
 __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_bits_to_f32(x); }
 __device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Reads accumulator element 0 with a VALU instruction and keeps the value alive, so that the
+// products that wrote it have completed before anything after this point issues.
+__device__ __forceinline__ void drain(const f32x4 &acc) {
+  const int s = __builtin_amdgcn_readfirstlane(__float_as_int(acc[0]));
+  asm volatile("" ::"s"(s));
+}
 
 // The tree waves meet here: each finishes its own memory work (loads into LDS included),
 // counts itself in, and waits for the others.  The wait is bounded; a wave that
@@ -230,17 +305,17 @@ __device__ __forceinline__ void store_rows(const VerifyParams &p, const unsigned
   }
 }
 
-template <int D, bool BF16IN, int NT>
-__global__ __launch_bounds__((VerifyShape<D, BF16IN, NT>::NTH), (VerifyShape<D, BF16IN, NT>::WPEU))
+template <int D, bool BF16IN, int NT, bool X65>
+__global__ __launch_bounds__((VerifyShape<D, BF16IN, NT, X65>::NTH), (VerifyShape<D, BF16IN, NT, X65>::WPEU))
 void verify_kernel(VerifyParams p) {
-  typedef VerifySmem<D, BF16IN, NT> SM;
+  typedef VerifySmem<D, BF16IN, NT, X65> SM;
   typedef typename SM::T T;
-  constexpr int RM = SM::RM, SPW = SM::SPW;
+  constexpr int RM = SM::RM;
   constexpr int CH = 16 / (int)sizeof(T), CPR = D / CH;
   constexpr int KS = D / 32;               // MFMA k-steps over d_k
-  constexpr int KSS = SM::SP / 32;         // MFMA k-steps over the node axis
-  constexpr int NW = D / 16;               // product waves; also the channel tiles of E
+  constexpr int NPW = D / 16;              // product waves
   constexpr int QMAX = SM::ROWB / 1024;    // 1 KiB row chunks per matrix
+  constexpr int NTG = NT + (X65 ? 1 : 0);  // Gram node tiles (the 65th row has one of its own)
   __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
@@ -253,179 +328,227 @@ void verify_kernel(VerifyParams p) {
   const int n = nn_c[b];
   if (n < 1 || n > p.R) return;  // no output for a request with an impossible node count
   const int nl = n - 1;
-  const int ntl = (n + 15) / 16;  // node tiles in use
+  const int ntl = (min(n, 16 * NT) + 15) / 16;  // MFMA row tiles in use
+  const bool row64 = X65 && n == 65;            // the 65th row, on VALU
   const size_t rowbase = (size_t)lb * p.R;
   const size_t rstride = (size_t)p.H * D;  // elements between consecutive slots of one head
-  const int nb = (int)(n * rstride * sizeof(T));  // byte range of this head's used rows
-  // fp16 rows of E (same swizzled layout as bf16 rows)
-  _Float16 *erow = reinterpret_cast<_Float16 *>(BF16IN ? s.qk : s.e16);
-  // Output rows are staged from the k rows on: once E is formed nothing reads the k rows, Y,
-  // W1 or the compact Gram rows again.
-  unsigned char *ostage = s.qk + SM::ROWB;
-  static_assert(offsetof(SM, mask) - SM::ROWB >= (size_t)SM::RM * D * 4, "output staging fits");
+  const int nb = (int)((nl * rstride + D) * sizeof(T));  // byte range of this head's used rows
+  const T *qrow = reinterpret_cast<const T *>(s.qk);
+  const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
+  const T *vrow = reinterpret_cast<const T *>(s.vr);
+  static_assert(SM::QKB >= RM * D * 4, "fp32 output rows fit over the q and k rows");
+  // Output rows are staged over the v rows when they fit there, else over the q and k rows
+  // (where the dense coefficient rows may be): either way after every read of them.
+  const bool stage_in_v = (p.out_bf16 ? 2 : 4) <= (int)sizeof(T);
+  unsigned char *ostage = stage_in_v ? s.vr : s.qk;
 
-  if (wave < NW) {
+  if (wave < NPW) {
     // ================================ product waves ==================================
     // The tree waves issue their row loads before this barrier, so they are queued ahead of
     // the state loads below.
-    __builtin_amdgcn_s_barrier();
-    const T *gv = static_cast<const T *>(p.v) + (rowbase * p.H + h) * (size_t)D;
-    // v fragments, the A operand of a 16 x 16 x 16 product: lane (g, r) holds V[16 mt + r]
-    // [16 wave + 4 g + 0..3].  Rows past the node count lie beyond the buffer's range and
-    // read as zero.
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    typename std::conditional<BF16IN, u32x2, u32x4>::type vld[NT];
-    {
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)gv, 0, nb, 0x00020000);
+    wg_barrier();  // (0)
+    const int j = 16 * wave + l16;  // this lane's value channel
+    // State fragments in the [d_k][d_v] layout: lane (g, c) gathers S0[32 ks + 8 g + e][j],
+    // 16 consecutive channels (64 bytes) per row and instruction.  The fragment of the next
+    // k-step is in flight while the current one is split and multiplied (register budget of
+    // two resident workgroups per CU).
+    constexpr int KW = 1;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(p.state) + (size_t)u * D * D, 0, D * D * 4, 0x00020000);
+    const int voff = (8 * g4 * D + j) * 4;
+    float raw[KS][8];
+    auto gather = [&](int ks) {
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        const int off = ((16 * mt + l16) * (int)rstride + 16 * wave + 4 * g4) * (int)sizeof(T);
-        if constexpr (BF16IN)
-          vld[mt] = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
-        else
-          vld[mt] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+      for (int e = 0; e < 8; ++e)
+        raw[ks][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, (32 * ks + e) * D * 4, 0));
+    };
+#pragma unroll
+    for (int ks = 0; ks < KW; ++ks) gather(ks);
+    wg_barrier();  // (1) the q, k, v rows and the per-node data are in LDS
+
+    // The rest of a product wave's work, as straight-line code for each count of row tiles in
+    // use (a runtime loop bound over the tiles would keep every accumulator live everywhere).
+    auto product_phase = [&](auto ntu_c) {
+      constexpr int NTU = decltype(ntu_c)::value;
+      constexpr bool R65 = X65 && NTU == NT;  // only a full set of tiles can have a 65th row
+      const bool r64 = R65 && row64;
+      f32x4 ak[NTU], aq[NTU];
+#pragma unroll
+      for (int mt = 0; mt < NTU; ++mt) {
+        ak[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aq[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-    }
-    // state fragments of this wave's value channels, the A operand of S0^T E^T: lane (g, c)
-    // holds S0[32 ks + 8 g + 0..7][channel 16 wave + c], contiguous in the [d_v][d_k] layout.
-    f32x4 s0r[KS][2];
-    {
-      const float *sr = p.state + ((size_t)u * D + 16 * wave + l16) * D + 8 * g4;
+      // The 65th row's products: one more tile whose row 0 is k_64 and row 1 is q_64 (the other
+      // rows repeat q_64 and are never used), so lane (0, c) ends with A_k[64][j] in element 0
+      // and A_q[64][j] in element 1.
+      f32x4 a65 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s0r[ks][0] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks);
-        s0r[ks][1] = *reinterpret_cast<const f32x4 *>(sr + 32 * ks + 4);
+        // The split of this k-step starts only after the previous k-step's drains (volatile asm
+        // keeps its order), and the next gather only after the split, so at most two raw
+        // fragments and one split are live.
+        asm volatile("" : "+v"(raw[ks][0]), "+v"(raw[ks][1]), "+v"(raw[ks][2]), "+v"(raw[ks][3]),
+                     "+v"(raw[ks][4]), "+v"(raw[ks][5]), "+v"(raw[ks][6]), "+v"(raw[ks][7]));
+        bf16x8 sh, sm, sl;
+        split3(raw[ks], sh, sm, sl);
+        asm volatile("" : "+v"(sh), "+v"(sm), "+v"(sl)::"memory");
+        if (ks + KW < KS) gather(ks + KW);
+        __builtin_amdgcn_sched_barrier(0);
+        // rows 16 mt + 0..15 of K and of Q times this k-step's state slice
+#pragma unroll
+        for (int mt = 0; mt < NTU; ++mt) {
+          bf16x8 xh, xm, xl;
+          row_frag<D, BF16IN>(krow, 16 * mt + l16, 32 * ks + 8 * g4, xh, xm, xl);
+          if constexpr (BF16IN) ak[mt] = mfma_x3(xh, sh, sm, sl, ak[mt]);
+          else ak[mt] = mfma_x6(xh, xm, xl, sh, sm, sl, ak[mt]);
+          if constexpr (!BF16IN) drain(ak[mt]);  // fp32 row fragments are split on VALU
+          row_frag<D, BF16IN>(qrow, 16 * mt + l16, 32 * ks + 8 * g4, xh, xm, xl);
+          if constexpr (BF16IN) aq[mt] = mfma_x3(xh, sh, sm, sl, aq[mt]);
+          else aq[mt] = mfma_x6(xh, xm, xl, sh, sm, sl, aq[mt]);
+          if constexpr (!BF16IN) drain(aq[mt]);
+        }
+        if constexpr (R65) {
+          bf16x8 xh, xm, xl;
+          row_frag<D, BF16IN>(l16 == 0 ? krow : qrow, 64, 32 * ks + 8 * g4, xh, xm, xl);
+          if constexpr (BF16IN) a65 = mfma_x3(xh, sh, sm, sl, a65);
+          else a65 = mfma_x6(xh, xm, xl, sh, sm, sl, a65);
+          drain(a65);
+        }
+        // the products of this k-step have completed before the next split overwrites sh, sm, sl
+#pragma unroll
+        for (int mt = 0; mt < NTU; ++mt) {
+          drain(ak[mt]);
+          drain(aq[mt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    __builtin_amdgcn_s_barrier();  // (1) W1 is in LDS
+      wg_barrier();  // (2) nobody reads q or k rows any more; coefficients are ready
+      const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
-    // ---- V^T W1^T for this wave's channels, before the state has landed ------------------
-    // v is scaled by a power of two 2^-ev chosen from its largest magnitude (the scaled
-    // values lie in [2^14, 2^15) at most), so the fp16 range holds for any v scale.
-    float mv = 0.f;
+      // ---- o[t] = g_t A_q[t] + sum_s Cy[t][s] A_k[s] + Cw[t][s] v[s] on MFMA -------------
+      // with the dense coefficient rows (Cy = -g_t Y, Cw = W1, zero off t's ancestors-or-self)
+      // over s < 16 NT, then the 65th row on VALU.  16x16x16 products: the A operand of lane
+      // (g, c) is Cy[16 mt + c][16 ms + 4 g + 0..3]; the B operand is A_k[16 ms + 4 g + 0..3][j],
+      // which is this lane's own K-pass accumulator of tile ms (C layout), split in three, or
+      // v[16 ms + 4 g + 0..3][j].  Every fp32 operand is split exactly; the v rows are bf16 (or
+      // fp32 split in three).
+      constexpr int SPD = SM::SPD;
+      const float *dcy = reinterpret_cast<const float *>(s.qk);
+      const float *dcw = dcy + RM * SPD;
+      auto dpos = [](int t, int s4) { return t * SPD + s4; };
+      f32x4 oc[NTU];
 #pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      if constexpr (BF16IN) {
+      for (int mt = 0; mt < NTU; ++mt)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          mv = fmaxf(mv, fabsf(__uint_as_float(vld[mt][i] << 16)));
-          mv = fmaxf(mv, fabsf(__uint_as_float(vld[mt][i] & 0xffff0000u)));
-        }
-      } else {
+        for (int r = 0; r < 4; ++r) oc[mt][r] = s.gamma[16 * mt + 4 * g4 + r] * aq[mt][r];  // rows >= n unused
+      const float v64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) : 0.f;
+      float p64 = 0.f;  // this lane's share of row 64's sum over s < 64
+      wg_barrier();     // (3) the dense coefficient rows are in LDS
+      // A_k tile ms outermost: only its split operands are live while the row tiles mt >= ms
+      // (the coefficient rows vanish above the diagonal) take their products.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mv = fmaxf(mv, fabsf(__uint_as_float(vld[mt][i])));
-      }
-    }
-    // non-negative floats order like their bit patterns; ex = clamped biased exponent
-    const int exv = min(max((wave_max_i32(__float_as_int(mv)) >> 23) & 0xff, 15), 254);
-    // V^T in the C layout (lane (g, c): rows 4 g + 0..3 of channel c) through a product with
-    // the identity, packed as the A operand of V^T W1^T.
-    f32x4 acc[NT];
-    {
-      f16x8 vph[KSS];
-      f16x4 ident;
+      for (int ms = 0; ms < NTU; ++ms) {
+        s16x4 kh, km, kl, vh, vm, vl;
+        f32x4 vv;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ident[e] = (_Float16)((4 * g4 + e == l16) ? 1.f : 0.f);
+        // rows >= n hold copies of row n - 1 (finite) and meet zero coefficients
+        for (int r = 0; r < 4; ++r) vv[r] = to_f32(vrow[swz<D, CH>(16 * ms + 4 * g4 + r, j)]);
+        split4(ak[ms], kh, km, kl);
+        if constexpr (BF16IN) {
 #pragma unroll
-      for (int mt = 0; mt < 2 * KSS; ++mt) {
-        f32x4 vp = {0.f, 0.f, 0.f, 0.f};
-        if (mt < NT && mt < ntl) {
-          const int mc_ = mt < NT ? mt : NT - 1;  // (static index; mt < NT here)
-          f16x4 a;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float x;
-            if constexpr (BF16IN)
-              x = (i & 1) ? __uint_as_float(vld[mc_][i >> 1] & 0xffff0000u) : __uint_as_float(vld[mc_][i >> 1] << 16);
-            else
-              x = __uint_as_float(vld[mc_][i]);
-            a[i] = (_Float16)__builtin_amdgcn_ldexpf(x, 141 - exv);
-          }
-          vp = mfma16_f16(a, ident, vp);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vph[mt >> 1][4 * (mt & 1) + i] = (_Float16)vp[i];
-      }
-      // W1 is zero above the diagonal, so node chunks past the tile are skipped
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt) {
-        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (mt >= ntl) continue;
-        const int t = 16 * mt + l16;
-#pragma unroll
-        for (int kk = 0; kk < KSS; ++kk) {
-          if (32 * kk > 16 * mt + 15) break;
-          acc[mt] = mfma_f16(vph[kk], hfrag(s.w1 + t * SPW + 32 * kk + 8 * g4), acc[mt]);
-        }
-      }
-    }
-    // The state, as soon as it has landed (before E is ready), is scaled by 2^(141 - ex) with
-    // ex >= the v exponent, so both scaled operands stay inside the fp16 range; the V^T W1^T
-    // part is rescaled to match (exact; nothing to do in the usual case ex == exv).
-    float ms = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ms = fmaxf(ms, fabsf(s0r[ks][j][i]));
-    const int exs = min(max((wave_max_i32(__float_as_int(ms)) >> 23) & 0xff, 15), 254);
-    const int ex = max(exs, exv);
-    f16x8 s0h[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s0h[ks][e] = (_Float16)__builtin_amdgcn_ldexpf(s0r[ks][e >> 2][e & 3], 141 - ex);
-    if (ex != exv) {
-#pragma unroll
-      for (int mt = 0; mt < NT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_amdgcn_ldexpf(acc[mt][i], exv - ex);
-    }
-    __builtin_amdgcn_s_barrier();  // (2) E is in LDS
-    const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
-
-    // ---- + S0^T E^T ------------------------------------------------------------------------
-    // Lane (g, t) ends with o[t][16 wave + 4 g + 0..3], written into the output rows staged in
-    // LDS (rows past the node count are not written).  An inconsistent tree gives NaN outputs.
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      if (mt >= ntl) break;
-      const int t = 16 * mt + l16;
-      f32x4 o4 = acc[mt];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) o4 = mfma_f16(s0h[ks], hfrag(erow + swz<D, 8>(t, 32 * ks + 8 * g4)), o4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = __builtin_amdgcn_ldexpf(o4[i], ex - 141);
-      if (bad) o4 = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      if (t < n) {
-        if (p.out_bf16) {
-          const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[0]) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[1]) << 16);
-          const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[2]) |
-                              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)o4[3]) << 16);
-          *reinterpret_cast<u32x2 *>(ostage + 2 * swz<D, 8>(t, 16 * wave + 4 * g4)) = u32x2{lo, hi};
+          for (int r = 0; r < 4; ++r) vh[r] = (short)(__float_as_uint(vv[r]) >> 16);  // exact
         } else {
-          *reinterpret_cast<f32x4 *>(ostage + 4 * swz<D, 4>(t, 16 * wave + 4 * g4)) = o4;
+          split4(vv, vh, vm, vl);
+        }
+        if (R65 && r64) {
+          const f32x4 cyv = *reinterpret_cast<const f32x4 *>(dcy + dpos(64, 16 * ms + 4 * g4));
+          const f32x4 cwv = *reinterpret_cast<const f32x4 *>(dcw + dpos(64, 16 * ms + 4 * g4));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p64 = fmaf(cyv[r], ak[ms][r], fmaf(cwv[r], vv[r], p64));
+        }
+#pragma unroll
+        for (int mt = ms; mt < NTU; ++mt) {
+          const f32x4 cyv = *reinterpret_cast<const f32x4 *>(dcy + dpos(16 * mt + l16, 16 * ms + 4 * g4));
+          const f32x4 cwv = *reinterpret_cast<const f32x4 *>(dcw + dpos(16 * mt + l16, 16 * ms + 4 * g4));
+          s16x4 ah, am, al, wh, wm, wl;
+          split4(cyv, ah, am, al);
+          split4(cwv, wh, wm, wl);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 c = oc[mt];
+          c = mfma16(al, kh, c);
+          c = mfma16(am, km, c);
+          c = mfma16(ah, kl, c);
+          c = mfma16(am, kh, c);
+          c = mfma16(ah, km, c);
+          c = mfma16(ah, kh, c);
+          if constexpr (BF16IN) {
+            c = mfma16(wl, vh, c);
+            c = mfma16(wm, vh, c);
+            c = mfma16(wh, vh, c);
+          } else {
+            c = mfma16(wl, vh, c);
+            c = mfma16(wm, vm, c);
+            c = mfma16(wh, vl, c);
+            c = mfma16(wm, vh, c);
+            c = mfma16(wh, vm, c);
+            c = mfma16(wh, vh, c);
+          }
+          oc[mt] = c;
+          drain(oc[mt]);  // these products have completed before the next split overwrites a*, w*, k*, v*
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's output rows are staged
-    __builtin_amdgcn_s_barrier();        // (3) every output row is staged
-    store_rows<D>(p, ostage, n, rowbase, h, 64 * wave + lane, 64 * (NW + kTreeWaves));
+      float o64 = 0.f;
+      if (R65 && r64) {  // the four lanes of a channel folded, then row 64's own term
+        p64 += __shfl_xor(p64, 16);
+        p64 += __shfl_xor(p64, 32);
+        const int d64 = imin((int)__popcll(s.mask[64]), kMaxP);
+        // a65 holds A_k[64][j], A_q[64][j] in the lanes of row group 0, which stage row 64
+        o64 = s.gamma[64] * a65[1] + p64 + s.cy[64 * kAR + d64] * a65[0] + s.cw[64 * kAR + d64] * v64;
+      }
+      if (bad) {
+#pragma unroll
+        for (int mt = 0; mt < NTU; ++mt) oc[mt] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+                                                       __builtin_nanf("")};
+        o64 = __builtin_nanf("");
+      }
+      wg_barrier();  // (4) nobody reads the v rows or the dense rows any more
+
+      // ---- output rows, staged over the v rows (or the q and k rows for wider outputs) -----
+      auto stage = [&](int t, float x) {
+        if (p.out_bf16)
+          reinterpret_cast<uint16_t *>(ostage)[swz<D, 8>(t, j)] = __builtin_bit_cast(uint16_t, (__bf16)x);
+        else
+          reinterpret_cast<float *>(ostage)[swz<D, 4>(t, j)] = x;
+      };
+#pragma unroll
+      for (int mt = 0; mt < NTU; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * mt + 4 * g4 + r;
+          if (t < n) stage(t, oc[mt][r]);
+        }
+      }
+      if (R65 && r64 && g4 == 0) stage(64, o64);
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's output rows are staged
+      wg_barrier();        // (5) every output row is staged
+    };
+    static_assert(NT >= 1 && NT <= 4, "one to four row tiles");
+    if (ntl == NT) product_phase(std::integral_constant<int, NT>{});
+    else if (ntl == 1) product_phase(std::integral_constant<int, 1>{});
+    else if (ntl == 2) product_phase(std::integral_constant<int, (NT > 2 ? 2 : 1)>{});
+    else product_phase(std::integral_constant<int, (NT > 3 ? 3 : 1)>{});
+    store_rows<D>(p, ostage, n, rowbase, h, tid, 64 * (NPW + kTreeWaves));
     return;
   }
 
   // ================================== tree waves =====================================
   __builtin_amdgcn_s_setprio(3);
-  const int tw = wave - NW;  // 0: per-node tree work and the path solves; 1..3: clears
-  const T *qrow = reinterpret_cast<const T *>(s.qk);
-  const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
+  const int tw = wave - NPW;  // 0: per-node tree work and the path solves; 1..3: clears and rows
   const size_t tb = (size_t)b * p.R;
-  // tw 0 issues only the small per-node loads: an LDS write of a wave waits for that wave's
-  // own loads into LDS, and its prologue writes LDS early.  tw 1..3 clear Y, W1 (zero off the
-  // ancestor pattern) and the compact Gram rows first, for the same reason, then load the q
-  // and k rows.
+  // tw 0 issues only the small per-node loads (its prologue writes LDS early, and an LDS
+  // write of a wave waits for that wave's own loads into LDS).  tw 1..3 clear the compact
+  // Gram rows first, for the same reason, then load the q, k and v rows.
   const int t_me = lane + 1;
   const int tn = min(t_me, nl);
   const int ts = min(lane, nl);
@@ -453,43 +576,41 @@ void verify_kernel(VerifyParams p) {
       w_b1 = reinterpret_cast<const uint32_t *>(gb)[(rowbase + tn) * p.H + h];
     }
   } else {
-    constexpr int NY = 2 * RM * SPW * 2 / 16, NL = 2 * RM * kAR * 4 / 16;
-    static_assert(offsetof(SM, w1) == offsetof(SM, y) + RM * SPW * 2, "Y and W1 adjacent");
-    static_assert(offsetof(SM, mc) == offsetof(SM, lc) + RM * kAR * 4, "lc and mc adjacent");
+    constexpr int NL = 2 * RM * kAR * 4 / 16;
+    static_assert(offsetof(SM, cw) == offsetof(SM, cy) + RM * kAR * 4, "cy and cw adjacent");
     constexpr int NC = kTreeWaves - 1;
-#pragma unroll
-    for (int x = 0; x < (NY + 64 * NC - 1) / (64 * NC); ++x) {
-      const int i = (tw - 1) * 64 + lane + 64 * NC * x;
-      if (i < NY) reinterpret_cast<uint4 *>(s.y)[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
 #pragma unroll
     for (int x = 0; x < (NL + 64 * NC - 1) / (64 * NC); ++x) {
       const int i = (tw - 1) * 64 + lane + 64 * NC * x;
-      if (i < NL) reinterpret_cast<uint4 *>(s.lc)[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < NL) reinterpret_cast<uint4 *>(s.cy)[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    // q and k rows straight into LDS, 1 KiB chunks dealt over tw 1..3: each wave instruction
-    // fills 64 consecutive 16-byte chunks; lane l of chunk qi holds physical chunk 64 qi + l
-    // and fetches the logical chunk that the swizzle places there.  Rows past the node count
-    // fetch row n-1 (never used).
+    // q, k and v rows straight into LDS, 1 KiB chunks dealt over tw 1..3: each wave
+    // instruction fills 64 consecutive 16-byte chunks; lane l of chunk qi holds physical chunk
+    // 64 qi + l and fetches the logical chunk that the swizzle places there.  Rows past the
+    // node count fetch row n-1 (never used).
+    const size_t hoff = (rowbase * p.H + h) * (size_t)D;
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const T *>(p.q) + (rowbase * p.H + h) * (size_t)D), 0, nb, 0x00020000);
+        (void *)(static_cast<const T *>(p.q) + hoff), 0, nb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const T *>(p.k) + (rowbase * p.H + h) * (size_t)D), 0, nb, 0x00020000);
+        (void *)(static_cast<const T *>(p.k) + hoff), 0, nb, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(static_cast<const T *>(p.v) + hoff), 0, nb, 0x00020000);
 #pragma unroll
-    for (int x = 0; x < (2 * QMAX + NC - 1) / NC; ++x) {
+    for (int x = 0; x < (3 * QMAX + NC - 1) / NC; ++x) {
       const int c = (tw - 1) + NC * x;
-      if (c < 2 * QMAX) {
-        const int qi = c < QMAX ? c : c - QMAX;
+      if (c < 3 * QMAX) {
+        const int mat = c / QMAX, qi = c % QMAX;
         const int pc = 64 * qi + lane, r = pc / CPR, cc = (pc % CPR) ^ (r & (CPR - 1));
         const unsigned off = (unsigned)((min(r, nl) * (int)rstride + cc * CH) * (int)sizeof(T));
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c < QMAX ? rq : rk,
-                                                 (lds_void_t *)(s.qk + (c < QMAX ? 0 : SM::ROWB) + 1024 * qi), 16,
-                                                 off, 0, 0, 0);
+        unsigned char *dst = (mat == 2 ? s.vr : s.qk + mat * SM::ROWB) + 1024 * qi;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(mat == 0 ? rq : (mat == 1 ? rk : rv), (lds_void_t *)dst, 16, off,
+                                                 0, 0, 0);
       }
     }
   }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the counter and the clears are written
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();  // the counter is clear; the product waves may queue their loads
+  wg_barrier();  // (0) the product waves may queue their state loads
   // keep every use of tw 0's loaded values (and the wait for them) after the barrier
   asm volatile("" : "+v"(w_mask), "+v"(my_mask), "+v"(w_par), "+v"(w_a0), "+v"(w_b0), "+v"(w_a1), "+v"(w_b1));
 
@@ -499,7 +620,7 @@ void verify_kernel(VerifyParams p) {
     const auto gate = [](uint32_t x) { return BF16IN ? __uint_as_float(x << 16) : __uint_as_float(x); };
     const float a0 = gate(w_a0), b0 = gate(w_b0), a1 = gate(w_a1), b1 = gate(w_b1);
     if (lane < n) s.mask[lane] = my_mask;
-    if constexpr (RM == kMaxSlots) {
+    if constexpr (X65) {
       if (lane == 63 && n == kMaxSlots) s.mask[64] = w_mask;  // slot 64 has no lane of its own
     }
     if (lane == 0 && my_mask != 0ull) s.bad = 1;  // the root has no ancestors
@@ -521,7 +642,7 @@ void verify_kernel(VerifyParams p) {
     unsigned long long mm = m;
 #pragma unroll
     for (int e = 1; e <= kMaxP; ++e) {
-      const int a = min(__ffsll((long long)mm), nl);  // 0 (the root) beyond the depth
+      const int a = imin((int)__ffsll((long long)mm), nl);  // 0 (the root) beyond the depth
       mm &= mm - 1;
       ancw[e >> 2] |= (uint32_t)a << (8 * (e & 3));
       // gates of slot a: held by lane a, except t itself (slot 64 has no lane)
@@ -534,7 +655,7 @@ void verify_kernel(VerifyParams p) {
       bet[e] = bv;
       g *= (e <= d_me) ? av : 1.f;
     }
-    // W1[t, anc e] = cw[e] z[e] with cw[e] = b_{anc e} g_t / g_{anc e}
+    // W1[t, anc e] = cwl[e] z[e] with cwl[e] = b_{anc e} g_t / g_{anc e}
     float rr = 1.f;
 #pragma unroll
     for (int e = kMaxP; e >= 0; --e) {
@@ -550,7 +671,8 @@ void verify_kernel(VerifyParams p) {
       s.beta[0] = bet[0];
     }
   }
-  tree_sync(&s.sync, &s.bad, kTreeWaves, lane);  // rows, masks, gates and cleared regions are in LDS
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): rows landed, prologue written
+  wg_barrier();   // (1) rows, masks, gates and cleared regions are in LDS
 
   // ---- Gram tiles [Q; K] K^T of the lower node triangle, dealt between the tree waves ----
   // Transposed: lane (g, t) owns node t = 16 mt + l16 and gets k_s . k_t and k_s . q_t for
@@ -558,27 +680,29 @@ void verify_kernel(VerifyParams p) {
   // ancestors-or-self in slots 0..s) - 1 (the k.k ones times b_t, the factor the path solve
   // applies); the rest go to padding entries 17..19.  Rows past the node count read finite
   // or arbitrary LDS contents; the entries they produce are never kept.
+  const int ntg = (n + 15) / 16;
 #pragma unroll
-  for (int mt = 0; mt < NT; ++mt) {
+  for (int mt = 0; mt < NTG; ++mt) {
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
-      if ((mt * (mt + 1) / 2 + nt) % kTreeWaves != kTreeWaves - 1 - tw || mt >= ntl) continue;
+      if ((mt * (mt + 1) / 2 + nt) % kTreeWaves != kTreeWaves - 1 - tw || mt >= ntg) continue;
       const int tme = 16 * mt + l16, ra = min(tme, nl);
       const int rb = 16 * nt + l16;
       f32x4 gk4 = {0.f, 0.f, 0.f, 0.f}, gq4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 aqh, aql, akh, akl, bh, bl;
-        row_frag<D, BF16IN>(qrow, tme, 32 * ks + 8 * g4, aqh, aql);
-        row_frag<D, BF16IN>(krow, tme, 32 * ks + 8 * g4, akh, akl);
-        row_frag<D, BF16IN>(krow, rb, 32 * ks + 8 * g4, bh, bl);
-        gk4 = mfma_bf16(bh, akh, gk4);
-        gq4 = mfma_bf16(bh, aqh, gq4);
-        if constexpr (!BF16IN) {
-          gk4 = mfma_bf16(bl, akh, gk4);
-          gk4 = mfma_bf16(bh, akl, gk4);
-          gq4 = mfma_bf16(bl, aqh, gq4);
-          gq4 = mfma_bf16(bh, aql, gq4);
+        bf16x8 aqh, aqm, aql, akh, akm, akl, bh, bm, bl;
+        row_frag<D, BF16IN>(qrow, tme, 32 * ks + 8 * g4, aqh, aqm, aql);
+        row_frag<D, BF16IN>(krow, tme, 32 * ks + 8 * g4, akh, akm, akl);
+        row_frag<D, BF16IN>(krow, rb, 32 * ks + 8 * g4, bh, bm, bl);
+        if constexpr (BF16IN) {
+          gk4 = mfma_bf16(bh, akh, gk4);
+          gq4 = mfma_bf16(bh, aqh, gq4);
+        } else {
+          gk4 = mfma_x6(bh, bm, bl, akh, akm, akl, gk4);
+          gq4 = mfma_x6(bh, bm, bl, aqh, aqm, aql, gq4);
+          drain(gk4);  // the next fragments are split on VALU into the same registers
+          drain(gq4);
         }
       }
       const unsigned long long tmask = s.mask[ra];
@@ -602,23 +726,28 @@ void verify_kernel(VerifyParams p) {
         const int es = cbelow + __popc(bits & ((2u << r) - 1u)) - 1;
         const bool keep = rowok && ((bits >> r) & 1u) && sn <= tme && es <= kMaxP;
         const int dummy = trow + kMaxAnc + (r % 3);
-        s.mc[keep ? trow + es : dummy] = gq4[r];
-        s.lc[keep && sn != tme ? trow + es : dummy] = gk4[r] * bt;
+        s.cw[keep ? trow + es : dummy] = gq4[r];
+        s.cy[keep && sn != tme ? trow + es : dummy] = gk4[r] * bt;
       }
+      // the next tile's fragments are loaded only after these products' results are stored
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-  tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the compact Gram rows are complete
+  tree_sync(&s.sync, &s.bad, kTreeWaves, lane);  // the compact Gram rows are complete
 
-  // ---- tw 0: path solve, one lane per node, then the node's Y and W1 rows (fp16) --------
+  // ---- tw 0: path solve, one lane per node, then the node's coefficient rows -------------
+  // Writes -g_t Y[t, e] over the k.k entries and W1[t, e] over the q.k entries: every read of
+  // them (this wave's, in program order) comes first.
   if (tw == 0) {
     const bool tv = t_me < n;
     const int t = tn;
     const int dmax = wave_max_i32(tv ? d_me : 0);
+    const float z_root = s.cw[0];  // q_0 . k_0
     auto anc_at = [&](int e) -> int { return (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu); };
     float z[kAR];  // right-hand side q_t . k_{anc e}; zero beyond the depth
 #pragma unroll
     for (int v = 0; v < kAR / 4; ++v) {
-      const float4 x = reinterpret_cast<const float4 *>(&s.mc[t * kAR])[v];
+      const float4 x = reinterpret_cast<const float4 *>(&s.cw[t * kAR])[v];
       z[4 * v] = x.x;
       z[4 * v + 1] = x.y;
       z[4 * v + 2] = x.z;
@@ -634,7 +763,7 @@ void verify_kernel(VerifyParams p) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int e2 = 2 * grp + 2 - r;
-        const float4 *row = reinterpret_cast<const float4 *>(&s.lc[anc_at(e2) * kAR]);
+        const float4 *row = reinterpret_cast<const float4 *>(&s.cy[anc_at(e2) * kAR]);
 #pragma unroll
         for (int v = 0; v < (e2 + 3) / 4; ++v) rw[r][v] = row[v];
       }
@@ -652,115 +781,71 @@ void verify_kernel(VerifyParams p) {
       }
     }
     if (tv) {
+      const float gt = s.gamma[t];
 #pragma unroll
       for (int e = 0; e <= kMaxP; ++e) {
         if (e <= d_me) {
-          const int a = anc_at(e);
-          const int pos = t * SPW + w1_pos(a);
-          s.w1[pos] = (_Float16)(s.cwl[e][lane] * z[e]);
-          s.y[pos] = (_Float16)(s.beta[a] * z[e]);
+          const float yv = s.beta[anc_at(e)] * z[e];  // Y[t, e]
+          s.cy[t * kAR + e] = -gt * yv;
+          s.cw[t * kAR + e] = s.cwl[e][lane] * z[e];
         }
       }
     }
-  } else if (tw == 1 && lane == 0) {
-    // the root: Y[0, 0] = W1[0, 0] = b_0 (q_0 . k_0)
-    const _Float16 w = (_Float16)(s.beta[0] * s.mc[0]);
-    s.w1[0] = w;
-    s.y[0] = w;
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): Y and W1 are written
-  __builtin_amdgcn_s_barrier();        // (1) the product waves may form V^T W1^T
-
-  // ---- E = g (Q - Y K) on MFMA, channel tiles dealt over the tree waves, written as fp16
-  //      over the q rows --------------------------------------------------------------------
-  // Per channel tile ct: K^T in the C layout (lane (g, c): nodes 4 g + 0..3 of each 16-node
-  // tile at channel 16 ct + c) through products with the negated identity (exact), packed as
-  // the A operand; then E^T tile by node tile with Q^T as the initial C tile and Y^T as the
-  // B operand (Y is zero above the diagonal).  Lane (g, t) ends with E[t][16 ct + 4 g + 0..3].
-  static_assert(NW % kTreeWaves == 0, "channel tiles dealt evenly");
-  // Straight-line code over all node tiles (rows past the node count are clamped, their K
-  // entries zeroed and their E rows never used), so the LDS reads of a channel tile can all
-  // be issued ahead of its products.
-#pragma unroll
-  for (int cc = 0; cc < NW / kTreeWaves; ++cc) {
-    const int ct = tw + kTreeWaves * cc;
-    f16x8 kt[KSS];
-#pragma unroll
-    for (int mt = 0; mt < 2 * KSS; ++mt) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (true) {
-        if (mt < NT) {
-          const int r = min(16 * mt + l16, nl);
-          if constexpr (BF16IN) {
-            s16x4 nid;  // bf16 -1 on the diagonal
-#pragma unroll
-            for (int e = 0; e < 4; ++e) nid[e] = (short)((4 * g4 + e == l16) ? 0xbf80 : 0);
-            const s16x4 a = *reinterpret_cast<const s16x4 *>(krow + swz<D, 8>(r, 16 * ct + 4 * g4));
-            c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, nid, c, 0, 0, 0);
-          } else {
-            f16x4 nid, a;
-            const f32x4 kv = row4<D, false>(krow, r, 16 * ct + 4 * g4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              nid[e] = (_Float16)((4 * g4 + e == l16) ? -1.f : 0.f);
-              a[e] = (_Float16)kv[e];
-            }
-            c = mfma16_f16(a, nid, c);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) c[i] = (16 * mt + 4 * g4 + i < n) ? c[i] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kt[mt >> 1][4 * (mt & 1) + i] = (_Float16)c[i];
+    if (lane == 0) {  // the root: Y[0, 0] = W1[0, 0] = b_0 (q_0 . k_0)
+      const float y0 = s.beta[0] * z_root;
+      s.cy[0] = -s.gamma[0] * y0;
+      s.cw[0] = y0;
     }
-    // Scheduling fences: this channel tile's K^T fragments are packed before its products,
-    // and the next tile's only after this tile's E rows (which read the last products'
-    // results).  An interleaved schedule, in which VALU packing of the next tile's fragments
-    // rewrote the B operand registers of an MFMA still waiting on the previous MFMA's
-    // accumulator, gave wrong E entries in workgroups sharing a CU.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int mt = 0; mt < NT; ++mt) {
-      const int t = 16 * mt + l16;
-      const int tq = min(t, nl);
-      f32x4 acc = row4<D, BF16IN>(qrow, tq, 16 * ct + 4 * g4);
-#pragma unroll
-      for (int kk = 0; kk < KSS; ++kk) {
-        if (32 * kk > 16 * mt + 15) break;
-        acc = mfma_f16(kt[kk], hfrag(s.y + tq * SPW + 32 * kk + 8 * g4), acc);
-      }
-      const float gt = s.gamma[t];
-      f16x4 ev;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ev[i] = (_Float16)(gt * acc[i]);
-      // rows n..RM-1 are unused scratch; rows past RM do not exist
-      if (mt < NT - 1 || t < RM) *reinterpret_cast<f16x4 *>(erow + swz<D, 8>(t, 16 * ct + 4 * g4)) = ev;
-    }
-    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): E is written
-  __builtin_amdgcn_s_barrier();        // (2) the product waves may read E
-  __builtin_amdgcn_s_barrier();        // (3) every output row is staged
-  store_rows<D>(p, ostage, n, rowbase, h, 64 * wave + lane, 64 * (NW + kTreeWaves));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the coefficient rows are written
+  wg_barrier();        // (2) nobody reads the q and k rows any more
+  {
+    // dense coefficient rows: [t][s] = the compact entry at s's depth when s is an
+    // ancestor-or-self of t (the root, or bit s - 1 of t's mask), else zero; four columns a lane
+    constexpr int SPD = SM::SPD, NCH = SPD / 4 - 1;  // four columns a lane; the padding stays unwritten
+    float *dcy = reinterpret_cast<float *>(s.qk);
+    float *dcw = dcy + RM * SPD;
+    for (int c = 64 * tw + lane; c < RM * NCH; c += 64 * kTreeWaves) {
+      const int t = c / NCH, q = c % NCH;
+      const bool tv = t < n;
+      const unsigned long long m = tv ? s.mask[t] : 0ull;
+      f32x4 yv, wv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sc = 4 * q + i;
+        const bool anc = tv && (sc == 0 || (sc <= t && ((m >> (sc - 1)) & 1ull)));
+        const int e = sc == 0 ? 0 : imin(1 + (int)__popcll(m & ((1ull << (sc - 1)) - 1ull)), kMaxP);
+        yv[i] = anc ? s.cy[t * kAR + e] : 0.f;
+        wv[i] = anc ? s.cw[t * kAR + e] : 0.f;
+      }
+      const int pos = t * SPD + 4 * q;
+      *reinterpret_cast<f32x4 *>(dcy + pos) = yv;
+      *reinterpret_cast<f32x4 *>(dcw + pos) = wv;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the dense rows are written
+  wg_barrier();                        // (3) the dense coefficient rows are in LDS
+  wg_barrier();                        // (4) nobody reads the v rows or the dense rows any more
+  wg_barrier();                        // (5) every output row is staged
+  store_rows<D>(p, ostage, n, rowbase, h, tid, 64 * (NPW + kTreeWaves));
 }
 
-template <int D, bool BF16IN, int NT>
+template <int D, bool BF16IN, int NT, bool X65>
 hipError_t launch_one(const VerifyParams &p, hipStream_t stream) {
   const unsigned units = (unsigned)(p.L * p.B * p.H);
-  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT>), dim3(units), dim3(VerifyShape<D, BF16IN, NT>::NTH), 0,
-                     stream, p);
+  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, X65>), dim3(units), dim3(VerifyShape<D, BF16IN, NT, X65>::NTH),
+                     0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool BF16IN>
 hipError_t launch_nt(const VerifyParams &p, hipStream_t stream) {
+  if (p.R == kMaxSlots) return launch_one<D, BF16IN, 4, true>(p, stream);
   switch ((p.R + 15) / 16) {
-    case 1: return launch_one<D, BF16IN, 1>(p, stream);
-    case 2: return launch_one<D, BF16IN, 2>(p, stream);
-    case 3: return launch_one<D, BF16IN, 3>(p, stream);
-    case 4: return launch_one<D, BF16IN, 4>(p, stream);
-    default: return launch_one<D, BF16IN, 5>(p, stream);
+    case 1: return launch_one<D, BF16IN, 1, false>(p, stream);
+    case 2: return launch_one<D, BF16IN, 2, false>(p, stream);
+    case 3: return launch_one<D, BF16IN, 3, false>(p, stream);
+    default: return launch_one<D, BF16IN, 4, false>(p, stream);
   }
 }
 

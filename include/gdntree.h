@@ -21,7 +21,7 @@
  * Conventions shared by every call
  *  - Every array argument is a DEVICE pointer to memory the caller owns.  The library never
  *    allocates, frees or synchronises; it validates arguments on the host, enqueues its
- *    kernels on `stream` (a hipStream_t; NULL = the default stream) and returns.
+ *    kernels on `stream` (NULL = the default stream) and returns.
  *  - Layouts are dense row-major with the shapes given; no strides.
  *  - On any error nothing is enqueued and no output is touched (except ERR_DEVICE after a
  *    failed launch, when the stream state is the runtime's).  No C++ exception crosses the
@@ -38,6 +38,8 @@
 #define GDNTREE_H
 
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h> /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -84,7 +86,7 @@ typedef struct {
  */
 gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
                              const int32_t *root_tok, int B, int P, int K, int N,
-                             gdntree_tree out, void *stream);
+                             gdntree_tree out, hipStream_t stream);
 
 /*
  * gdntree_build_shared - best-first trees for a whole batch under one shared node budget.
@@ -112,7 +114,7 @@ gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
  */
 gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_tok,
                                     const int32_t *root_tok, const int32_t *positions, int B,
-                                    int P, int K, int N, int G, gdntree_tree out, void *stream);
+                                    int P, int K, int N, int G, gdntree_tree out, hipStream_t stream);
 
 /*
  * gdntree_verify - per-node gated delta rule over the tree, one or more layers.
@@ -122,11 +124,11 @@ gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_to
  *     S_t = alpha_t (I - beta_t k_t k_t^T) S_p + beta_t k_t v_t^T,    o_t = S_t^T q_t
  * (SpecPilot summary, Prerequisites > hybrid recurrent architecture).  Node states are
  * derived along root paths from h0 and never written to memory (no per-node snapshots);
- * only o is written.  No 1/sqrt(d_k) scale is applied.  Arithmetic: gates, path solves and
- * accumulation in fp32; the matrix products take fp16 operands (bf16 rows convert exactly;
- * the state and v are scaled by a power of two per 16 value channels, so any finite scale
- * fits), which keeps the error within 2e-3 of each node state's Frobenius norm for
- * L2-normalised q and k, alpha and beta in [0, 1] (the Gated DeltaNet setting).
+ * only o is written.  No 1/sqrt(d_k) scale is applied.  Arithmetic: the products of the
+ * state with the q and k rows are fp32-exact on the matrix cores (each fp32 state entry is
+ * split into three bf16 parts that hold its 24-bit significand exactly; bf16 rows enter as
+ * they are, fp32 rows are split likewise), accumulated in fp32; the tree terms (Gram entries
+ * of ancestor pairs, the per-node path solves, the gates) and the final sums are fp32.
  *
  * Reads tree.parent, tree.anc and tree.n_nodes only (the ancestor bitmask gives each
  * node's depth and ancestors).  A request whose tree is inconsistent (parent[t] >= t,
@@ -137,16 +139,15 @@ gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_to
  *   v         in_dtype [L][B][N+1][H][d_v]
  *   alpha     in_dtype [L][B][N+1][H]   decay gate in (0, 1]
  *   beta      in_dtype [L][B][N+1][H]   write strength
- *   state     f32 [L][B][H][d_v][d_k]   committed state, read only.  NOTE the layout: the
- *             d_v x d_k transpose of the d_k x d_v matrix S, i.e. column j of S (the key-
- *             space vector of value channel j) is contiguous.
+ *   state     f32 [L][B][H][d_k][d_v]   committed state S (row i = key channel, column j =
+ *             value channel), read only
  *   o         out_dtype [L][B][N+1][H][d_v]  written for slots < n_nodes[b]
  */
 gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, int L, int H, int dk, int dv,
                               gdntree_dtype in_dtype, const void *q, const void *k,
                               const void *v, const void *alpha, const void *beta,
                               const float *state, gdntree_dtype out_dtype, void *o,
-                              void *stream);
+                              hipStream_t stream);
 
 /*
  * gdntree_accept_commit - greedy acceptance plus bonus, then the accepted-path commit.
@@ -157,11 +158,11 @@ gdntree_status gdntree_verify(gdntree_tree tree, int B, int N, int L, int H, int
  * tokens are the accepted drafts' tokens followed by the bonus target_argmax[u].
  * Commit: for every layer and head, state[l][b][h] <- the state of node u, recomputed in
  * fp32 from the committed state along root -> u with the gated delta rule and written in
- * place (same layout as gdntree_verify).
+ * place (same [d_k][d_v] layout as gdntree_verify).
  *
  *   target_argmax  i32 [B][N+1]  the target's argmax after each slot's node
  *   k, v, alpha, beta            as for gdntree_verify (rows of the accepted slots are read)
- *   state          f32 [L][B][H][d_v][d_k], updated in place
+ *   state          f32 [L][B][H][d_k][d_v], updated in place
  *   acc_len        i32 [B]       tau
  *   acc_tok        i32 [B][P+1]  accepted draft tokens then the bonus; padded with -1
  *   acc_node       i32 [B][P+1]  root slot 0 then the accepted slots; padded with -1
@@ -172,7 +173,7 @@ gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, int N, int P,
                                      int dv, gdntree_dtype in_dtype, const void *k,
                                      const void *v, const void *alpha, const void *beta,
                                      float *state, int32_t *acc_len, int32_t *acc_tok,
-                                     int32_t *acc_node, void *stream);
+                                     int32_t *acc_node, hipStream_t stream);
 
 /*
  * gdntree_accept - the acceptance half of gdntree_accept_commit on its own (one wave per
@@ -184,7 +185,7 @@ gdntree_status gdntree_accept_commit(gdntree_tree tree, int B, int N, int P,
  */
 gdntree_status gdntree_accept(gdntree_tree tree, int B, int N, int P,
                               const int32_t *target_argmax, int32_t *acc_len, int32_t *acc_tok,
-                              int32_t *acc_node, void *stream);
+                              int32_t *acc_node, hipStream_t stream);
 
 /*
  * gdntree_commit - the commit half of gdntree_accept_commit for an accepted path given by a
@@ -203,7 +204,7 @@ gdntree_status gdntree_accept(gdntree_tree tree, int B, int N, int P,
 gdntree_status gdntree_commit(gdntree_tree tree, int B, int N, int P, const int32_t *acc_len,
                               const int32_t *acc_node, int L, int H, int dk, int dv,
                               gdntree_dtype in_dtype, const void *k, const void *v,
-                              const void *alpha, const void *beta, float *state, void *stream);
+                              const void *alpha, const void *beta, float *state, hipStream_t stream);
 
 /*
  * gdntree_commit_build - gdntree_commit for this step's batch and gdntree_build for the next
@@ -227,7 +228,7 @@ gdntree_status gdntree_commit_build(gdntree_tree tree, int B, int N, int P,
                                     const float *next_lat_logp, const int32_t *next_lat_tok,
                                     const int32_t *next_root_tok, int next_B, int next_P,
                                     int next_K, int next_N, gdntree_tree next_tree,
-                                    void *stream);
+                                    hipStream_t stream);
 
 /*
  * gdntree_accept_commit_build - gdntree_accept_commit for this step and gdntree_build for
@@ -251,7 +252,7 @@ gdntree_status gdntree_accept_commit_build(gdntree_tree tree, int B, int N, int 
                                            const int32_t *next_lat_tok,
                                            const int32_t *next_root_tok, int next_B, int next_P,
                                            int next_K, int next_N, gdntree_tree next_tree,
-                                           void *stream);
+                                           hipStream_t stream);
 
 /*
  * gdntree_accept_commit_build_shared - gdntree_accept_commit_build with the next step's trees
@@ -272,10 +273,10 @@ gdntree_status gdntree_accept_commit_build_shared(
     const void *beta, float *state, int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node,
     const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
     const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
-    gdntree_tree next_tree, void *stream);
+    gdntree_tree next_tree, hipStream_t stream);
 
 /* Human-readable name of a status code ("unknown status" for other values). */
-const char *gdntree_status_str(int status);
+const char *gdntree_status_str(gdntree_status status);
 
 #ifdef __cplusplus
 }

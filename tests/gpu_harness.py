@@ -37,7 +37,7 @@ def device_inputs(w, dev="cuda"):
         lat_logp=torch.from_numpy(w.lat_logp).to(dev), lat_tok=torch.from_numpy(w.lat_tok).to(dev),
         root_tok=torch.from_numpy(w.root_tok).to(dev),
         q=w.q.to(dev), k=w.k.to(dev), v=w.v.to(dev), alpha=w.alpha.to(dev), beta=w.beta.to(dev),
-        state=g.state_from_math(w.h0).to(dev))
+        state=w.h0.to(dev))
 
 
 def run_gpu(w, out_dtype=None, d=None, split=False, shared=None):
@@ -52,7 +52,10 @@ def run_gpu(w, out_dtype=None, d=None, split=False, shared=None):
         G, positions = shared
         pos = None if positions is None else torch.tensor(np.asarray(positions, np.int32)).cuda()
         tree = g.gdntree_build_shared(d["lat_logp"], d["lat_tok"], d["root_tok"], w.cfg.N, G, pos)
-    o = g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], out_dtype=out_dtype)
+    L, B, R, Hh, D = w.q.shape
+    # zero-filled, so that converting the whole buffer never reads slots the kernel leaves alone
+    o = torch.zeros(L, B, R, Hh, D, dtype=out_dtype or d["q"].dtype, device=d["q"].device)
+    g.gdntree_verify(tree, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o=o, out_dtype=out_dtype)
     torch.cuda.synchronize()
     depth = tree.depth.cpu().numpy()
     n_nodes = tree.n_nodes.cpu().numpy()
@@ -68,7 +71,7 @@ def run_gpu(w, out_dtype=None, d=None, split=False, shared=None):
                       ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")},
                 o=o.float().cpu().numpy().astype(np.float64), target=target,
                 acc_len=acc[0].cpu().numpy(), acc_tok=acc[1].cpu().numpy(), acc_node=acc[2].cpu().numpy(),
-                state=g.state_to_math(d["state"]).cpu().numpy().astype(np.float64))
+                state=d["state"].cpu().numpy().astype(np.float64))
 
 
 def run_oracle(w, shared=None):
@@ -133,3 +136,77 @@ def config(name):
 
 def make(name, seed=0, **kw):
     return generate(name, seed=seed, **kw)
+
+
+# ---------------------------------------------------------------------------------------------
+# The oracle on every unit of a full-size configuration, in worker processes (spawned, so that
+# no GPU state is inherited; each regenerates the seeded workload itself).
+_UNIT_CACHE: dict = {}
+
+
+def _oracle_unit(job):
+    """Worker: the oracle's pipeline on request b, layers [l0, l1), of a generated workload.
+    Returns the tree, acceptance, outputs, state norms and committed states of that request."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from workloads import generate as gen
+    from workloads import resolve_target as rt
+    name, seed, b, l0, l1, scale_h0 = job
+    key = (name, seed)
+    if key not in _UNIT_CACHE:
+        _UNIT_CACHE.clear()
+        _UNIT_CACHE[key] = gen(name, seed=seed)
+    w = _UNIT_CACHE[key]
+    sl, ll = slice(b, b + 1), slice(l0, l1)
+    x = {f: getattr(w, f)[ll, sl].to(torch.float64).numpy() for f in ("q", "k", "v", "alpha", "beta")}
+    h0 = w.h0[ll, sl].double().numpy() * scale_h0
+    lat_tok, tch, tun = w.lat_tok[sl], w.tgt_choice[sl], w.tgt_uniform[sl]
+    with threadpool_limits(limits=1):
+        r = oracle.pipeline(w.lat_logp[sl], lat_tok, w.root_tok[sl], w.cfg.N, x["q"], x["k"], x["v"], x["alpha"],
+                            x["beta"], h0, lambda t: rt(t["depth"], t["n_nodes"], lat_tok, tch, tun))
+    return dict(tree={k: v[0] for k, v in r["tree"].items()}, target=r["target"][0], acc_len=r["acc_len"][0],
+                acc_tok=r["acc_tok"][0], acc_node=r["acc_node"][0], o=r["o"][:, 0].astype(np.float32),
+                hnorm=r["hnorm"][:, 0], state=r["state"][:, 0].astype(np.float32),
+                state_norm=np.sqrt((r["state"][:, 0] ** 2).sum(axis=(-2, -1))))
+
+
+def oracle_every_unit(name, seed=0, scale_h0=1.0, workers=None):
+    """The oracle on every request (and every layer) of a full configuration, one request per
+    task over up to 16 spawned worker processes.  Returns per-request results."""
+    import multiprocessing as mp
+    import os
+    B, L = CONFIGS[name].B, CONFIGS[name].L
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    lchunk = max(1, -(-L * B // workers) // B) if B < workers else L   # split layers when requests are few
+    jobs = [(name, seed, b, l0, min(L, l0 + lchunk), scale_h0) for b in range(B) for l0 in range(0, L, lchunk)]
+    with mp.get_context("spawn").Pool(min(workers, len(jobs))) as pool:
+        parts = pool.map(_oracle_unit, jobs, chunksize=1)
+    out = []
+    for b in range(B):   # layers of one request back together
+        ps = [p for j, p in zip(jobs, parts) if j[2] == b]
+        r = dict(ps[0])
+        for f in ("o", "hnorm", "state", "state_norm"):
+            r[f] = np.concatenate([p[f] for p in ps], axis=0)
+        out.append(r)
+    return out
+
+
+def check_every_unit(gpu, refs):
+    """Trees, targets and acceptance bit-exact for every request; outputs and committed states
+    of every (layer, request, head) within the bar.  Returns (out_err, state_err)."""
+    errs_o, errs_s = [], []
+    for b, r in enumerate(refs):
+        n = int(r["tree"]["n_nodes"])
+        for f in ("parent", "depth", "rank", "token"):
+            np.testing.assert_array_equal(gpu["tree"][f][b, :n], r["tree"][f][:n], err_msg=f"{f} b={b}")
+        assert gpu["tree"]["score"][b, :n].tobytes() == r["tree"]["score"][:n].tobytes(), f"score b={b}"
+        np.testing.assert_array_equal(gpu["tree"]["anc"][b, :n].view(np.uint64), r["tree"]["anc"][:n])
+        np.testing.assert_array_equal(gpu["target"][b], r["target"])
+        assert int(gpu["acc_len"][b]) == int(r["acc_len"]), f"tau b={b}"
+        np.testing.assert_array_equal(gpu["acc_tok"][b], r["acc_tok"])
+        np.testing.assert_array_equal(gpu["acc_node"][b], r["acc_node"])
+        errs_o.append(np.abs(gpu["o"][:, b, :n] - r["o"][:, :n]).max(-1) / r["hnorm"][:, :n])
+        errs_s.append(np.abs(gpu["state"][:, b] - r["state"]).max(axis=(-2, -1)) / r["state_norm"])
+    return worst(errs_o), worst(errs_s)

@@ -44,43 +44,124 @@ def test_configs(name, seed, heads, reqs, layers):
 
 
 @pytest.mark.parametrize("name", ["one_layer", "batched", "ragged", "deep"])
-def test_full_size_sampled(name):
-    """Full configuration on the GPU (the bench's launch shape); the oracle checks a sample
-    of heads and requests, the tree and acceptance of every request."""
+def test_full_size_every_unit(name):
+    """Full configuration on the GPU in the bench's launch shape; the oracle (in worker
+    processes) checks every (layer, request, head) unit: trees, targets and acceptance of every
+    request bit-exact, every output row and committed state within the bar."""
     w = generate(name, seed=0)
+    _say(f"{name} full size: GPU pipeline")
     gpu = H.run_gpu(w)
-    cfg = w.cfg
-    heads = sorted({0, cfg.H // 2, cfg.H - 1})
-    reqs = sorted({0, cfg.B - 1})
-    layers = sorted({0, cfg.L - 1})
+    _say(f"{name} full size: oracle on every unit")
+    refs = H.oracle_every_unit(name, seed=0)
+    oe, se = H.check_every_unit(gpu, refs)
+    _say(f"{name} full size, every unit: out_err={oe:.2e} state_err={se:.2e}")
+    assert oe <= H.TOL and se <= H.TOL
+
+
+@pytest.mark.parametrize("scale", [100.0, 1e-4])
+def test_state_scale_far_from_the_rows(scale):
+    """A committed state 100x larger or 10^4x smaller than the rows' scale (v ~ N(0, 1)):
+    the products stay exact at any scale, so the bar holds relative to each node state."""
+    w = H.slice_workload(generate("ragged", seed=4, B=6), H=4)
+    w.h0.mul_(scale)
+    r = H.check_all(w)
+    _say(f"h0 x {scale:g}: out_err={r['out_err']:.2e} state_err={r['state_err']:.2e}")
+
+
+def test_full_size_state_scaled_up():
+    """Every unit of the ragged batch with the committed state 100x larger."""
+    w = generate("ragged", seed=1)
+    w.h0.mul_(100.0)
+    gpu = H.run_gpu(w)
+    refs = H.oracle_every_unit("ragged", seed=1, scale_h0=100.0)
+    oe, se = H.check_every_unit(gpu, refs)
+    _say(f"ragged x100 every unit: out_err={oe:.2e} state_err={se:.2e}")
+    assert oe <= H.TOL and se <= H.TOL
+
+
+@pytest.mark.parametrize("name,heads", [("ragged", 4), ("batched", 8)])
+def test_pipelined_steps(name, heads):
+    """Four decode steps run as the bench runs them (verify(i), then acceptance + commit of
+    step i with the build of step i+1 in one launch, then verify(i+1) on the committed
+    states): every step's trees, outputs, acceptance and committed states against the oracle's
+    pipeline, each step starting from the oracle's previous committed state."""
+    import gdn_draft_tree_amd as g
     import oracle
-    tree = oracle.build_tree(w.lat_logp, w.lat_tok, w.root_tok, cfg.N)
-    H.assert_tree_equal(gpu["tree"], tree)
     from workloads import resolve_target
-    target = resolve_target(tree["depth"], tree["n_nodes"], w.lat_tok, w.tgt_choice, w.tgt_uniform)
-    acc_len, acc_tok, acc_node = oracle.accept(tree, target, cfg.P)
-    np.testing.assert_array_equal(gpu["acc_len"], acc_len)
-    np.testing.assert_array_equal(gpu["acc_tok"], acc_tok)
-    np.testing.assert_array_equal(gpu["acc_node"], acc_node)
-    errs_o, errs_s = [], []
-    for l in layers:
-        for b in reqs:
-            n = int(tree["n_nodes"][b])
-            for h in heads:
-                q, k, v = (w.f64(x)[l, b, :, h] for x in ("q", "k", "v"))
-                a, bb = w.f64("alpha")[l, b, :, h], w.f64("beta")[l, b, :, h]
-                h0 = w.h0[l, b, h].double().numpy()
-                st, ou = oracle.verify_request(tree["parent"][b], n, q[:, None], k[:, None], v[:, None],
-                                               a[:, None], bb[:, None], h0[None])
-                hn = np.sqrt((st[:, 0] ** 2).sum(axis=(-2, -1)))
-                err = np.abs(gpu["o"][l, b, :n, h] - ou[:, 0]).max(-1) / hn
-                errs_o.append(err)
-                u = int(acc_node[b, int(acc_len[b]) - 1])
-                se = np.abs(gpu["state"][l, b, h] - st[u, 0]).max() / np.linalg.norm(st[u, 0])
-                errs_s.append(se)
-    worst_o, worst_s = H.worst(errs_o), H.worst(errs_s)
-    _say(f"{name} full size: sampled out_err={worst_o:.2e} state_err={worst_s:.2e}")
-    assert worst_o <= H.TOL and worst_s <= H.TOL
+    steps = [H.slice_workload(generate(name, seed=20 + i, B=8), H=heads) for i in range(4)]
+    w0 = steps[0]
+    d = [H.device_inputs(w) for w in steps]
+    state = d[0]["state"]                     # the committed state carried across steps
+    h_ref = w0.h0.double().numpy()
+    trees = [g.gdntree_build(d[0]["lat_logp"], d[0]["lat_tok"], d[0]["root_tok"], w0.cfg.N)]
+    for i, w in enumerate(steps):
+        tree = trees[i]
+        o = torch.zeros_like(d[i]["q"])
+        g.gdntree_verify(tree, d[i]["q"], d[i]["k"], d[i]["v"], d[i]["alpha"], d[i]["beta"], state, o=o)
+        torch.cuda.synchronize()
+        depth, nn = tree.depth.cpu().numpy(), tree.n_nodes.cpu().numpy()
+        target = torch.from_numpy(resolve_target(depth, nn, w.lat_tok, w.tgt_choice, w.tgt_uniform)).cuda()
+        if i + 1 < len(steps):
+            nxt = g.Tree.empty(w.cfg.B, w.cfg.N, "cuda")
+            acc = g.gdntree_accept_commit_build(tree, target, d[i]["k"], d[i]["v"], d[i]["alpha"], d[i]["beta"],
+                                                state, w.cfg.P, d[i + 1]["lat_logp"], d[i + 1]["lat_tok"],
+                                                d[i + 1]["root_tok"], w.cfg.N, nxt)
+            trees.append(nxt)
+        else:
+            acc = g.gdntree_accept_commit(tree, target, d[i]["k"], d[i]["v"], d[i]["alpha"], d[i]["beta"], state,
+                                          w.cfg.P)
+        torch.cuda.synchronize()
+        ref = oracle.pipeline(w.lat_logp, w.lat_tok, w.root_tok, w.cfg.N, w.f64("q"), w.f64("k"), w.f64("v"),
+                              w.f64("alpha"), w.f64("beta"), h_ref,
+                              lambda t: resolve_target(t["depth"], t["n_nodes"], w.lat_tok, w.tgt_choice,
+                                                       w.tgt_uniform))
+        H.assert_tree_equal({f: getattr(tree, f).cpu().numpy() for f in
+                             ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")}, ref["tree"])
+        oe = H.output_errors(o.float().cpu().numpy().astype(np.float64), ref["o"], ref["hnorm"],
+                             ref["tree"]["n_nodes"])
+        for x, y in zip(acc, (ref["acc_len"], ref["acc_tok"], ref["acc_node"])):
+            np.testing.assert_array_equal(x.cpu().numpy(), y)
+        se = H.state_errors(state.cpu().numpy().astype(np.float64), ref["state"])
+        _say(f"{name} step {i}: out_err={oe:.2e} state_err={se:.2e} tau={ref['acc_len'].tolist()}")
+        assert oe <= H.TOL and se <= H.TOL
+        h_ref = ref["state"]                   # the next step starts from the oracle's commit
+
+
+def test_nan_gate_is_confined_to_its_head():
+    """A NaN decay gate at one used slot of one (layer, request, head) stays in that head: every
+    other (layer, request, head) gives the oracle's outputs and committed state, and so do the
+    affected head's nodes outside the slot's subtree."""
+    import oracle
+    w = _custom(P=16, K=16, N=64, B=4, H_=4, L=2, seed=6)
+    tree = oracle.build_tree(w.lat_logp, w.lat_tok, w.root_tok, w.cfg.N)
+    l0, b0, h0_, slot = 1, 2, 3, 5
+    w.alpha[l0, b0, slot, h0_] = float("nan")
+    gpu = H.run_gpu(w)
+    ref = H.run_oracle(w)
+    H.assert_tree_equal(gpu["tree"], ref["tree"])
+    n = int(tree["n_nodes"][b0])
+    anc = tree["anc"][b0].astype(np.uint64)
+    sub = [t for t in range(n) if (int(anc[t]) >> (slot - 1)) & 1]   # the slot's subtree
+    assert slot in sub
+    hit = np.zeros(gpu["o"].shape[:4], bool)
+    hit[l0, b0, sub, h0_] = True
+    used = np.zeros_like(hit)
+    for b, nb in enumerate(ref["tree"]["n_nodes"]):
+        used[:, b, :int(nb)] = True
+    ok = used & ~hit
+    err = np.abs(gpu["o"] - ref["o"]).max(-1)[ok] / ref["hnorm"][ok]
+    assert np.isfinite(gpu["o"][ok]).all() and err.max() <= H.TOL, err.max()
+    assert np.isnan(gpu["o"][l0, b0, sub, h0_]).all()
+    # committed states: every other head exact to the bar; the affected head NaN only if the
+    # accepted path went through the slot
+    se = np.abs(gpu["state"] - ref["state"]).max(axis=(-2, -1)) / np.sqrt((ref["state"] ** 2).sum(axis=(-2, -1)))
+    mask = np.ones(se.shape, bool)
+    mask[l0, b0, h0_] = False
+    assert np.isfinite(se[mask]).all() and se[mask].max() <= H.TOL
+    on_path = slot in ref["acc_node"][b0, :int(ref["acc_len"][b0])].tolist()
+    assert np.isnan(gpu["state"][l0, b0, h0_]).any() == on_path
+    _say(f"NaN gate at (l={l0}, b={b0}, h={h0_}, slot {slot}): {len(sub)} nodes NaN, others "
+         f"out_err={err.max():.2e}, state on the accepted path: {on_path}")
 
 
 def _custom(P, K, N, B=2, H_=2, D=128, dtype="bf16", L=1, seed=0, V=1000):
