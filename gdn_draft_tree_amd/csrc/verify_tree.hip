@@ -71,14 +71,15 @@ struct VerifySmem {
   typedef typename InT<BF16IN>::T T;
   static constexpr int RM = 16 * NT + (X65 ? 1 : 0);                       // rows held
   static constexpr int ROWB = (RM * D * (int)sizeof(T) + 1023) / 1024 * 1024;  // whole 1 KiB loads
-  // Dense coefficient rows for the sums on MFMA: -g_t Y and W1 at [t][s] for s < 16 NT, zero
-  // off t's ancestors-or-self; rows padded by 16 bytes, so that 16 consecutive rows read at one
+  // Dense W1 rows for the sum on MFMA: W1[t][s] for s < 32 NB (whole 32-slot blocks), zero off
+  // t's ancestors-or-self; rows padded by 16 bytes, so that 16 consecutive rows read at one
   // column hit distinct banks.
-  static constexpr int SPD = 16 * NT + 4;
-  static constexpr int DENSEB = 2 * RM * SPD * 4;
+  static constexpr int NB = (NT + 1) / 2;
+  static constexpr int SPD = 32 * NB + 4;
+  static constexpr int DENSEB = RM * SPD * 4;
   static constexpr int QKB = 2 * ROWB > DENSEB ? 2 * ROWB : (DENSEB + 15) / 16 * 16;
-  // q rows then k rows; after the products, the dense coefficient rows; after the sums, the
-  // output rows when they are wider than the v rows
+  // q rows then k rows; after the products, the dense W1 rows; after the sums, the output rows
+  // when they are wider than the v rows
   alignas(16) unsigned char qk[QKB];
   alignas(16) unsigned char vr[ROWB];      // v rows
   alignas(16) float cy[RM * kAR];          // Gram b_t k_t.k_s (strict ancestors s), then -g_t Y[t, e]
@@ -144,35 +145,6 @@ __device__ __forceinline__ void split3(const float *x, bf16x8 &hi, bf16x8 &mid, 
     mid[i] = m[0]; mid[i + 1] = m[1];
     lo[i] = l[0]; lo[i + 1] = l[1];
   }
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-// Four fp32 values split exactly in three bf16 parts (as bf16 bit patterns): the same split as
-// split3, into bf16 vectors reinterpreted whole (no per-element casts of vector elements).
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void split4(const f32x4 &x, s16x4 &hi, s16x4 &mid, s16x4 &lo) {
-  bf16x4 h4, m4, l4;
-#pragma unroll
-  for (int i = 0; i < 4; i += 2) {
-    const f32x2 v = {x[i], x[i + 1]};
-    const bf16x2 h = __builtin_convertvector(v, bf16x2);
-    const f32x2 r = v - __builtin_convertvector(h, f32x2);
-    const bf16x2 m = __builtin_convertvector(r, bf16x2);
-    const bf16x2 l = __builtin_convertvector(r - __builtin_convertvector(m, f32x2), bf16x2);
-    h4[i] = h[0]; h4[i + 1] = h[1];
-    m4[i] = m[0]; m4[i + 1] = m[1];
-    l4[i] = l[0]; l4[i + 1] = l[1];
-  }
-  hi = __builtin_bit_cast(s16x4, h4);
-  mid = __builtin_bit_cast(s16x4, m4);
-  lo = __builtin_bit_cast(s16x4, l4);
-}
-
-// 16 x 16 x 16 bf16 product: lane (g, c) holds A[c][4 g + 0..3] and B[4 g + 0..3][c], and gets
-// C[4 g + 0..3][c] -- so the C tile of one product is the B operand of the next.
-__device__ __forceinline__ f32x4 mfma16(s16x4 a, s16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -244,6 +216,14 @@ __device__ __forceinline__ void row8(const typename InT<BF16IN>::T *rows, int r,
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   }
+}
+
+// The eight W1 values of one A fragment of the sum: columns c..c+3 and c+16..c+19 of a dense row.
+__device__ __forceinline__ void row8w(const float *p, float *x) {
+  const float4 a = *reinterpret_cast<const float4 *>(p);
+  const float4 b = *reinterpret_cast<const float4 *>(p + 16);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
 __device__ __forceinline__ int wave_max_i32(int x) {
@@ -337,8 +317,8 @@ void verify_kernel(VerifyParams p) {
   const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
   const T *vrow = reinterpret_cast<const T *>(s.vr);
   static_assert(SM::QKB >= RM * D * 4, "fp32 output rows fit over the q and k rows");
-  // Output rows are staged over the v rows when they fit there, else over the q and k rows
-  // (where the dense coefficient rows may be): either way after every read of them.
+  // Output rows are staged over the v rows when they fit there (the last v reads come before
+  // barrier (3)), else over the q and k rows after one more barrier (the dense rows are there).
   const bool stage_in_v = (p.out_bf16 ? 2 : 4) <= (int)sizeof(T);
   unsigned char *ostage = stage_in_v ? s.vr : s.qk;
 
@@ -425,76 +405,54 @@ void verify_kernel(VerifyParams p) {
       wg_barrier();  // (2) nobody reads q or k rows any more; coefficients are ready
       const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
-      // ---- o[t] = g_t A_q[t] + sum_s Cy[t][s] A_k[s] + Cw[t][s] v[s] on MFMA -------------
-      // with the dense coefficient rows (Cy = -g_t Y, Cw = W1, zero off t's ancestors-or-self)
-      // over s < 16 NT, then the 65th row on VALU.  16x16x16 products: the A operand of lane
-      // (g, c) is Cy[16 mt + c][16 ms + 4 g + 0..3]; the B operand is A_k[16 ms + 4 g + 0..3][j],
-      // which is this lane's own K-pass accumulator of tile ms (C layout), split in three, or
-      // v[16 ms + 4 g + 0..3][j].  Every fp32 operand is split exactly; the v rows are bf16 (or
-      // fp32 split in three).
+      // ---- o[t] = g_t A_q[t] + sum_s W1[t][s] U[s] on MFMA, U[s] = v[s] - g_s A_k[s] ---------
+      // (the two sums of the tree form in one: W1[t][s] U[s] = W1[t][s] v[s] - g_t Y[t, s] A_k[s],
+      // as W1 = (g_t / g_s) Y).  U takes A_k's place in this lane's registers (rows >= n zero).
+      // 16x16x32 products over 32-slot blocks, the contraction index k = 8 g + e of lane (g, c)
+      // standing for slot s = 32 mb + 16 (e / 4) + 4 g + e % 4: the B operand of lane (g, c) is
+      // then its own U rows of tiles 2 mb and 2 mb + 1 (C layout, rows 4 g + 0..3) split in three,
+      // and the A operand holds W1[16 mt + c][s(8 g + e)] from the dense rows.  The 65th row goes
+      // on VALU.
       constexpr int SPD = SM::SPD;
-      const float *dcy = reinterpret_cast<const float *>(s.qk);
-      const float *dcw = dcy + RM * SPD;
-      auto dpos = [](int t, int s4) { return t * SPD + s4; };
+      const float *dw = reinterpret_cast<const float *>(s.qk);
       f32x4 oc[NTU];
 #pragma unroll
-      for (int mt = 0; mt < NTU; ++mt)
+      for (int mt = 0; mt < NTU; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) oc[mt][r] = s.gamma[16 * mt + 4 * g4 + r] * aq[mt][r];  // rows >= n unused
-      const float v64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) : 0.f;
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * mt + 4 * g4 + r;
+          const float gt = s.gamma[t];
+          oc[mt][r] = gt * aq[mt][r];  // rows >= n are never stored
+          ak[mt][r] = t < n ? to_f32(vrow[swz<D, CH>(t, j)]) - gt * ak[mt][r] : 0.f;
+        }
+      }
+      // the 65th row: A_k[64] and A_q[64] sit in lanes (0, c) of a65
+      const float u64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) - s.gamma[64] * a65[0] : 0.f;
       float p64 = 0.f;  // this lane's share of row 64's sum over s < 64
-      wg_barrier();     // (3) the dense coefficient rows are in LDS
-      // A_k tile ms outermost: only its split operands are live while the row tiles mt >= ms
-      // (the coefficient rows vanish above the diagonal) take their products.
+      wg_barrier();     // (3) the dense W1 rows are in LDS; nobody reads the v rows any more
+      constexpr int NBU = (NTU + 1) / 2;  // 32-slot blocks in use
 #pragma unroll
-      for (int ms = 0; ms < NTU; ++ms) {
-        s16x4 kh, km, kl, vh, vm, vl;
-        f32x4 vv;
+      for (int mb = 0; mb < NBU; ++mb) {
+        bf16x8 uh, um, ul;
+        float ua[8];
 #pragma unroll
-        // rows >= n hold copies of row n - 1 (finite) and meet zero coefficients
-        for (int r = 0; r < 4; ++r) vv[r] = to_f32(vrow[swz<D, CH>(16 * ms + 4 * g4 + r, j)]);
-        split4(ak[ms], kh, km, kl);
-        if constexpr (BF16IN) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vh[r] = (short)(__float_as_uint(vv[r]) >> 16);  // exact
-        } else {
-          split4(vv, vh, vm, vl);
-        }
+        for (int e = 0; e < 8; ++e) ua[e] = (2 * mb + (e >> 2) < NTU) ? ak[imin(2 * mb + (e >> 2), NTU - 1)][e & 3] : 0.f;
+        split3(ua, uh, um, ul);
         if (R65 && r64) {
-          const f32x4 cyv = *reinterpret_cast<const f32x4 *>(dcy + dpos(64, 16 * ms + 4 * g4));
-          const f32x4 cwv = *reinterpret_cast<const f32x4 *>(dcw + dpos(64, 16 * ms + 4 * g4));
+          float wr[8];
+          row8w(dw + 64 * SPD + 32 * mb + 4 * g4, wr);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) p64 = fmaf(cyv[r], ak[ms][r], fmaf(cwv[r], vv[r], p64));
+          for (int e = 0; e < 8; ++e) p64 = fmaf(wr[e], ua[e], p64);
         }
 #pragma unroll
-        for (int mt = ms; mt < NTU; ++mt) {
-          const f32x4 cyv = *reinterpret_cast<const f32x4 *>(dcy + dpos(16 * mt + l16, 16 * ms + 4 * g4));
-          const f32x4 cwv = *reinterpret_cast<const f32x4 *>(dcw + dpos(16 * mt + l16, 16 * ms + 4 * g4));
-          s16x4 ah, am, al, wh, wm, wl;
-          split4(cyv, ah, am, al);
-          split4(cwv, wh, wm, wl);
+        for (int mt = 2 * mb; mt < NTU; ++mt) {
+          float wa[8];
+          row8w(dw + (16 * mt + l16) * SPD + 32 * mb + 4 * g4, wa);
+          bf16x8 wh, wm, wl;
+          split3(wa, wh, wm, wl);
           __builtin_amdgcn_sched_barrier(0);
-          f32x4 c = oc[mt];
-          c = mfma16(al, kh, c);
-          c = mfma16(am, km, c);
-          c = mfma16(ah, kl, c);
-          c = mfma16(am, kh, c);
-          c = mfma16(ah, km, c);
-          c = mfma16(ah, kh, c);
-          if constexpr (BF16IN) {
-            c = mfma16(wl, vh, c);
-            c = mfma16(wm, vh, c);
-            c = mfma16(wh, vh, c);
-          } else {
-            c = mfma16(wl, vh, c);
-            c = mfma16(wm, vm, c);
-            c = mfma16(wh, vl, c);
-            c = mfma16(wm, vh, c);
-            c = mfma16(wh, vm, c);
-            c = mfma16(wh, vh, c);
-          }
-          oc[mt] = c;
-          drain(oc[mt]);  // these products have completed before the next split overwrites a*, w*, k*, v*
+          oc[mt] = mfma_x6(wh, wm, wl, uh, um, ul, oc[mt]);
+          drain(oc[mt]);  // these products have completed before the next split overwrites w*
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -503,8 +461,7 @@ void verify_kernel(VerifyParams p) {
         p64 += __shfl_xor(p64, 16);
         p64 += __shfl_xor(p64, 32);
         const int d64 = imin((int)__popcll(s.mask[64]), kMaxP);
-        // a65 holds A_k[64][j], A_q[64][j] in the lanes of row group 0, which stage row 64
-        o64 = s.gamma[64] * a65[1] + p64 + s.cy[64 * kAR + d64] * a65[0] + s.cw[64 * kAR + d64] * v64;
+        o64 = s.gamma[64] * a65[1] + p64 + s.cw[64 * kAR + d64] * u64;
       }
       if (bad) {
 #pragma unroll
@@ -512,7 +469,7 @@ void verify_kernel(VerifyParams p) {
                                                        __builtin_nanf("")};
         o64 = __builtin_nanf("");
       }
-      wg_barrier();  // (4) nobody reads the v rows or the dense rows any more
+      if (!stage_in_v) wg_barrier();  // (4) nobody reads the dense rows over the q and k rows any more
 
       // ---- output rows, staged over the v rows (or the q and k rows for wider outputs) -----
       auto stage = [&](int t, float x) {
@@ -800,32 +757,29 @@ void verify_kernel(VerifyParams p) {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the coefficient rows are written
   wg_barrier();        // (2) nobody reads the q and k rows any more
   {
-    // dense coefficient rows: [t][s] = the compact entry at s's depth when s is an
-    // ancestor-or-self of t (the root, or bit s - 1 of t's mask), else zero; four columns a lane
-    constexpr int SPD = SM::SPD, NCH = SPD / 4 - 1;  // four columns a lane; the padding stays unwritten
-    float *dcy = reinterpret_cast<float *>(s.qk);
-    float *dcw = dcy + RM * SPD;
-    for (int c = 64 * tw + lane; c < RM * NCH; c += 64 * kTreeWaves) {
-      const int t = c / NCH, q = c % NCH;
-      const bool tv = t < n;
-      const unsigned long long m = tv ? s.mask[t] : 0ull;
-      f32x4 yv, wv;
+    // dense W1 rows over the q and k rows: zeros, then each node's entries at its ancestors'
+    // slots (tw 0, one lane per node, from the compact rows)
+    constexpr int SPD = SM::SPD;
+    float *dw = reinterpret_cast<float *>(s.qk);
+    for (int i = 64 * tw + lane; i < SM::DENSEB / 16; i += 64 * kTreeWaves)
+      reinterpret_cast<uint4 *>(dw)[i] = make_uint4(0u, 0u, 0u, 0u);
+    tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the dense rows are zero
+    if (tw == 0) {
+      if (t_me < n) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sc = 4 * q + i;
-        const bool anc = tv && (sc == 0 || (sc <= t && ((m >> (sc - 1)) & 1ull)));
-        const int e = sc == 0 ? 0 : imin(1 + (int)__popcll(m & ((1ull << (sc - 1)) - 1ull)), kMaxP);
-        yv[i] = anc ? s.cy[t * kAR + e] : 0.f;
-        wv[i] = anc ? s.cw[t * kAR + e] : 0.f;
+        for (int e = 0; e <= kMaxP; ++e) {
+          if (e <= d_me) {
+            const int a = (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu);  // slot at depth e
+            dw[t_me * SPD + a] = s.cw[t_me * kAR + e];
+          }
+        }
       }
-      const int pos = t * SPD + 4 * q;
-      *reinterpret_cast<f32x4 *>(dcy + pos) = yv;
-      *reinterpret_cast<f32x4 *>(dcw + pos) = wv;
+      if (lane == 0) dw[0] = s.cw[0];  // the root
     }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the dense rows are written
-  wg_barrier();                        // (3) the dense coefficient rows are in LDS
-  wg_barrier();                        // (4) nobody reads the v rows or the dense rows any more
+  wg_barrier();                        // (3) the dense W1 rows are in LDS
+  if (!stage_in_v) wg_barrier();       // (4) nobody reads the dense rows any more
   wg_barrier();                        // (5) every output row is staged
   store_rows<D>(p, ostage, n, rowbase, h, tid, 64 * (NPW + kTreeWaves));
 }
