@@ -72,18 +72,21 @@ struct VerifySmem {
   static constexpr int RM = 16 * NT + (X65 ? 1 : 0);                       // rows held
   static constexpr int ROWB = (RM * D * (int)sizeof(T) + 1023) / 1024 * 1024;  // whole 1 KiB loads
   // Dense W1 rows for the sum on MFMA: W1[t][s] for s < 32 NB (whole 32-slot blocks), zero off
-  // t's ancestors-or-self; rows padded by 16 bytes, so that 16 consecutive rows read at one
-  // column hit distinct banks.
+  // t's ancestors-or-self; 16-byte chunks XOR-swizzled by the row, so that 16 consecutive rows
+  // read at one column hit distinct banks.  Over the compact k.k rows, which the path solves are
+  // the last to read.
   static constexpr int NB = (NT + 1) / 2;
-  static constexpr int SPD = 32 * NB + 4;
-  static constexpr int DENSEB = RM * SPD * 4;
-  static constexpr int QKB = 2 * ROWB > DENSEB ? 2 * ROWB : (DENSEB + 15) / 16 * 16;
-  // q rows then k rows; after the products, the dense W1 rows; after the sums, the output rows
-  // when they are wider than the v rows
+  static constexpr int SPD = 32 * NB;
+  static constexpr int CHM = SPD / 4 - 1;  // chunk index mask of a dense row
+  static constexpr int QKB = 2 * ROWB;
+  // q rows then k rows; after the sums, the output rows when they are wider than the v rows
   alignas(16) unsigned char qk[QKB];
   alignas(16) unsigned char vr[ROWB];      // v rows
-  alignas(16) float cy[RM * kAR];          // Gram b_t k_t.k_s (strict ancestors s), then -g_t Y[t, e]
-  alignas(16) float cw[RM * kAR];          // Gram q_t.k_s (ancestors-or-self s), then W1[t, e]
+  union alignas(16) {
+    float cy[RM * kAR];                    // Gram b_t k_t.k_s (strict ancestors s)
+    float dw[RM * SPD];                    // then the dense W1 rows
+  };
+  alignas(16) float cw[RM * kAR];          // Gram q_t.k_s (ancestors-or-self s), then W1[t, e] (compact)
   alignas(16) unsigned long long mask[RM];
   float gamma[RM];                         // path gate g_t
   float beta[RM];                          // b per node
@@ -218,10 +221,16 @@ __device__ __forceinline__ void row8(const typename InT<BF16IN>::T *rows, int r,
   }
 }
 
-// The eight W1 values of one A fragment of the sum: columns c..c+3 and c+16..c+19 of a dense row.
-__device__ __forceinline__ void row8w(const float *p, float *x) {
-  const float4 a = *reinterpret_cast<const float4 *>(p);
-  const float4 b = *reinterpret_cast<const float4 *>(p + 16);
+// Position of W1[t][s] in the dense rows: 16-byte chunks XOR-swizzled by the row.
+template <int SPD, int CHM>
+__device__ __forceinline__ int wpos(int t, int sc) {
+  return t * SPD + ((((sc >> 2) ^ t) & CHM) << 2) + (sc & 3);
+}
+// The eight W1 values of one A fragment of the sum: columns c..c+3 and c+16..c+19 of row t.
+template <int SPD, int CHM>
+__device__ __forceinline__ void row8w(const float *dw, int t, int c, float *x) {
+  const float4 a = *reinterpret_cast<const float4 *>(dw + wpos<SPD, CHM>(t, c));
+  const float4 b = *reinterpret_cast<const float4 *>(dw + wpos<SPD, CHM>(t, c + 16));
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -317,8 +326,8 @@ void verify_kernel(VerifyParams p) {
   const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
   const T *vrow = reinterpret_cast<const T *>(s.vr);
   static_assert(SM::QKB >= RM * D * 4, "fp32 output rows fit over the q and k rows");
-  // Output rows are staged over the v rows when they fit there (the last v reads come before
-  // barrier (3)), else over the q and k rows after one more barrier (the dense rows are there).
+  // Output rows are staged over the v rows when they fit there, else over the q and k rows; after
+  // barrier (3) either way (the last v reads come before it).
   const bool stage_in_v = (p.out_bf16 ? 2 : 4) <= (int)sizeof(T);
   unsigned char *ostage = stage_in_v ? s.vr : s.qk;
 
@@ -402,7 +411,7 @@ void verify_kernel(VerifyParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      wg_barrier();  // (2) nobody reads q or k rows any more; coefficients are ready
+      wg_barrier();  // (2) nobody reads q or k rows any more; the dense W1 rows are ready
       const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
       // ---- o[t] = g_t A_q[t] + sum_s W1[t][s] U[s] on MFMA, U[s] = v[s] - g_s A_k[s] ---------
@@ -413,8 +422,8 @@ void verify_kernel(VerifyParams p) {
       // then its own U rows of tiles 2 mb and 2 mb + 1 (C layout, rows 4 g + 0..3) split in three,
       // and the A operand holds W1[16 mt + c][s(8 g + e)] from the dense rows.  The 65th row goes
       // on VALU.
-      constexpr int SPD = SM::SPD;
-      const float *dw = reinterpret_cast<const float *>(s.qk);
+      constexpr int SPD = SM::SPD, CHM = SM::CHM;
+      const float *dw = s.dw;
       f32x4 oc[NTU];
 #pragma unroll
       for (int mt = 0; mt < NTU; ++mt) {
@@ -429,7 +438,6 @@ void verify_kernel(VerifyParams p) {
       // the 65th row: A_k[64] and A_q[64] sit in lanes (0, c) of a65
       const float u64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) - s.gamma[64] * a65[0] : 0.f;
       float p64 = 0.f;  // this lane's share of row 64's sum over s < 64
-      wg_barrier();     // (3) the dense W1 rows are in LDS; nobody reads the v rows any more
       constexpr int NBU = (NTU + 1) / 2;  // 32-slot blocks in use
 #pragma unroll
       for (int mb = 0; mb < NBU; ++mb) {
@@ -440,14 +448,14 @@ void verify_kernel(VerifyParams p) {
         split3(ua, uh, um, ul);
         if (R65 && r64) {
           float wr[8];
-          row8w(dw + 64 * SPD + 32 * mb + 4 * g4, wr);
+          row8w<SPD, CHM>(dw, 64, 32 * mb + 4 * g4, wr);
 #pragma unroll
           for (int e = 0; e < 8; ++e) p64 = fmaf(wr[e], ua[e], p64);
         }
 #pragma unroll
         for (int mt = 2 * mb; mt < NTU; ++mt) {
           float wa[8];
-          row8w(dw + (16 * mt + l16) * SPD + 32 * mb + 4 * g4, wa);
+          row8w<SPD, CHM>(dw, 16 * mt + l16, 32 * mb + 4 * g4, wa);
           bf16x8 wh, wm, wl;
           split3(wa, wh, wm, wl);
           __builtin_amdgcn_sched_barrier(0);
@@ -469,7 +477,7 @@ void verify_kernel(VerifyParams p) {
                                                        __builtin_nanf("")};
         o64 = __builtin_nanf("");
       }
-      if (!stage_in_v) wg_barrier();  // (4) nobody reads the dense rows over the q and k rows any more
+      wg_barrier();  // (3) nobody reads the v rows any more
 
       // ---- output rows, staged over the v rows (or the q and k rows for wider outputs) -----
       auto stage = [&](int t, float x) {
@@ -488,7 +496,7 @@ void verify_kernel(VerifyParams p) {
       }
       if (R65 && r64 && g4 == 0) stage(64, o64);
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's output rows are staged
-      wg_barrier();        // (5) every output row is staged
+      wg_barrier();        // (4) every output row is staged
     };
     static_assert(NT >= 1 && NT <= 4, "one to four row tiles");
     if (ntl == NT) product_phase(std::integral_constant<int, NT>{});
@@ -533,13 +541,15 @@ void verify_kernel(VerifyParams p) {
       w_b1 = reinterpret_cast<const uint32_t *>(gb)[(rowbase + tn) * p.H + h];
     }
   } else {
-    constexpr int NL = 2 * RM * kAR * 4 / 16;
-    static_assert(offsetof(SM, cw) == offsetof(SM, cy) + RM * kAR * 4, "cy and cw adjacent");
+    constexpr int NL = RM * kAR * 4 / 16;  // 16-byte pieces of each compact array
     constexpr int NC = kTreeWaves - 1;
 #pragma unroll
     for (int x = 0; x < (NL + 64 * NC - 1) / (64 * NC); ++x) {
       const int i = (tw - 1) * 64 + lane + 64 * NC * x;
-      if (i < NL) reinterpret_cast<uint4 *>(s.cy)[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < NL) {
+        reinterpret_cast<uint4 *>(s.cy)[i] = make_uint4(0u, 0u, 0u, 0u);
+        reinterpret_cast<uint4 *>(s.cw)[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
     // q, k and v rows straight into LDS, 1 KiB chunks dealt over tw 1..3: each wave
     // instruction fills 64 consecutive 16-byte chunks; lane l of chunk qi holds physical chunk
@@ -738,49 +748,38 @@ void verify_kernel(VerifyParams p) {
       }
     }
     if (tv) {
-      const float gt = s.gamma[t];
+#pragma unroll
+      for (int e = 0; e <= kMaxP; ++e)
+        if (e <= d_me) s.cw[t * kAR + e] = s.cwl[e][lane] * z[e];  // W1[t, e]
+    }
+    if (lane == 0) s.cw[0] = s.beta[0] * z_root;  // the root: W1[0, 0] = b_0 (q_0 . k_0)
+    // the compact k.k rows are read for the last time above: zero their part of the dense rows
+    for (int i = lane; i < RM * kAR / 4; i += 64) reinterpret_cast<uint4 *>(s.dw)[i] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    // the part of the dense rows past the compact k.k rows
+    for (int i = RM * kAR / 4 + 64 * (tw - 1) + lane; i < RM * SM::SPD / 4; i += 64 * (kTreeWaves - 1))
+      reinterpret_cast<uint4 *>(s.dw)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the dense rows are zero, the W1 rows written
+  if (tw == 0) {
+    // each node's W1 entries at its ancestors' slots
+    constexpr int SPD = SM::SPD, CHM = SM::CHM;
+    if (t_me < n) {
 #pragma unroll
       for (int e = 0; e <= kMaxP; ++e) {
         if (e <= d_me) {
-          const float yv = s.beta[anc_at(e)] * z[e];  // Y[t, e]
-          s.cy[t * kAR + e] = -gt * yv;
-          s.cw[t * kAR + e] = s.cwl[e][lane] * z[e];
+          const int a = (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu);  // slot at depth e
+          // slot 64 (node 64 itself) has no column: its term is added on VALU
+          if (a < SPD) s.dw[wpos<SPD, CHM>(t_me, a)] = s.cw[t_me * kAR + e];
         }
       }
     }
-    if (lane == 0) {  // the root: Y[0, 0] = W1[0, 0] = b_0 (q_0 . k_0)
-      const float y0 = s.beta[0] * z_root;
-      s.cy[0] = -s.gamma[0] * y0;
-      s.cw[0] = y0;
-    }
+    if (lane == 0) s.dw[0] = s.cw[0];  // the root
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the coefficient rows are written
-  wg_barrier();        // (2) nobody reads the q and k rows any more
-  {
-    // dense W1 rows over the q and k rows: zeros, then each node's entries at its ancestors'
-    // slots (tw 0, one lane per node, from the compact rows)
-    constexpr int SPD = SM::SPD;
-    float *dw = reinterpret_cast<float *>(s.qk);
-    for (int i = 64 * tw + lane; i < SM::DENSEB / 16; i += 64 * kTreeWaves)
-      reinterpret_cast<uint4 *>(dw)[i] = make_uint4(0u, 0u, 0u, 0u);
-    tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the dense rows are zero
-    if (tw == 0) {
-      if (t_me < n) {
-#pragma unroll
-        for (int e = 0; e <= kMaxP; ++e) {
-          if (e <= d_me) {
-            const int a = (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu);  // slot at depth e
-            dw[t_me * SPD + a] = s.cw[t_me * kAR + e];
-          }
-        }
-      }
-      if (lane == 0) dw[0] = s.cw[0];  // the root
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the dense rows are written
-  wg_barrier();                        // (3) the dense W1 rows are in LDS
-  if (!stage_in_v) wg_barrier();       // (4) nobody reads the dense rows any more
-  wg_barrier();                        // (5) every output row is staged
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the dense W1 rows are written
+  wg_barrier();        // (2) the dense W1 rows are ready
+  wg_barrier();        // (3) nobody reads the v rows any more
+  wg_barrier();        // (4) every output row is staged
   store_rows<D>(p, ostage, n, rowbase, h, tid, 64 * (NPW + kTreeWaves));
 }
 
