@@ -266,6 +266,9 @@ def main():
                     help="verify (and commit) launches timed one by one for the medians (>= 100)")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the streaming probe that measures what this part streams for the verify's bytes")
+    ap.add_argument("--verify-only", type=int, default=0, metavar="K",
+                    help="instead of the step benchmark: K verify launches back to back over the input "
+                         "sets, then exit (a short, single-kernel program for profiler runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X and has no "
@@ -355,6 +358,18 @@ def main():
                 d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
                 dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, cfg.G, dn["tree"],
                 next_positions=dn["positions"], acc=d["acc"], stream=stream, prepare=True)
+
+    if args.verify_only:
+        for i in range(args.verify_only):
+            sets[i % nsets]["p_verify"]()
+        torch.cuda.synchronize()
+        if args.copy_calibration:
+            src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            torch.mul(src, 1.0, out=dst)
+            torch.cuda.synchronize()
+        print(json.dumps({"verify_only": args.verify_only, "workload": args.workload, "sets": nsets}))
+        return
 
     def step(i, events=None):
         d = sets[i % nsets]

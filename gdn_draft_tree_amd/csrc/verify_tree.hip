@@ -14,38 +14,44 @@
 // ancestors-or-self anc e at depths e = 0..d_t, let z solve (deepest first)
 //     z[e] + sum_{e2 > e} z[e2] b_{anc e2} (k_{anc e2} . k_{anc e}) = q_t . k_{anc e};
 // with Y[t, e] = b_{anc e} z[e] and W1[t, e] = (g_t / g_{anc e}) Y[t, e],
-//     o_t = g_t (S0^T q_t - sum_e Y[t, e] S0^T k_{anc e}) + sum_e W1[t, e] v_{anc e}.
+//     o_t = g_t (S0^T q_t - sum_e Y[t, e] S0^T k_{anc e}) + sum_e W1[t, e] v_{anc e}
+//         = g_t S0^T q_t + sum_e W1[t, e] U[anc e],     U[s] = v_s - g_s S0^T k_s.
 // So the committed state S0 (d_k x d_v fp32), the only large operand, enters through the
 // dense products A_q = Q S0 and A_k = K S0 over the rows as they are, which need neither
 // the tree nor the gates; the tree enters through small work on q, k, a, b only (Gram
-// entries of ancestor pairs, one path solve per node), and the two meet in a sparse sum over
-// each node's ancestors.
+// entries of ancestor pairs, one path solve per node), and the two meet in one product of
+// the (sparse, lower triangular) W1 rows with U.
 //
 // Precision.  The products A_q and A_k are fp32-exact: each fp32 state entry is split into
 // three bf16 parts hi + mid + lo that hold its 24-bit significand exactly (hi = RN(x),
 // mid = RN(x - hi), lo = x - hi - mid, every difference exact in fp32), and every part
 // multiplies the bf16 rows exactly on MFMA with fp32 accumulation.  fp32 rows are split the
 // same way (six of the nine part products; the three dropped ones are below 2^-24 of the
-// term).  The Gram entries are exact products accumulated in fp32 (split likewise for fp32
-// rows), and the path solves, gates and the sparse sums run in fp32.
+// term), and so are W1 and U in their product.  The Gram entries are exact products
+// accumulated in fp32 (split likewise for fp32 rows), and the path solves and gates run in
+// fp32.
 //
-// Work decomposition: one workgroup per (layer, request, head) with two kinds of waves.
+// Work decomposition: one workgroup per (layer, request, head), two resident per CU, with two
+// kinds of waves.
 //  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they gather this
 //    head's state columns from the [d_k][d_v] layout (lane (g, c) holds S0[32 ks + 8 g + e]
-//    [16 w + c], the B operand of a 16x16x32 product), split it as it lands, and form A_k and
-//    A_q for their channels with the row tiles read from LDS; then the sparse sums.
+//    [16 w + c], an operand of a 16x16x32 product), split them as they land, and form A_k and
+//    A_q for their channels with the row tiles read from LDS; then the W1 U product and the
+//    output rows.
 //  * four tree waves: wave 0 loads the per-node inputs and does the per-node prologue; waves
 //    1..3 stream the q, k and v rows into LDS (buffer loads to LDS).  Together they compute
 //    the Gram tiles [Q; K] K^T of the lower node triangle, then wave 0 does the per-node path
-//    solves (one lane per node), which give each node's coefficient rows.
-// Rows 0..63 go through 16-row MFMA tiles; a 65th row (a tree of 64 drafts) is done on VALU
-// from the fp32 state fragments, so that a single row never costs a whole tile.
+//    solves (one lane per node).
+// Once the q and k rows are dead, every wave writes its share of the W1 rows over them as
+// dense bf16 parts, the operand of the W1 U product.  Rows 0..63 go through 16-row MFMA
+// tiles; a 65th row (a tree of 64 drafts) rides in one extra tile of its own, and its W1 row
+// is summed on VALU.
 //
 // MFMA operand registers are refilled only after the products that read them have completed:
 // every chain of products is fenced off from the code that refills its operands, and before a
-// product wave splits the next state fragment into the registers the previous products read,
-// it reads each accumulator those products wrote (a VALU read of an MFMA result, which the
-// compiler delays by the required wait states, so the products have finished).
+// wave overwrites registers that earlier products read, it reads each accumulator those
+// products wrote (a VALU read of an MFMA result, which the compiler delays by the required
+// wait states, so the products have finished).
 
 #include <type_traits>
 
@@ -67,29 +73,37 @@ struct InT<false> { typedef float T; };
 
 // NT 16-row tiles of rows (rows 0 .. 16 NT - 1) plus, with X65, the 65th row.
 template <int D, bool BF16IN, int NT, bool X65>
-struct VerifySmem {
+struct VerifyGeom {
   typedef typename InT<BF16IN>::T T;
   static constexpr int RM = 16 * NT + (X65 ? 1 : 0);                       // rows held
   static constexpr int ROWB = (RM * D * (int)sizeof(T) + 1023) / 1024 * 1024;  // whole 1 KiB loads
-  // Dense W1 rows for the sum on MFMA: W1[t][s] for s < 32 NB (whole 32-slot blocks), zero off
-  // t's ancestors-or-self; 16-byte chunks XOR-swizzled by the row, so that 16 consecutive rows
-  // read at one column hit distinct banks.  Over the compact k.k rows, which the path solves are
-  // the last to read.
-  static constexpr int NB = (NT + 1) / 2;
-  static constexpr int SPD = 32 * NB;
-  static constexpr int CHM = SPD / 4 - 1;  // chunk index mask of a dense row
-  static constexpr int QKB = 2 * ROWB;
-  // q rows then k rows; after the sums, the output rows when they are wider than the v rows
-  alignas(16) unsigned char qk[QKB];
-  alignas(16) unsigned char vr[ROWB];      // v rows
-  union alignas(16) {
-    float cy[RM * kAR];                    // Gram b_t k_t.k_s (strict ancestors s)
-    float dw[RM * SPD];                    // then the dense W1 rows
-  };
-  alignas(16) float cw[RM * kAR];          // Gram q_t.k_s (ancestors-or-self s), then W1[t, e] (compact)
-  alignas(16) unsigned long long mask[RM];
-  float gamma[RM];                         // path gate g_t
-  float beta[RM];                          // b per node
+  static constexpr int NB = (NT + 1) / 2;  // 32-slot blocks of the W1 U product
+  static constexpr int SPD = 32 * NB;      // slots per dense W1 row
+  static constexpr int PR = 16 * NT;       // dense W1 rows (the 65th row is kept apart, in fp32)
+  static constexpr int CPW = SPD / 8;      // 16-byte chunks per dense W1 row
+  static constexpr bool PL_R0 = 3 * PR * SPD * 2 <= 2 * ROWB;  // the dense parts fit over q and k
+  static constexpr int NPW = D / 16;       // product waves
+  static constexpr int WAVES = NPW + kTreeWaves;
+  static constexpr int NTH = 64 * WAVES;
+};
+
+template <int D, bool BF16IN, int NT, bool X65>
+struct VerifySmem {
+  typedef VerifyGeom<D, BF16IN, NT, X65> G;
+  // q rows | k rows; once they are dead, the dense W1 rows as three bf16 parts (when they fit):
+  // W1[t][s] for t < PR, s < SPD, zero off t's ancestors-or-self.  Within a 32-slot block,
+  // slot 16 h + 4 g + i sits at 8 g + 4 h + i, so that one lane's operand fragment is one
+  // 16-byte chunk; chunks are XOR-swizzled by the row, so that 16 consecutive rows read at one
+  // chunk hit distinct banks.  Output rows wider than the inputs are staged here at the end.
+  alignas(16) unsigned char r0[2 * G::ROWB];
+  alignas(16) unsigned char r1[G::ROWB];   // v rows; then the output rows (when they fit)
+  alignas(16) uint16_t plx[G::PL_R0 ? 8 : 3 * G::PR * G::SPD];  // the dense W1 parts otherwise
+  alignas(16) float cy[G::RM * kAR];       // Gram b_t k_t.k_s (strict ancestors s)
+  alignas(16) float cw[G::RM * kAR];       // Gram q_t.k_s (ancestors-or-self s), then W1[t, e] (compact)
+  alignas(16) float w64[X65 ? 64 : 4];     // W1[64][s], s < 64, in fp32
+  alignas(16) unsigned long long mask[G::RM];
+  float gamma[G::RM];                      // path gate g_t
+  float beta[G::RM];                       // b per node
   float cwl[kMaxAnc][64];                  // W1 weights b_{anc e} g_t / g_{anc e}, per depth and lane
   int bad;
   int sync;                                // tree-wave phase counter
@@ -97,15 +111,13 @@ struct VerifySmem {
 
 template <int D, bool BF16IN, int NT, bool X65>
 struct VerifyShape {
-  static constexpr int NPW = D / 16;       // product waves
-  static constexpr int WAVES = NPW + kTreeWaves;
-  static constexpr int NTH = 64 * WAVES;
+  typedef VerifyGeom<D, BF16IN, NT, X65> G;
   static constexpr int LDS = (int)sizeof(VerifySmem<D, BF16IN, NT, X65>);
-  static constexpr int WG_PER_CU0 = kLdsBytes / LDS < 1 ? 1 : kLdsBytes / LDS;
-  static constexpr int WG_PER_CU = WG_PER_CU0 < 2 ? WG_PER_CU0 : 2;
+  static_assert(LDS <= kLdsBytes, "a workgroup's LDS fits a CU");
+  static constexpr int WG_PER_CU = kLdsBytes / LDS < 2 ? 1 : 2;
   // A workgroup's waves are dealt over the CU's four SIMDs, so the register budget must let
   // every SIMD hold ceil(WAVES / 4) waves of each resident workgroup.
-  static constexpr int WPEU = WG_PER_CU * ((WAVES + 3) / 4);
+  static constexpr int WPEU = WG_PER_CU * ((G::WAVES + 3) / 4);
 };
 
 // Rows live in LDS unpadded with their 16-byte chunks XOR-swizzled by the row index, so that
@@ -154,11 +166,17 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Product of an exactly split fp32 operand (three parts) with a bf16 operand (exact).
+// Product of a bf16 operand (exact) with an exactly split fp32 operand (three parts), the
+// split operand second (B) or first (A).
 __device__ __forceinline__ f32x4 mfma_x3(bf16x8 a, const bf16x8 &bh, const bf16x8 &bm, const bf16x8 &bl, f32x4 c) {
   c = mfma_bf16(a, bl, c);
   c = mfma_bf16(a, bm, c);
   return mfma_bf16(a, bh, c);
+}
+__device__ __forceinline__ f32x4 mfma_x3t(const bf16x8 &ah, const bf16x8 &am, const bf16x8 &al, bf16x8 b, f32x4 c) {
+  c = mfma_bf16(al, b, c);
+  c = mfma_bf16(am, b, c);
+  return mfma_bf16(ah, b, c);
 }
 // Product of two exactly split fp32 operands: the six part products down to 2^-16 relative.
 __device__ __forceinline__ f32x4 mfma_x6(const bf16x8 &ah, const bf16x8 &am, const bf16x8 &al, const bf16x8 &bh,
@@ -187,54 +205,6 @@ __device__ __forceinline__ void row_frag(const typename InT<BF16IN>::T *rows, in
   }
 }
 
-// Four consecutive elements of one LDS row as fp32 (col is a multiple of 4).
-template <int D, bool BF16IN>
-__device__ __forceinline__ void row4(const typename InT<BF16IN>::T *rows, int r, int col, float *x) {
-  if constexpr (BF16IN) {
-    const uint2 w = *reinterpret_cast<const uint2 *>(rows + swz<D, 8>(r, col));
-    x[0] = __uint_as_float(w.x << 16);
-    x[1] = __uint_as_float(w.x & 0xffff0000u);
-    x[2] = __uint_as_float(w.y << 16);
-    x[3] = __uint_as_float(w.y & 0xffff0000u);
-  } else {
-    const float4 a = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  }
-}
-
-// Eight consecutive elements of one LDS row as fp32 (col is a multiple of 8).
-template <int D, bool BF16IN>
-__device__ __forceinline__ void row8(const typename InT<BF16IN>::T *rows, int r, int col, float *x) {
-  if constexpr (BF16IN) {
-    const uint4 w = *reinterpret_cast<const uint4 *>(rows + swz<D, 8>(r, col));
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(ww[i] << 16);
-      x[2 * i + 1] = __uint_as_float(ww[i] & 0xffff0000u);
-    }
-  } else {
-    const float4 a = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col));
-    const float4 b = *reinterpret_cast<const float4 *>(rows + swz<D, 4>(r, col + 4));
-    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-  }
-}
-
-// Position of W1[t][s] in the dense rows: 16-byte chunks XOR-swizzled by the row.
-template <int SPD, int CHM>
-__device__ __forceinline__ int wpos(int t, int sc) {
-  return t * SPD + ((((sc >> 2) ^ t) & CHM) << 2) + (sc & 3);
-}
-// The eight W1 values of one A fragment of the sum: columns c..c+3 and c+16..c+19 of row t.
-template <int SPD, int CHM>
-__device__ __forceinline__ void row8w(const float *dw, int t, int c, float *x) {
-  const float4 a = *reinterpret_cast<const float4 *>(dw + wpos<SPD, CHM>(t, c));
-  const float4 b = *reinterpret_cast<const float4 *>(dw + wpos<SPD, CHM>(t, c + 16));
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-
 __device__ __forceinline__ int wave_max_i32(int x) {
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x121, 0xf, 0xf, false));  // row_ror 1
   x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x122, 0xf, 0xf, false));  // row_ror 2
@@ -260,11 +230,11 @@ __device__ __forceinline__ void drain(const f32x4 &acc) {
   asm volatile("" ::"s"(s));
 }
 
-// The tree waves meet here: each finishes its own memory work (loads into LDS included),
-// counts itself in, and waits for the others.  The wait is bounded; a wave that
-// gives up marks the request bad (NaN outputs) instead of hanging.
+// The tree waves meet here: each makes its own LDS writes visible, counts itself in, and
+// waits for the others.  The wait is bounded; a wave that gives up marks the request bad (NaN
+// outputs) instead of hanging.
 __device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int lane) {
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   int spins = 0;
   while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
@@ -276,35 +246,20 @@ __device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int la
   }
 }
 
-// Output rows of one head, staged in LDS with swizzled 16-byte chunks, stored as whole rows
-// (16-byte pieces, consecutive lanes along a row) by every wave of the workgroup.
-template <int D>
-__device__ __forceinline__ void store_rows(const VerifyParams &p, const unsigned char *stage, int n,
-                                           size_t rowbase, int h, int tid, int nth) {
-  const int oes = p.out_bf16 ? 2 : 4;
-  const int cpr = D * oes / 16;  // 16-byte chunks per row: a power of two
-  const unsigned ostride = (unsigned)(p.H * D * oes);
-  char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
-  const int orange = ((n - 1) * p.H * D + D) * oes;
-  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
-  for (int c = tid; c < n * cpr; c += nth) {
-    const int r = c / cpr, lc = c % cpr;
-    const u32x4 x = *reinterpret_cast<const u32x4 *>(stage + 16 * (r * cpr + (lc ^ (r & (cpr - 1)))));
-    __builtin_amdgcn_raw_buffer_store_b128(x, ro, (int)((unsigned)r * ostride + 16u * lc), 0, 0);
-  }
-}
-
 template <int D, bool BF16IN, int NT, bool X65>
-__global__ __launch_bounds__((VerifyShape<D, BF16IN, NT, X65>::NTH), (VerifyShape<D, BF16IN, NT, X65>::WPEU))
+__global__ __launch_bounds__((VerifyGeom<D, BF16IN, NT, X65>::NTH), (VerifyShape<D, BF16IN, NT, X65>::WPEU))
 void verify_kernel(VerifyParams p) {
+  typedef VerifyGeom<D, BF16IN, NT, X65> G;
   typedef VerifySmem<D, BF16IN, NT, X65> SM;
-  typedef typename SM::T T;
-  constexpr int RM = SM::RM;
+  typedef typename G::T T;
+  constexpr int RM = G::RM, ROWB = G::ROWB, NTH = G::NTH;
   constexpr int CH = 16 / (int)sizeof(T), CPR = D / CH;
   constexpr int KS = D / 32;               // MFMA k-steps over d_k
-  constexpr int NPW = D / 16;              // product waves
-  constexpr int QMAX = SM::ROWB / 1024;    // 1 KiB row chunks per matrix
+  constexpr int NPW = G::NPW;              // product waves
+  constexpr int QMAX = ROWB / 1024;        // 1 KiB row chunks per matrix
   constexpr int NTG = NT + (X65 ? 1 : 0);  // Gram node tiles (the 65th row has one of its own)
+  constexpr int SPD = G::SPD, CPW = G::CPW;
+  static_assert(2 * ROWB >= RM * D * 4, "fp32 output rows fit over the q and k rows");
   __shared__ SM s;
 
   const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, l16 = lane & 15;
@@ -317,26 +272,84 @@ void verify_kernel(VerifyParams p) {
   const int n = nn_c[b];
   if (n < 1 || n > p.R) return;  // no output for a request with an impossible node count
   const int nl = n - 1;
-  const int ntl = (min(n, 16 * NT) + 15) / 16;  // MFMA row tiles in use
-  const bool row64 = X65 && n == 65;            // the 65th row, on VALU
+  const int ntl = (imin(n, 16 * NT) + 15) / 16;  // MFMA row tiles in use
+  const bool row64 = X65 && n == 65;             // the 65th row
   const size_t rowbase = (size_t)lb * p.R;
   const size_t rstride = (size_t)p.H * D;  // elements between consecutive slots of one head
-  const int nb = (int)((nl * rstride + D) * sizeof(T));  // byte range of this head's used rows
-  const T *qrow = reinterpret_cast<const T *>(s.qk);
-  const T *krow = reinterpret_cast<const T *>(s.qk + SM::ROWB);
-  const T *vrow = reinterpret_cast<const T *>(s.vr);
-  static_assert(SM::QKB >= RM * D * 4, "fp32 output rows fit over the q and k rows");
-  // Output rows are staged over the v rows when they fit there, else over the q and k rows; after
-  // barrier (3) either way (the last v reads come before it).
-  const bool stage_in_v = (p.out_bf16 ? 2 : 4) <= (int)sizeof(T);
-  unsigned char *ostage = stage_in_v ? s.vr : s.qk;
+  const T *qrow = reinterpret_cast<const T *>(s.r0);
+  const T *krow = reinterpret_cast<const T *>(s.r0 + ROWB);
+  const T *vrow = reinterpret_cast<const T *>(s.r1);
+  uint16_t *pl = G::PL_R0 ? reinterpret_cast<uint16_t *>(s.r0) : s.plx;  // dense W1 part 0; parts 1, 2 follow
+  // Output rows are staged over the v rows when they fit there, else over the q and k rows once
+  // the dense W1 parts are read.
+  const bool stage_v = (p.out_bf16 ? 2 : 4) <= (int)sizeof(T);
+  unsigned char *stg = stage_v ? s.r1 : s.r0;
+
+  // ---- the dense W1 rows as three bf16 parts, by every wave once the compact rows are solved:
+  // item (t, mb, g) is row t's slots 32 mb + 16 h + 4 g + i, one 16-byte chunk per part;
+  // W1[t][s] is the compact entry at s's depth on t's path, or zero.  The 65th row's entries
+  // (s < 64) go to w64 in fp32.
+  auto fill = [&]() {
+    constexpr int IPR = G::NB * 4;  // items per row
+    constexpr int NIT = G::PR * IPR + (X65 ? 64 : 0);
+    for (int it = tid; it < NIT; it += NTH) {
+      if (it < G::PR * IPR) {
+        const int t = it / IPR, mb = (it % IPR) >> 2, g = it & 3;
+        const unsigned long long aset = t < n ? ((s.mask[t] << 1) | 1ull) : 0ull;
+        // the block's 32 slot flags, and t's ancestors-or-self in the blocks below it
+        const uint32_t wb = (uint32_t)(aset >> (32 * mb));
+        const int below = mb ? __popc((uint32_t)aset) : 0;
+        float xv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int q = 16 * (e >> 2) + 4 * g + (e & 3);            // slot 32 mb + q
+          const int d = below + __popc(wb & ((2u << q) - 1u)) - 1;  // its depth on t's path
+          xv[e] = ((wb >> q) & 1u) ? s.cw[t * kAR + imin(max(d, 0), kAR - 1)] : 0.f;
+        }
+        bf16x8 xh, xm, xl;
+        split3(xv, xh, xm, xl);
+        const int off = t * SPD + 8 * ((4 * mb + g) ^ (t & (CPW - 1)));
+        *reinterpret_cast<uint4 *>(pl + off) = __builtin_bit_cast(uint4, xh);
+        *reinterpret_cast<uint4 *>(pl + G::PR * SPD + off) = __builtin_bit_cast(uint4, xm);
+        *reinterpret_cast<uint4 *>(pl + 2 * G::PR * SPD + off) = __builtin_bit_cast(uint4, xl);
+      } else if (row64) {
+        const int sl = it - G::PR * IPR;  // W1[64][sl]
+        const unsigned long long aset = (s.mask[64] << 1) | 1ull;
+        const int d = imin((int)__popcll(aset & ((2ull << sl) - 1ull)) - 1, kAR - 1);
+        s.w64[sl] = ((aset >> sl) & 1ull) ? s.cw[64 * kAR + d] : 0.f;
+      }
+    }
+  };
+
+  // ---- the staged rows to HBM by every wave: whole rows, 16-byte pieces, consecutive lanes
+  // along a row; a fixed number of pieces per lane, the ones past the rows in use falling
+  // outside the buffer range (the hardware drops them) -------------------------------------
+  auto store_rows = [&]() {
+    const int oes = p.out_bf16 ? 2 : 4;
+    const int lcpr = p.out_bf16 ? (D == 128 ? 4 : 3) : (D == 128 ? 5 : 4);  // log2 chunks per row
+    const int cpr = 1 << lcpr;
+    const unsigned ostride = (unsigned)(p.H * D * oes);
+    char *obase = static_cast<char *>(p.o) + (rowbase * p.H + h) * (size_t)D * oes;
+    const int orange = ((n - 1) * p.H * D + D) * oes;
+    const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(obase, 0, orange, 0x00020000);
+    constexpr int PIECES = (RM * D * 4 / 16 + NTH - 1) / NTH;  // enough for fp32 rows
+    const int nch = n * cpr;
+#pragma unroll
+    for (int x = 0; x < PIECES; ++x) {
+      const int c = tid + NTH * x;
+      const int r = imin(c >> lcpr, RM - 1), lc = c & (cpr - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stg + 16 * (r * cpr + (lc ^ (r & (cpr - 1)))));
+      const int off = c < nch ? (int)((unsigned)r * ostride + 16u * lc) : orange;
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, off, 0, 0);
+    }
+  };
 
   if (wave < NPW) {
     // ================================ product waves ==================================
     // The tree waves issue their row loads before this barrier, so they are queued ahead of
     // the state loads below.
     wg_barrier();  // (0)
-    const int j = 16 * wave + l16;  // this lane's value channel
+    const int j = 16 * wave + l16;  // this lane's value channel (K pass and the 65th row)
     // State fragments in the [d_k][d_v] layout: lane (g, c) gathers S0[32 ks + 8 g + e][j],
     // 16 consecutive channels (64 bytes) per row and instruction.  The fragment of the next
     // k-step is in flight while the current one is split and multiplied (register budget of
@@ -361,6 +374,8 @@ void verify_kernel(VerifyParams p) {
       constexpr int NTU = decltype(ntu_c)::value;
       constexpr bool R65 = X65 && NTU == NT;  // only a full set of tiles can have a 65th row
       const bool r64 = R65 && row64;
+      // ak[mt]: A_k rows 16 mt + 4 g + r, channel j (lane (g, c) = (g, j - 16 w)).
+      // aq[mt]: A_q transposed, lane (g, c) holding node 16 mt + c, channels 16 w + 4 g + r.
       f32x4 ak[NTU], aq[NTU];
 #pragma unroll
       for (int mt = 0; mt < NTU; ++mt) {
@@ -383,7 +398,6 @@ void verify_kernel(VerifyParams p) {
         asm volatile("" : "+v"(sh), "+v"(sm), "+v"(sl)::"memory");
         if (ks + KW < KS) gather(ks + KW);
         __builtin_amdgcn_sched_barrier(0);
-        // rows 16 mt + 0..15 of K and of Q times this k-step's state slice
 #pragma unroll
         for (int mt = 0; mt < NTU; ++mt) {
           bf16x8 xh, xm, xl;
@@ -392,8 +406,8 @@ void verify_kernel(VerifyParams p) {
           else ak[mt] = mfma_x6(xh, xm, xl, sh, sm, sl, ak[mt]);
           if constexpr (!BF16IN) drain(ak[mt]);  // fp32 row fragments are split on VALU
           row_frag<D, BF16IN>(qrow, 16 * mt + l16, 32 * ks + 8 * g4, xh, xm, xl);
-          if constexpr (BF16IN) aq[mt] = mfma_x3(xh, sh, sm, sl, aq[mt]);
-          else aq[mt] = mfma_x6(xh, xm, xl, sh, sm, sl, aq[mt]);
+          if constexpr (BF16IN) aq[mt] = mfma_x3t(sh, sm, sl, xh, aq[mt]);
+          else aq[mt] = mfma_x6(sh, sm, sl, xh, xm, xl, aq[mt]);
           if constexpr (!BF16IN) drain(aq[mt]);
         }
         if constexpr (R65) {
@@ -411,32 +425,35 @@ void verify_kernel(VerifyParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      wg_barrier();  // (2) nobody reads q or k rows any more; the dense W1 rows are ready
+      wg_barrier();  // (2) nobody reads q or k rows any more; the compact W1 rows are solved
       const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
       // ---- o[t] = g_t A_q[t] + sum_s W1[t][s] U[s] on MFMA, U[s] = v[s] - g_s A_k[s] ---------
-      // (the two sums of the tree form in one: W1[t][s] U[s] = W1[t][s] v[s] - g_t Y[t, s] A_k[s],
-      // as W1 = (g_t / g_s) Y).  U takes A_k's place in this lane's registers (rows >= n zero).
-      // 16x16x32 products over 32-slot blocks, the contraction index k = 8 g + e of lane (g, c)
-      // standing for slot s = 32 mb + 16 (e / 4) + 4 g + e % 4: the B operand of lane (g, c) is
-      // then its own U rows of tiles 2 mb and 2 mb + 1 (C layout, rows 4 g + 0..3) split in three,
-      // and the A operand holds W1[16 mt + c][s(8 g + e)] from the dense rows.  The 65th row goes
-      // on VALU.
-      constexpr int SPD = SM::SPD, CHM = SM::CHM;
-      const float *dw = s.dw;
+      // U takes A_k's place in this lane's registers (rows >= n zero); then this wave's share of
+      // the dense W1 rows.
       f32x4 oc[NTU];
 #pragma unroll
       for (int mt = 0; mt < NTU; ++mt) {
+        const float gq = s.gamma[16 * mt + l16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
+          oc[mt][r] = gq * aq[mt][r];  // rows >= n are never stored
           const int t = 16 * mt + 4 * g4 + r;
-          const float gt = s.gamma[t];
-          oc[mt][r] = gt * aq[mt][r];  // rows >= n are never stored
-          ak[mt][r] = t < n ? to_f32(vrow[swz<D, CH>(t, j)]) - gt * ak[mt][r] : 0.f;
+          ak[mt][r] = t < n ? to_f32(vrow[swz<D, CH>(t, j)]) - s.gamma[t] * ak[mt][r] : 0.f;
         }
       }
       // the 65th row: A_k[64] and A_q[64] sit in lanes (0, c) of a65
       const float u64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) - s.gamma[64] * a65[0] : 0.f;
+      fill();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dense W1 items are written
+      wg_barrier();  // (3) the dense W1 rows are ready; nobody reads the v rows any more
+
+      // Transposed, o^T = U^T W1^T: 16x16x32 products over 32-slot blocks, the contraction
+      // index k = 8 g + e of lane (g, c) standing for slot s = 32 mb + 16 (e / 4) + 4 g + e % 4.
+      // The A operand of lane (g, c) is then its own U rows of tiles 2 mb and 2 mb + 1 (the K
+      // pass's layout, rows 4 g + 0..3) split in three, and the B operand, W1[16 mt + c] at
+      // those slots, is one 16-byte chunk of each dense part.  The result has A_q's transposed
+      // layout.  The 65th row goes on VALU.
       float p64 = 0.f;  // this lane's share of row 64's sum over s < 64
       constexpr int NBU = (NTU + 1) / 2;  // 32-slot blocks in use
 #pragma unroll
@@ -444,23 +461,26 @@ void verify_kernel(VerifyParams p) {
         bf16x8 uh, um, ul;
         float ua[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ua[e] = (2 * mb + (e >> 2) < NTU) ? ak[imin(2 * mb + (e >> 2), NTU - 1)][e & 3] : 0.f;
+        for (int e = 0; e < 8; ++e)
+          ua[e] = (2 * mb + (e >> 2) < NTU) ? ak[imin(2 * mb + (e >> 2), NTU - 1)][e & 3] : 0.f;
         split3(ua, uh, um, ul);
         if (R65 && r64) {
-          float wr[8];
-          row8w<SPD, CHM>(dw, 64, 32 * mb + 4 * g4, wr);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p64 = fmaf(wr[e], ua[e], p64);
+          const float4 wa = *reinterpret_cast<const float4 *>(&s.w64[32 * mb + 4 * g4]);
+          const float4 wb = *reinterpret_cast<const float4 *>(&s.w64[32 * mb + 16 + 4 * g4]);
+          p64 = fmaf(wa.x, ua[0], p64); p64 = fmaf(wa.y, ua[1], p64);
+          p64 = fmaf(wa.z, ua[2], p64); p64 = fmaf(wa.w, ua[3], p64);
+          p64 = fmaf(wb.x, ua[4], p64); p64 = fmaf(wb.y, ua[5], p64);
+          p64 = fmaf(wb.z, ua[6], p64); p64 = fmaf(wb.w, ua[7], p64);
         }
 #pragma unroll
         for (int mt = 2 * mb; mt < NTU; ++mt) {
-          float wa[8];
-          row8w<SPD, CHM>(dw, 16 * mt + l16, 32 * mb + 4 * g4, wa);
-          bf16x8 wh, wm, wl;
-          split3(wa, wh, wm, wl);
+          const int t = 16 * mt + l16;
+          const int off = t * SPD + 8 * ((4 * mb + g4) ^ (t & (CPW - 1)));
+          const bf16x8 wh = frag16(pl + off), wm = frag16(pl + G::PR * SPD + off);
+          const bf16x8 wl = frag16(pl + 2 * G::PR * SPD + off);
           __builtin_amdgcn_sched_barrier(0);
-          oc[mt] = mfma_x6(wh, wm, wl, uh, um, ul, oc[mt]);
-          drain(oc[mt]);  // these products have completed before the next split overwrites w*
+          oc[mt] = mfma_x6(uh, um, ul, wh, wm, wl, oc[mt]);
+          drain(oc[mt]);  // these products have completed before the next loads overwrite w*
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -477,33 +497,47 @@ void verify_kernel(VerifyParams p) {
                                                        __builtin_nanf("")};
         o64 = __builtin_nanf("");
       }
-      wg_barrier();  // (3) nobody reads the v rows any more
+      if (!stage_v) wg_barrier();  // (3b) the dense W1 rows are read before the outputs go over them
 
-      // ---- output rows, staged over the v rows (or the q and k rows for wider outputs) -----
-      auto stage = [&](int t, float x) {
-        if (p.out_bf16)
-          reinterpret_cast<uint16_t *>(ostage)[swz<D, 8>(t, j)] = __builtin_bit_cast(uint16_t, (__bf16)x);
-        else
-          reinterpret_cast<float *>(ostage)[swz<D, 4>(t, j)] = x;
-      };
+      // ---- output rows: lane (g, c) holds node 16 mt + c at channels 16 w + 4 g + 0..3, one
+      // 8-byte (bf16) or 16-byte (fp32) piece of a row whose 16-byte chunks are swizzled by the row
 #pragma unroll
       for (int mt = 0; mt < NTU; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = 16 * mt + 4 * g4 + r;
-          if (t < n) stage(t, oc[mt][r]);
+        const int t = 16 * mt + l16;
+        if (t < n) {
+          if (p.out_bf16) {
+            constexpr int OC = D * 2 / 16;
+            const int lc = 2 * wave + (g4 >> 1);
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            const bf16x4 o4 = __builtin_convertvector(oc[mt], bf16x4);
+            *reinterpret_cast<uint2 *>(stg + 16 * (t * OC + (lc ^ (t & (OC - 1)))) + 8 * (g4 & 1)) =
+                __builtin_bit_cast(uint2, o4);
+          } else {
+            constexpr int OC = D * 4 / 16;
+            const int lc = 4 * wave + g4;
+            *reinterpret_cast<f32x4 *>(stg + 16 * (t * OC + (lc ^ (t & (OC - 1))))) = oc[mt];
+          }
         }
       }
-      if (R65 && r64 && g4 == 0) stage(64, o64);
+      if (R65 && r64 && g4 == 0) {
+        if (p.out_bf16) {
+          constexpr int OC = D * 2 / 16;
+          *reinterpret_cast<uint16_t *>(stg + 16 * (64 * OC + (j >> 3)) + 2 * (j & 7)) =
+              __builtin_bit_cast(uint16_t, (__bf16)o64);
+        } else {
+          constexpr int OC = D * 4 / 16;
+          *reinterpret_cast<float *>(stg + 16 * (64 * OC + (j >> 2)) + 4 * (j & 3)) = o64;
+        }
+      }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's output rows are staged
-      wg_barrier();        // (4) every output row is staged
+      wg_barrier();                        // (4) every output row is staged
     };
     static_assert(NT >= 1 && NT <= 4, "one to four row tiles");
     if (ntl == NT) product_phase(std::integral_constant<int, NT>{});
     else if (ntl == 1) product_phase(std::integral_constant<int, 1>{});
     else if (ntl == 2) product_phase(std::integral_constant<int, (NT > 2 ? 2 : 1)>{});
     else product_phase(std::integral_constant<int, (NT > 3 ? 3 : 1)>{});
-    store_rows<D>(p, ostage, n, rowbase, h, tid, 64 * (NPW + kTreeWaves));
+    store_rows();
     return;
   }
 
@@ -515,8 +549,8 @@ void verify_kernel(VerifyParams p) {
   // write of a wave waits for that wave's own loads into LDS).  tw 1..3 clear the compact
   // Gram rows first, for the same reason, then load the q, k and v rows.
   const int t_me = lane + 1;
-  const int tn = min(t_me, nl);
-  const int ts = min(lane, nl);
+  const int tn = imin(t_me, nl);
+  const int ts = imin(lane, nl);
   unsigned long long w_mask = 0ull, my_mask = 0ull;
   int w_par = 0;
   uint32_t w_a0 = 0u, w_b0 = 0u, w_a1 = 0u, w_b1 = 0u;  // gate bits
@@ -556,6 +590,7 @@ void verify_kernel(VerifyParams p) {
     // 64 qi + l and fetches the logical chunk that the swizzle places there.  Rows past the
     // node count fetch row n-1 (never used).
     const size_t hoff = (rowbase * p.H + h) * (size_t)D;
+    const int nb = (int)((nl * rstride + D) * sizeof(T));  // byte range of this head's used rows
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(static_cast<const T *>(p.q) + hoff), 0, nb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -568,8 +603,8 @@ void verify_kernel(VerifyParams p) {
       if (c < 3 * QMAX) {
         const int mat = c / QMAX, qi = c % QMAX;
         const int pc = 64 * qi + lane, r = pc / CPR, cc = (pc % CPR) ^ (r & (CPR - 1));
-        const unsigned off = (unsigned)((min(r, nl) * (int)rstride + cc * CH) * (int)sizeof(T));
-        unsigned char *dst = (mat == 2 ? s.vr : s.qk + mat * SM::ROWB) + 1024 * qi;
+        const unsigned off = (unsigned)((imin(r, nl) * (int)rstride + cc * CH) * (int)sizeof(T));
+        unsigned char *dst = (mat == 2 ? s.r1 : s.r0 + mat * ROWB) + 1024 * qi;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(mat == 0 ? rq : (mat == 1 ? rk : rv), (lds_void_t *)dst, 16, off,
                                                  0, 0, 0);
       }
@@ -595,13 +630,13 @@ void verify_kernel(VerifyParams p) {
     const unsigned long long m = w_mask;
     d_me = __popcll(m);
     // the parent's mask is the node mask held by lane parent - 1 (the root's mask is zero)
-    const int pl = min(max(w_par - 1, 0), 63);
-    const uint32_t pm_lo = (uint32_t)__builtin_amdgcn_ds_bpermute(pl << 2, (int)(uint32_t)m);
-    const uint32_t pm_hi = (uint32_t)__builtin_amdgcn_ds_bpermute(pl << 2, (int)(uint32_t)(m >> 32));
+    const int pl_ = imin(max(w_par - 1, 0), 63);
+    const uint32_t pm_lo = (uint32_t)__builtin_amdgcn_ds_bpermute(pl_ << 2, (int)(uint32_t)m);
+    const uint32_t pm_hi = (uint32_t)__builtin_amdgcn_ds_bpermute(pl_ << 2, (int)(uint32_t)(m >> 32));
     const unsigned long long pm = w_par == 0 ? 0ull : (((unsigned long long)pm_hi << 32) | pm_lo);
     const bool ok = d_me <= kMaxP && w_par >= 0 && w_par < t_me && m == (pm | (1ull << (t_me - 1)));
     if (tv && !ok) s.bad = 1;
-    d_me = min(d_me, kMaxP);
+    d_me = imin(d_me, kMaxP);
     float bet[kMaxAnc], alp[kMaxAnc];  // b and a of the ancestor at depth e
     alp[0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a0), 0));
     bet[0] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(b0), 0));
@@ -653,15 +688,15 @@ void verify_kernel(VerifyParams p) {
 #pragma unroll
     for (int nt = 0; nt <= mt; ++nt) {
       if ((mt * (mt + 1) / 2 + nt) % kTreeWaves != kTreeWaves - 1 - tw || mt >= ntg) continue;
-      const int tme = 16 * mt + l16, ra = min(tme, nl);
-      const int rb = 16 * nt + l16;
+      const int tme = 16 * mt + l16, ra = imin(tme, nl);
+      const int rbr = 16 * nt + l16;
       f32x4 gk4 = {0.f, 0.f, 0.f, 0.f}, gq4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         bf16x8 aqh, aqm, aql, akh, akm, akl, bh, bm, bl;
         row_frag<D, BF16IN>(qrow, tme, 32 * ks + 8 * g4, aqh, aqm, aql);
         row_frag<D, BF16IN>(krow, tme, 32 * ks + 8 * g4, akh, akm, akl);
-        row_frag<D, BF16IN>(krow, rb, 32 * ks + 8 * g4, bh, bm, bl);
+        row_frag<D, BF16IN>(krow, rbr, 32 * ks + 8 * g4, bh, bm, bl);
         if constexpr (BF16IN) {
           gk4 = mfma_bf16(bh, akh, gk4);
           gq4 = mfma_bf16(bh, aqh, gq4);
@@ -702,7 +737,7 @@ void verify_kernel(VerifyParams p) {
   }
   tree_sync(&s.sync, &s.bad, kTreeWaves, lane);  // the compact Gram rows are complete
 
-  // ---- tw 0: path solve, one lane per node, then the node's coefficient rows -------------
+  // ---- tw 0: path solve, one lane per node, then the node's compact W1 row ---------------
   // Writes -g_t Y[t, e] over the k.k entries and W1[t, e] over the q.k entries: every read of
   // them (this wave's, in program order) comes first.
   if (tw == 0) {
@@ -753,40 +788,21 @@ void verify_kernel(VerifyParams p) {
         if (e <= d_me) s.cw[t * kAR + e] = s.cwl[e][lane] * z[e];  // W1[t, e]
     }
     if (lane == 0) s.cw[0] = s.beta[0] * z_root;  // the root: W1[0, 0] = b_0 (q_0 . k_0)
-    // the compact k.k rows are read for the last time above: zero their part of the dense rows
-    for (int i = lane; i < RM * kAR / 4; i += 64) reinterpret_cast<uint4 *>(s.dw)[i] = make_uint4(0u, 0u, 0u, 0u);
-  } else {
-    // the part of the dense rows past the compact k.k rows
-    for (int i = RM * kAR / 4 + 64 * (tw - 1) + lane; i < RM * SM::SPD / 4; i += 64 * (kTreeWaves - 1))
-      reinterpret_cast<uint4 *>(s.dw)[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the dense rows are zero, the W1 rows written
-  if (tw == 0) {
-    // each node's W1 entries at its ancestors' slots
-    constexpr int SPD = SM::SPD, CHM = SM::CHM;
-    if (t_me < n) {
-#pragma unroll
-      for (int e = 0; e <= kMaxP; ++e) {
-        if (e <= d_me) {
-          const int a = (int)((ancw[e >> 2] >> (8 * (e & 3))) & 0xffu);  // slot at depth e
-          // slot 64 (node 64 itself) has no column: its term is added on VALU
-          if (a < SPD) s.dw[wpos<SPD, CHM>(t_me, a)] = s.cw[t_me * kAR + e];
-        }
-      }
-    }
-    if (lane == 0) s.dw[0] = s.cw[0];  // the root
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the dense W1 rows are written
-  wg_barrier();        // (2) the dense W1 rows are ready
-  wg_barrier();        // (3) nobody reads the v rows any more
-  wg_barrier();        // (4) every output row is staged
-  store_rows<D>(p, ostage, n, rowbase, h, tid, 64 * (NPW + kTreeWaves));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the compact W1 rows are written
+  wg_barrier();  // (2) the compact W1 rows are solved; nobody reads q or k rows any more
+  fill();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dense W1 items are written
+  wg_barrier();  // (3) the dense W1 rows are ready
+  if (!stage_v) wg_barrier();  // (3b) the dense W1 rows are read
+  wg_barrier();  // (4) every output row is staged
+  store_rows();
 }
 
 template <int D, bool BF16IN, int NT, bool X65>
 hipError_t launch_one(const VerifyParams &p, hipStream_t stream) {
   const unsigned units = (unsigned)(p.L * p.B * p.H);
-  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, X65>), dim3(units), dim3(VerifyShape<D, BF16IN, NT, X65>::NTH),
+  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, X65>), dim3(units), dim3(VerifyGeom<D, BF16IN, NT, X65>::NTH),
                      0, stream, p);
   return hipGetLastError();
 }
