@@ -429,15 +429,20 @@ def main():
     t_commit = float(np.mean([c.elapsed_time(d_) for _, _, c, d_ in ev])) * 1e3
 
     # the verify kernel's mean duration for the roofline: the same launches back to back on the
-    # launch stream (rotating input sets), two events around all of them, so that the per-launch
-    # figure carries no event or neighbouring-kernel overhead
+    # launch stream (rotating input sets), two events around each batch of them, so that the
+    # per-launch figure carries no event or neighbouring-kernel overhead; the median over five
+    # batches, so that one stray delay does not move it
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        sets[(args.warmup + i) % nsets]["p_verify"]()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_verify = e0.elapsed_time(e1) * 1e3 / args.steps
+    batch = max(20, args.steps)
+    b2b = []
+    for _ in range(5):
+        e0.record(stream)
+        for i in range(batch):
+            sets[(args.warmup + i) % nsets]["p_verify"]()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b2b.append(e0.elapsed_time(e1) * 1e3 / batch)
+    t_verify = float(np.median(b2b))
 
     # the verify and the commit one launch at a time, each between its own pair of events, over
     # `reps` launches (rotating input sets): medians
@@ -507,7 +512,8 @@ def main():
                      "kernel's own time is verify_nodes_per_s"),
         "verify_nodes_per_s": float(np.median(vnodes / (vus * 1e-6))),
         "verify_us": {"median": vmed, "p10": float(np.percentile(vus, 10)), "p90": float(np.percentile(vus, 90)),
-                      "reps": reps, "mean_back_to_back": t_verify, "mean_in_step": t_verify_step},
+                      "reps": reps, "mean_back_to_back": t_verify, "back_to_back_batches": [round(x, 2) for x in b2b],
+                      "mean_in_step": t_verify_step},
         "commit_us": {"median": float(np.median(cus)), "reps": reps,
                       "what": "acceptance + accepted-path commit (one launch), after a build"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -230,11 +230,11 @@ __device__ __forceinline__ void drain(const f32x4 &acc) {
   asm volatile("" ::"s"(s));
 }
 
-// The tree waves meet here: each makes its own LDS writes visible, counts itself in, and
-// waits for the others.  The wait is bounded; a wave that gives up marks the request bad (NaN
-// outputs) instead of hanging.
+// The tree waves meet here: each finishes its own memory work (loads into LDS included),
+// counts itself in, and waits for the others.  The wait is bounded; a wave that gives up marks
+// the request bad (NaN outputs) instead of hanging.
 __device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int lane) {
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
   if (lane == 0) __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   int spins = 0;
   while (__hip_atomic_load(cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
@@ -259,6 +259,7 @@ void verify_kernel(VerifyParams p) {
   constexpr int QMAX = ROWB / 1024;        // 1 KiB row chunks per matrix
   constexpr int NTG = NT + (X65 ? 1 : 0);  // Gram node tiles (the 65th row has one of its own)
   constexpr int SPD = G::SPD, CPW = G::CPW;
+  constexpr int NC = kTreeWaves - 1;       // tree waves that load rows
   static_assert(2 * ROWB >= RM * D * 4, "fp32 output rows fit over the q and k rows");
   __shared__ SM s;
 
@@ -266,12 +267,13 @@ void verify_kernel(VerifyParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = blockIdx.x;  // (layer, request, head)
   const int h = u % p.H, lb = u / p.H, b = lb % p.B;
-  // n_nodes is read-only here: a scalar load
+  // n_nodes is read-only here: a scalar load.  The row and per-node loads do not wait for it:
+  // they cover all R slots of the request (slots past the node count are read, never used).
   const int32_t __attribute__((address_space(4))) *nn_c =
       (const int32_t __attribute__((address_space(4))) *)p.n_nodes;
   const int n = nn_c[b];
-  if (n < 1 || n > p.R) return;  // no output for a request with an impossible node count
-  const int nl = n - 1;
+  const bool valid = n >= 1 && n <= p.R;  // no output for a request with an impossible node count
+  const int nl = n - 1, rl = p.R - 1;
   const int ntl = (imin(n, 16 * NT) + 15) / 16;  // MFMA row tiles in use
   const bool row64 = X65 && n == 65;             // the 65th row
   const size_t rowbase = (size_t)lb * p.R;
@@ -285,40 +287,31 @@ void verify_kernel(VerifyParams p) {
   const bool stage_v = (p.out_bf16 ? 2 : 4) <= (int)sizeof(T);
   unsigned char *stg = stage_v ? s.r1 : s.r0;
 
-  // ---- the dense W1 rows as three bf16 parts, by every wave once the compact rows are solved:
-  // item (t, mb, g) is row t's slots 32 mb + 16 h + 4 g + i, one 16-byte chunk per part;
-  // W1[t][s] is the compact entry at s's depth on t's path, or zero.  The 65th row's entries
-  // (s < 64) go to w64 in fp32.
-  auto fill = [&]() {
-    constexpr int IPR = G::NB * 4;  // items per row
-    constexpr int NIT = G::PR * IPR + (X65 ? 64 : 0);
-    for (int it = tid; it < NIT; it += NTH) {
-      if (it < G::PR * IPR) {
-        const int t = it / IPR, mb = (it % IPR) >> 2, g = it & 3;
-        const unsigned long long aset = t < n ? ((s.mask[t] << 1) | 1ull) : 0ull;
-        // the block's 32 slot flags, and t's ancestors-or-self in the blocks below it
-        const uint32_t wb = (uint32_t)(aset >> (32 * mb));
-        const int below = mb ? __popc((uint32_t)aset) : 0;
-        float xv[8];
+  // ---- the dense W1 rows as three bf16 parts: item (t, mb, g) is row t's slots
+  // 32 mb + 16 h + 4 g + i, one 16-byte chunk per part; W1[t][s] is the compact entry at s's
+  // depth on t's path, or zero.  The tree waves compute their items once the compact rows are
+  // solved and write them over the q and k rows once those are dead.
+  constexpr int IPR = G::NB * 4;                       // items per row
+  constexpr int PIT = G::PR * IPR;                     // items
+  constexpr int PXN = (PIT + 64 * kTreeWaves - 1) / (64 * kTreeWaves);  // per tree lane
+  auto fill_item = [&](int it, bf16x8 &xh, bf16x8 &xm, bf16x8 &xl) {
+    const int t = it / IPR, mb = (it % IPR) >> 2, g = it & 3;
+    const unsigned long long aset = t < n ? ((s.mask[t] << 1) | 1ull) : 0ull;
+    // the block's 32 slot flags, and t's ancestors-or-self in the blocks below it
+    const uint32_t wb = (uint32_t)(aset >> (32 * mb));
+    const int below = mb ? __popc((uint32_t)aset) : 0;
+    float xv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int q = 16 * (e >> 2) + 4 * g + (e & 3);            // slot 32 mb + q
-          const int d = below + __popc(wb & ((2u << q) - 1u)) - 1;  // its depth on t's path
-          xv[e] = ((wb >> q) & 1u) ? s.cw[t * kAR + imin(max(d, 0), kAR - 1)] : 0.f;
-        }
-        bf16x8 xh, xm, xl;
-        split3(xv, xh, xm, xl);
-        const int off = t * SPD + 8 * ((4 * mb + g) ^ (t & (CPW - 1)));
-        *reinterpret_cast<uint4 *>(pl + off) = __builtin_bit_cast(uint4, xh);
-        *reinterpret_cast<uint4 *>(pl + G::PR * SPD + off) = __builtin_bit_cast(uint4, xm);
-        *reinterpret_cast<uint4 *>(pl + 2 * G::PR * SPD + off) = __builtin_bit_cast(uint4, xl);
-      } else if (row64) {
-        const int sl = it - G::PR * IPR;  // W1[64][sl]
-        const unsigned long long aset = (s.mask[64] << 1) | 1ull;
-        const int d = imin((int)__popcll(aset & ((2ull << sl) - 1ull)) - 1, kAR - 1);
-        s.w64[sl] = ((aset >> sl) & 1ull) ? s.cw[64 * kAR + d] : 0.f;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int q = 16 * (e >> 2) + 4 * g + (e & 3);            // slot 32 mb + q
+      const int d = below + __popc(wb & ((2u << q) - 1u)) - 1;  // its depth on t's path
+      xv[e] = ((wb >> q) & 1u) ? s.cw[t * kAR + imin(max(d, 0), kAR - 1)] : 0.f;
     }
+    split3(xv, xh, xm, xl);
+  };
+  auto fill_off = [&](int it) {
+    const int t = it / IPR, mb = (it % IPR) >> 2, g = it & 3;
+    return t * SPD + 8 * ((4 * mb + g) ^ (t & (CPW - 1)));
   };
 
   // ---- the staged rows to HBM by every wave: whole rows, 16-byte pieces, consecutive lanes
@@ -349,6 +342,7 @@ void verify_kernel(VerifyParams p) {
     // The tree waves issue their row loads before this barrier, so they are queued ahead of
     // the state loads below.
     wg_barrier();  // (0)
+    if (!valid) return;
     const int j = 16 * wave + l16;  // this lane's value channel (K pass and the 65th row)
     // State fragments in the [d_k][d_v] layout: lane (g, c) gathers S0[32 ks + 8 g + e][j],
     // 16 consecutive channels (64 bytes) per row and instruction.  The fragment of the next
@@ -429,7 +423,7 @@ void verify_kernel(VerifyParams p) {
       const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
 
       // ---- o[t] = g_t A_q[t] + sum_s W1[t][s] U[s] on MFMA, U[s] = v[s] - g_s A_k[s] ---------
-      // U takes A_k's place in this lane's registers (rows >= n zero); then this wave's share of
+      // U takes A_k's place in this lane's registers (rows >= n zero) while the tree waves write
       // the dense W1 rows.
       f32x4 oc[NTU];
 #pragma unroll
@@ -444,8 +438,6 @@ void verify_kernel(VerifyParams p) {
       }
       // the 65th row: A_k[64] and A_q[64] sit in lanes (0, c) of a65
       const float u64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) - s.gamma[64] * a65[0] : 0.f;
-      fill();
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dense W1 items are written
       wg_barrier();  // (3) the dense W1 rows are ready; nobody reads the v rows any more
 
       // Transposed, o^T = U^T W1^T: 16x16x32 products over 32-slot blocks, the contraction
@@ -549,8 +541,8 @@ void verify_kernel(VerifyParams p) {
   // write of a wave waits for that wave's own loads into LDS).  tw 1..3 clear the compact
   // Gram rows first, for the same reason, then load the q, k and v rows.
   const int t_me = lane + 1;
-  const int tn = imin(t_me, nl);
-  const int ts = imin(lane, nl);
+  const int tn = imin(t_me, rl);
+  const int ts = imin(lane, rl);
   unsigned long long w_mask = 0ull, my_mask = 0ull;
   int w_par = 0;
   uint32_t w_a0 = 0u, w_b0 = 0u, w_a1 = 0u, w_b1 = 0u;  // gate bits
@@ -576,7 +568,6 @@ void verify_kernel(VerifyParams p) {
     }
   } else {
     constexpr int NL = RM * kAR * 4 / 16;  // 16-byte pieces of each compact array
-    constexpr int NC = kTreeWaves - 1;
 #pragma unroll
     for (int x = 0; x < (NL + 64 * NC - 1) / (64 * NC); ++x) {
       const int i = (tw - 1) * 64 + lane + 64 * NC * x;
@@ -588,9 +579,9 @@ void verify_kernel(VerifyParams p) {
     // q, k and v rows straight into LDS, 1 KiB chunks dealt over tw 1..3: each wave
     // instruction fills 64 consecutive 16-byte chunks; lane l of chunk qi holds physical chunk
     // 64 qi + l and fetches the logical chunk that the swizzle places there.  Rows past the
-    // node count fetch row n-1 (never used).
+    // slot count fetch slot R-1 (never used).
     const size_t hoff = (rowbase * p.H + h) * (size_t)D;
-    const int nb = (int)((nl * rstride + D) * sizeof(T));  // byte range of this head's used rows
+    const int nb = (int)((rl * rstride + D) * sizeof(T));  // byte range of this head's slots
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(static_cast<const T *>(p.q) + hoff), 0, nb, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
@@ -603,7 +594,7 @@ void verify_kernel(VerifyParams p) {
       if (c < 3 * QMAX) {
         const int mat = c / QMAX, qi = c % QMAX;
         const int pc = 64 * qi + lane, r = pc / CPR, cc = (pc % CPR) ^ (r & (CPR - 1));
-        const unsigned off = (unsigned)((imin(r, nl) * (int)rstride + cc * CH) * (int)sizeof(T));
+        const unsigned off = (unsigned)((imin(r, rl) * (int)rstride + cc * CH) * (int)sizeof(T));
         unsigned char *dst = (mat == 2 ? s.r1 : s.r0 + mat * ROWB) + 1024 * qi;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(mat == 0 ? rq : (mat == 1 ? rk : rv), (lds_void_t *)dst, 16, off,
                                                  0, 0, 0);
@@ -613,6 +604,10 @@ void verify_kernel(VerifyParams p) {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the counter and the clears are written
   __builtin_amdgcn_sched_barrier(0);
   wg_barrier();  // (0) the product waves may queue their state loads
+  if (!valid) {
+    __builtin_amdgcn_s_waitcnt(0);  // loads into this workgroup's LDS land before it ends
+    return;
+  }
   // keep every use of tw 0's loaded values (and the wait for them) after the barrier
   asm volatile("" : "+v"(w_mask), "+v"(my_mask), "+v"(w_par), "+v"(w_a0), "+v"(w_b0), "+v"(w_a1), "+v"(w_b1));
 
@@ -789,10 +784,35 @@ void verify_kernel(VerifyParams p) {
     }
     if (lane == 0) s.cw[0] = s.beta[0] * z_root;  // the root: W1[0, 0] = b_0 (q_0 . k_0)
   }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the compact W1 rows are written
+  tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the compact W1 rows are written
+  const int tt = tid - 64 * NPW;
+  bf16x8 fh[PXN], fm[PXN], fl[PXN];
+#pragma unroll
+  for (int x = 0; x < PXN; ++x)
+    if (tt + 64 * kTreeWaves * x < PIT) fill_item(tt + 64 * kTreeWaves * x, fh[x], fm[x], fl[x]);
+  float f64v = 0.f;  // W1[64][lane] on tree wave 0
+  if constexpr (X65) {
+    if (tw == 0 && row64) {
+      const unsigned long long aset = (s.mask[64] << 1) | 1ull;
+      const int d = imin((int)__popcll(aset & ((2ull << lane) - 1ull)) - 1, kAR - 1);
+      f64v = ((aset >> lane) & 1ull) ? s.cw[64 * kAR + d] : 0.f;
+    }
+  }
   wg_barrier();  // (2) the compact W1 rows are solved; nobody reads q or k rows any more
-  fill();
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's dense W1 items are written
+#pragma unroll
+  for (int x = 0; x < PXN; ++x) {
+    const int it = tt + 64 * kTreeWaves * x;
+    if (it < PIT) {
+      const int off = fill_off(it);
+      *reinterpret_cast<uint4 *>(pl + off) = __builtin_bit_cast(uint4, fh[x]);
+      *reinterpret_cast<uint4 *>(pl + G::PR * SPD + off) = __builtin_bit_cast(uint4, fm[x]);
+      *reinterpret_cast<uint4 *>(pl + 2 * G::PR * SPD + off) = __builtin_bit_cast(uint4, fl[x]);
+    }
+  }
+  if constexpr (X65) {
+    if (tw == 0 && row64) s.w64[lane] = f64v;
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the dense W1 rows are written
   wg_barrier();  // (3) the dense W1 rows are ready
   if (!stage_v) wg_barrier();  // (3b) the dense W1 rows are read
   wg_barrier();  // (4) every output row is staged
