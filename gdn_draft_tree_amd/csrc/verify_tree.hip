@@ -33,19 +33,18 @@
 //
 // Work decomposition: one workgroup per (layer, request, head), two resident per CU, with two
 // kinds of waves.
-//  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they gather this
-//    head's state columns from the [d_k][d_v] layout (lane (g, c) holds S0[32 ks + 8 g + e]
-//    [16 w + c], an operand of a 16x16x32 product), split them as they land, and form A_k and
-//    A_q for their channels with the row tiles read from LDS; then the W1 U product and the
-//    output rows.
+//  * d/16 product waves, wave w owning value channels [16 w, 16 w + 16): they stream the q,
+//    k and v rows into LDS (buffer loads to LDS), gather this head's state columns from the
+//    [d_k][d_v] layout (lane (g, c) holds S0[32 ks + 8 g + e][16 w + c], an operand of a
+//    16x16x32 product), split them as they land, and form A_k and A_q for their channels with
+//    the row tiles read from LDS; then the W1 U product and the output rows.
 //  * four tree waves: wave 0 loads the per-node inputs and does the per-node prologue; waves
-//    1..3 stream the q, k and v rows into LDS (buffer loads to LDS).  Together they compute
-//    the Gram tiles [Q; K] K^T of the lower node triangle, then wave 0 does the per-node path
-//    solves (one lane per node).
-// Once the q and k rows are dead, every wave writes its share of the W1 rows over them as
-// dense bf16 parts, the operand of the W1 U product.  Rows 0..63 go through 16-row MFMA
-// tiles; a 65th row (a tree of 64 drafts) rides in one extra tile of its own, and its W1 row
-// is summed on VALU.
+//    1..3 clear the compact Gram rows.  Together they compute the Gram tiles [Q; K] K^T of the
+//    lower node triangle, then wave 0 does the per-node path solves (one lane per node), and
+//    all four form the W1 rows as dense bf16 parts, which they write over the q and k rows
+//    once those are dead: the operand of the W1 U product.
+// Rows 0..63 go through 16-row MFMA tiles; a 65th row (a tree of 64 drafts) rides in one
+// extra tile of its own, and its W1 row is summed on VALU.
 //
 // MFMA operand registers are refilled only after the products that read them have completed:
 // every chain of products is fenced off from the code that refills its operands, and before a
@@ -339,10 +338,38 @@ void verify_kernel(VerifyParams p) {
 
   if (wave < NPW) {
     // ================================ product waves ==================================
-    // The tree waves issue their row loads before this barrier, so they are queued ahead of
-    // the state loads below.
+    // q, k and v rows straight into LDS, 1 KiB chunks dealt over the product waves (which
+    // write no LDS before these have landed): each wave instruction fills 64 consecutive
+    // 16-byte chunks; lane l of chunk qi holds physical chunk 64 qi + l and fetches the logical
+    // chunk that the swizzle places there.  Rows past the slot count fetch slot R-1 (never
+    // used).  They are queued ahead of the state loads below.
+    {
+      const size_t hoff = (rowbase * p.H + h) * (size_t)D;
+      const int nb = (int)((rl * rstride + D) * sizeof(T));  // byte range of this head's slots
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(static_cast<const T *>(p.q) + hoff), 0, nb, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(static_cast<const T *>(p.k) + hoff), 0, nb, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(static_cast<const T *>(p.v) + hoff), 0, nb, 0x00020000);
+#pragma unroll
+      for (int x = 0; x < (3 * QMAX + NPW - 1) / NPW; ++x) {
+        const int c = wave + NPW * x;
+        if (c < 3 * QMAX) {
+          const int mat = c / QMAX, qi = c % QMAX;
+          const int pc = 64 * qi + lane, r = pc / CPR, cc = (pc % CPR) ^ (r & (CPR - 1));
+          const unsigned off = (unsigned)((imin(r, rl) * (int)rstride + cc * CH) * (int)sizeof(T));
+          unsigned char *dst = (mat == 2 ? s.r1 : s.r0 + mat * ROWB) + 1024 * qi;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(mat == 0 ? rq : (mat == 1 ? rk : rv), (lds_void_t *)dst, 16,
+                                                   off, 0, 0, 0);
+        }
+      }
+    }
     wg_barrier();  // (0)
-    if (!valid) return;
+    if (!valid) {
+      __builtin_amdgcn_s_waitcnt(0);  // loads into this workgroup's LDS land before it ends
+      return;
+    }
     const int j = 16 * wave + l16;  // this lane's value channel (K pass and the 65th row)
     // State fragments in the [d_k][d_v] layout: lane (g, c) gathers S0[32 ks + 8 g + e][j],
     // 16 consecutive channels (64 bytes) per row and instruction.  The fragment of the next
@@ -360,6 +387,10 @@ void verify_kernel(VerifyParams p) {
     };
 #pragma unroll
     for (int ks = 0; ks < KW; ++ks) gather(ks);
+    // vmcnt(8 KW): this wave's row loads have landed (loads complete in order; the state loads
+    // just issued may still be in flight)
+    static_assert(8 * KW < 16, "the wait count fits");
+    __builtin_amdgcn_s_waitcnt((8 * KW) | (7 << 4) | (15 << 8));
     wg_barrier();  // (1) the q, k, v rows and the per-node data are in LDS
 
     // The rest of a product wave's work, as straight-line code for each count of row tiles in
@@ -419,12 +450,9 @@ void verify_kernel(VerifyParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      wg_barrier();  // (2) nobody reads q or k rows any more; the compact W1 rows are solved
-      const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
-
       // ---- o[t] = g_t A_q[t] + sum_s W1[t][s] U[s] on MFMA, U[s] = v[s] - g_s A_k[s] ---------
-      // U takes A_k's place in this lane's registers (rows >= n zero) while the tree waves write
-      // the dense W1 rows.
+      // U takes A_k's place in this lane's registers (rows >= n zero) while the tree waves finish
+      // the path solves (the gates and the v rows are in LDS since barrier (1)).
       f32x4 oc[NTU];
 #pragma unroll
       for (int mt = 0; mt < NTU; ++mt) {
@@ -437,7 +465,12 @@ void verify_kernel(VerifyParams p) {
         }
       }
       // the 65th row: A_k[64] and A_q[64] sit in lanes (0, c) of a65
-      const float u64 = (R65 && r64) ? to_f32(vrow[swz<D, CH>(64, j)]) - s.gamma[64] * a65[0] : 0.f;
+      float u64 = 0.f;
+      if constexpr (R65) {
+        if (r64) u64 = to_f32(vrow[swz<D, CH>(64, j)]) - s.gamma[64] * a65[0];
+      }
+      wg_barrier();  // (2) nobody reads q or k rows any more; the compact W1 rows are solved
+      const bool bad = __builtin_amdgcn_readfirstlane(s.bad) != 0;
       wg_barrier();  // (3) the dense W1 rows are ready; nobody reads the v rows any more
 
       // Transposed, o^T = U^T W1^T: 16x16x32 products over 32-slot blocks, the contraction
@@ -456,13 +489,15 @@ void verify_kernel(VerifyParams p) {
         for (int e = 0; e < 8; ++e)
           ua[e] = (2 * mb + (e >> 2) < NTU) ? ak[imin(2 * mb + (e >> 2), NTU - 1)][e & 3] : 0.f;
         split3(ua, uh, um, ul);
-        if (R65 && r64) {
-          const float4 wa = *reinterpret_cast<const float4 *>(&s.w64[32 * mb + 4 * g4]);
-          const float4 wb = *reinterpret_cast<const float4 *>(&s.w64[32 * mb + 16 + 4 * g4]);
-          p64 = fmaf(wa.x, ua[0], p64); p64 = fmaf(wa.y, ua[1], p64);
-          p64 = fmaf(wa.z, ua[2], p64); p64 = fmaf(wa.w, ua[3], p64);
-          p64 = fmaf(wb.x, ua[4], p64); p64 = fmaf(wb.y, ua[5], p64);
-          p64 = fmaf(wb.z, ua[6], p64); p64 = fmaf(wb.w, ua[7], p64);
+        if constexpr (R65) {
+          if (r64) {
+            const float4 wa = *reinterpret_cast<const float4 *>(&s.w64[32 * mb + 4 * g4]);
+            const float4 wb = *reinterpret_cast<const float4 *>(&s.w64[32 * mb + 16 + 4 * g4]);
+            p64 = fmaf(wa.x, ua[0], p64); p64 = fmaf(wa.y, ua[1], p64);
+            p64 = fmaf(wa.z, ua[2], p64); p64 = fmaf(wa.w, ua[3], p64);
+            p64 = fmaf(wb.x, ua[4], p64); p64 = fmaf(wb.y, ua[5], p64);
+            p64 = fmaf(wb.z, ua[6], p64); p64 = fmaf(wb.w, ua[7], p64);
+          }
         }
 #pragma unroll
         for (int mt = 2 * mb; mt < NTU; ++mt) {
@@ -477,11 +512,13 @@ void verify_kernel(VerifyParams p) {
         }
       }
       float o64 = 0.f;
-      if (R65 && r64) {  // the four lanes of a channel folded, then row 64's own term
-        p64 += __shfl_xor(p64, 16);
-        p64 += __shfl_xor(p64, 32);
-        const int d64 = imin((int)__popcll(s.mask[64]), kMaxP);
-        o64 = s.gamma[64] * a65[1] + p64 + s.cw[64 * kAR + d64] * u64;
+      if constexpr (R65) {
+        if (r64) {  // the four lanes of a channel folded, then row 64's own term
+          p64 += __shfl_xor(p64, 16);
+          p64 += __shfl_xor(p64, 32);
+          const int d64 = imin((int)__popcll(s.mask[64]), kMaxP);
+          o64 = s.gamma[64] * a65[1] + p64 + s.cw[64 * kAR + d64] * u64;
+        }
       }
       if (bad) {
 #pragma unroll
@@ -535,11 +572,9 @@ void verify_kernel(VerifyParams p) {
 
   // ================================== tree waves =====================================
   __builtin_amdgcn_s_setprio(3);
-  const int tw = wave - NPW;  // 0: per-node tree work and the path solves; 1..3: clears and rows
+  const int tw = wave - NPW;  // 0: per-node tree work and the path solves; 1..3: clears
   const size_t tb = (size_t)b * p.R;
-  // tw 0 issues only the small per-node loads (its prologue writes LDS early, and an LDS
-  // write of a wave waits for that wave's own loads into LDS).  tw 1..3 clear the compact
-  // Gram rows first, for the same reason, then load the q, k and v rows.
+  // tw 0 issues the small per-node loads; tw 1..3 clear the compact Gram rows.
   const int t_me = lane + 1;
   const int tn = imin(t_me, rl);
   const int ts = imin(lane, rl);
@@ -576,36 +611,12 @@ void verify_kernel(VerifyParams p) {
         reinterpret_cast<uint4 *>(s.cw)[i] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-    // q, k and v rows straight into LDS, 1 KiB chunks dealt over tw 1..3: each wave
-    // instruction fills 64 consecutive 16-byte chunks; lane l of chunk qi holds physical chunk
-    // 64 qi + l and fetches the logical chunk that the swizzle places there.  Rows past the
-    // slot count fetch slot R-1 (never used).
-    const size_t hoff = (rowbase * p.H + h) * (size_t)D;
-    const int nb = (int)((rl * rstride + D) * sizeof(T));  // byte range of this head's slots
-    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const T *>(p.q) + hoff), 0, nb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const T *>(p.k) + hoff), 0, nb, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(static_cast<const T *>(p.v) + hoff), 0, nb, 0x00020000);
-#pragma unroll
-    for (int x = 0; x < (3 * QMAX + NC - 1) / NC; ++x) {
-      const int c = (tw - 1) + NC * x;
-      if (c < 3 * QMAX) {
-        const int mat = c / QMAX, qi = c % QMAX;
-        const int pc = 64 * qi + lane, r = pc / CPR, cc = (pc % CPR) ^ (r & (CPR - 1));
-        const unsigned off = (unsigned)((imin(r, rl) * (int)rstride + cc * CH) * (int)sizeof(T));
-        unsigned char *dst = (mat == 2 ? s.r1 : s.r0 + mat * ROWB) + 1024 * qi;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(mat == 0 ? rq : (mat == 1 ? rk : rv), (lds_void_t *)dst, 16, off,
-                                                 0, 0, 0);
-      }
-    }
   }
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the counter and the clears are written
   __builtin_amdgcn_sched_barrier(0);
   wg_barrier();  // (0) the product waves may queue their state loads
   if (!valid) {
-    __builtin_amdgcn_s_waitcnt(0);  // loads into this workgroup's LDS land before it ends
+    __builtin_amdgcn_s_waitcnt(0);  // the per-node loads complete before the wave ends
     return;
   }
   // keep every use of tw 0's loaded values (and the wait for them) after the barrier
