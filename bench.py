@@ -70,6 +70,31 @@ def commit_bytes(cfg, tau_total: int) -> int:
     return cfg.L * cfg.H * (cfg.B * 8 * cfg.D * cfg.D + tau_total * (2 * cfg.D * e + 2 * e))
 
 
+def calibration_kernels(dev) -> None:
+    """Kernels of known traffic for scaling hardware byte counters: a plain 256 MiB copy
+    (dst = src * 1, torch's elementwise kernel), then the streaming probe reading 256 MiB once
+    from a buffer that a 1 GiB write has since pushed out of every cache (no writes)."""
+    import ctypes
+
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    cal = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush.fill_(0)
+    probe = ctypes.CDLL(os.path.join(ROOT, "gdn_draft_tree_amd", "libgdntree_probe.so"))
+    probe.gdntree_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_int, ctypes.c_void_p]
+    st = probe.gdntree_probe_stream(cal.data_ptr(), COPY_BYTES, None, 0, 4096,
+                                    torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    if st != 0:
+        raise RuntimeError(f"stream probe failed ({st})")
+
+
 # The workload the CPU baseline's worker processes share (set before they are forked).
 _CPU_WORK: dict = {}
 
@@ -256,8 +281,9 @@ def main():
                     help="oracle worker processes (0: the CPUs this process may use, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 256 MiB copy kernel (dst = src * 1), the reference "
-                         "dispatch for scaling hardware byte counters")
+                    help="also run kernels of known traffic, the reference dispatches for scaling "
+                         "hardware byte counters: a plain 256 MiB copy (dst = src * 1) and a 256 MiB "
+                         "read of a buffer pushed out of the caches (the streaming probe)")
     ap.add_argument("--tau-curve", action="store_true",
                     help="instead of the step benchmark: replay build + acceptance on the GPU over "
                          "the workload's seeded lattices for a sweep of node budgets N and print tau(N)")
@@ -364,10 +390,7 @@ def main():
             sets[i % nsets]["p_verify"]()
         torch.cuda.synchronize()
         if args.copy_calibration:
-            src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-            dst = torch.empty_like(src)
-            torch.mul(src, 1.0, out=dst)
-            torch.cuda.synchronize()
+            calibration_kernels(dev)
         print(json.dumps({"verify_only": args.verify_only, "workload": args.workload, "sets": nsets}))
         return
 
@@ -401,11 +424,7 @@ def main():
     run_pipelined(0, args.warmup)
     torch.cuda.synchronize()
     if args.copy_calibration:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_kernels(dev)
 
     # whole-step throughput (no timing events inside the timed region): pipelined steps (the
     # reported value), then the same steps strictly one after the other
