@@ -240,20 +240,40 @@ def test_commit_equals_node_state():
     np.testing.assert_allclose(new, kept, rtol=1e-12, atol=1e-13)
 
 
+def _stock_chain(rows_q, rows_k, rows_v, rows_a, rows_b, h0_head):
+    """The stock sequential recurrence over a row sequence of one head, written out here on its
+    own (expanded form: h <- a h - a b k (k^T h) + b k v^T, then o = h^T q), independent of the
+    oracle's code: states and outputs after every row."""
+    h = np.array(h0_head, dtype=np.float64)
+    states, outs = [], []
+    for q_, k_, v_, a_, b_ in zip(rows_q, rows_k, rows_v, rows_a, rows_b):
+        kh = np.einsum("i,ij->j", k_, h)
+        h = a_ * h - (a_ * b_) * np.einsum("i,j->ij", k_, kh) + b_ * np.einsum("i,j->ij", k_, v_)
+        states.append(h.copy())
+        outs.append(np.einsum("ij,i->j", h, q_))
+    return states, outs
+
+
 def test_chain_tree_equals_sequence():
-    """A chain-shaped tree verifies exactly like the sequential (stock) recurrence over the
-    same rows: node i's parent is i-1."""
+    """A chain-shaped tree (node i's parent is i-1) verifies like the stock sequential
+    recurrence over the same rows, and a node of a branching tree like the stock recurrence over
+    the rows of its root path; the recurrence is the separate loop above."""
     rng = np.random.default_rng(9)
     n, H, d = 12, 2, 8
     q, k, v, alpha, beta, h0 = _data(rng, n, H, d, d)
     st, o = oracle.verify_request(np.arange(-1, n - 1), n, q, k, v, alpha, beta, h0)
-    # a random tree whose node 5 path is 0-2-5: rows along it must reproduce the chain
-    # verify over just those rows
-    parent = np.array([-1, 0, 0, 1, 2, 2, 3, 4])
-    st_t, o_t = oracle.verify_request(parent, 8, q[:8], k[:8], v[:8], alpha[:8], beta[:8], h0)
-    rows = [0, 2, 5]
-    st_c, o_c = oracle.verify_request(np.arange(-1, 2), 3, q[rows], k[rows], v[rows],
-                                      alpha[rows], beta[rows], h0)
-    np.testing.assert_array_equal(st_t[5], st_c[2])
-    np.testing.assert_array_equal(o_t[5], o_c[2])
     assert st.shape == (n, H, d, d) and o.shape == (n, H, d)
+    for hh in range(H):
+        states, outs = _stock_chain(q[:, hh], k[:, hh], v[:, hh], alpha[:, hh], beta[:, hh], h0[hh])
+        for i in range(n):
+            np.testing.assert_allclose(st[i, hh], states[i], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(o[i, hh], outs[i], rtol=1e-12, atol=1e-13)
+    # a branching tree: node 5's root path is 0-2-5, node 7's is 0-1-3-6-7
+    parent = np.array([-1, 0, 0, 1, 2, 2, 3, 6])
+    st_t, o_t = oracle.verify_request(parent, 8, q[:8], k[:8], v[:8], alpha[:8], beta[:8], h0)
+    for node, rows in ((5, [0, 2, 5]), (7, [0, 1, 3, 6, 7])):
+        for hh in range(H):
+            states, outs = _stock_chain(q[rows, hh], k[rows, hh], v[rows, hh], alpha[rows, hh], beta[rows, hh],
+                                        h0[hh])
+            np.testing.assert_allclose(st_t[node, hh], states[-1], rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(o_t[node, hh], outs[-1], rtol=1e-12, atol=1e-13)
