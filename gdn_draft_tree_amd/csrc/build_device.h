@@ -119,18 +119,22 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
   // first-child log-prob of a node at depth d (children sit at lattice position d): lane d
   const float lp_first = s_logp[min(lane, P - 1) * K];
 
-  // Lane l holds node l (its slot) and the one frontier candidate it offers: its lowest
-  // unexpanded child rank `next`, that child's score `cand`, and, fetched ahead, the
-  // log-prob `nlp` of the rank after it, so no LDS read sits between two pops.
+  // Lane l holds node l (its slot) and the one frontier candidate it offers (`has`): its
+  // lowest unexpanded child rank `next`, that child's score `cand`, and, fetched ahead, the
+  // log-prob `nlp` of the rank after it, so no LDS read sits between two pops.  Whether a
+  // lane offers a candidate is a flag of its own: a candidate's score may be -inf (a log-prob
+  // of -inf, or a finite fp64 sum that rounds to -inf in fp32) and is still a candidate.
   const double kNone = -__builtin_inf();
   int my_parent = -1, my_depth = 0, my_rank = -1, my_next = 0;
   double my_score = 0.0, cand = kNone;
+  bool has = false;
   unsigned long long my_anc = 0ull;
   // LDS index of the fetched-ahead log-prob; every lane reloads its entry after each pop
   // (one unconditional read, so the value lands straight in its register)
   int nlp_at = 0;
   if (lane == 0) {  // the root (P >= 1 and K >= 1); no children when the request has no positions
-    cand = Pb > 0 ? 0.0 + (double)s_logp[0] : kNone;
+    has = Pb > 0;
+    cand = 0.0 + (double)s_logp[0];
     nlp_at = min(1, K - 1);
   }
   float nlp = s_logp[nlp_at];
@@ -142,19 +146,21 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
   int n = 1;
   while (n <= N) {
     const double nlpd = (double)nlp;  // last use of the fetched-ahead value before it is refilled
-    // The winner: rounding to fp32 is monotonic, so the fp64 maximum is among the lanes whose
-    // rounded score equals the fp32 maximum; when that lane is unique it is the winner,
-    // otherwise the exact fp64 maximum is taken over those lanes (ties to the lowest lane).
+    // The winner: rounding to fp32 is monotonic, so the fp64 maximum is among the offering
+    // lanes whose rounded score equals the fp32 maximum; when that lane is unique it is the
+    // winner, otherwise the exact fp64 maximum is taken over those lanes (ties to the lowest
+    // lane, which holds the smallest parent slot).
+    if (__ballot(has) == 0ull) break;                             // the trie is exhausted
     const float c32 = (float)cand;
-    const float m32 = wave_max_f32(c32);
-    if (m32 == -__builtin_inff()) break;                          // the trie is exhausted
-    unsigned long long hit = __ballot(c32 == m32);
+    const float m32 = wave_max_f32(has ? c32 : -__builtin_inff());
+    const bool top = has && c32 == m32;
+    unsigned long long hit = __ballot(top);
     double m;
     if (__popcll(hit) == 1) {
       m = __longlong_as_double(readlane_u64((unsigned long long)__double_as_longlong(cand), __ffsll((long long)hit) - 1));
     } else {
-      m = wave_max_f64(c32 == m32 ? cand : kNone);
-      hit = __ballot(cand == m);
+      m = wave_max_f64(top ? cand : kNone);
+      hit = __ballot(top && cand == m);
     }
     const int p = __ffsll((long long)hit) - 1;                    // smallest parent slot
     const int r = __builtin_amdgcn_readlane(my_next, p);
@@ -167,14 +173,16 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
     // position is never used)
     if (lane == p) {  // offer p's next child rank
       my_next = r + 1;
-      cand = (r + 1 < K) ? my_score + nlpd : kNone;
+      has = r + 1 < K;
+      cand = my_score + nlpd;
       nlp_at = dp * K + min(r + 2, K - 1);
     }
     if (n < 64) {
       if (lane == n) {
         my_parent = p; my_depth = d; my_rank = r; my_score = m; my_anc = a;
         my_next = 0;
-        cand = (d < Pb) ? m + (double)first : kNone;
+        has = d < Pb;
+        cand = m + (double)first;
         nlp_at = min(d, P - 1) * K + min(1, K - 1);
       }
     } else {

@@ -27,9 +27,15 @@ namespace {
 constexpr int kSelThreads = 1024;
 
 // Bp: B rounded up to a power of two; 1 <= G < B * N; Bp * min(N, G) <= kSharedMaxSlots.
-// Keys are the scores alone: every merge joins a list A of lower requests with a list C of
-// higher ones, so on equal scores A's key comes first, and within one list equal scores keep
-// slot order; each key carries its request (-1 for a sentinel, a slot that holds no node).
+// Keys are the scores: every merge joins a list A of lower requests with a list C of higher
+// ones, so on equal scores A's key comes first, and within one list equal scores keep slot
+// order; each key carries its request (-1 for a sentinel, a slot that holds no node), and a
+// sentinel comes after every real key, one scored -inf included.
+__device__ __forceinline__ bool key_first(double ka, int ra, double kc, int rc) {
+  if (rc < 0) return true;   // C is a sentinel: A (real or not) comes first
+  if (ra < 0) return false;  // A is a sentinel, C is real
+  return ka >= kc;
+}
 __global__ __launch_bounds__(kSelThreads) void select_budget_kernel(const double *score, int32_t *n_nodes,
                                                                     int B, int Bp, int N, int G) {
   __shared__ double s_key[2][kSharedMaxSlots];
@@ -69,6 +75,7 @@ __global__ __launch_bounds__(kSelThreads) void select_budget_kernel(const double
   while (nl > 1) {
     const int nlen = 2 * len < G ? 2 * len : G;
     const double *ks = s_key[cur];
+    const short *rq = s_req[cur];
     for (int t = tid; t < (nl / 2) * nlen; t += kSelThreads) {
       const int m = t / nlen, k = t % nlen;
       const int a0 = 2 * m * len, c0 = a0 + len;  // lists A = [a0, a0 + len) and C = [c0, c0 + len)
@@ -77,11 +84,11 @@ __global__ __launch_bounds__(kSelThreads) void select_budget_kernel(const double
       int lo = k > len ? k - len : 0, hi = k < len ? k : len;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (ks[a0 + mid] >= ks[c0 + k - 1 - mid]) lo = mid + 1;
+        if (key_first(ks[a0 + mid], rq[a0 + mid], ks[c0 + k - 1 - mid], rq[c0 + k - 1 - mid])) lo = mid + 1;
         else hi = mid;
       }
       const int i = lo, j = k - lo;
-      const int src = (i < len && (j >= len || ks[a0 + i] >= ks[c0 + j])) ? a0 + i : c0 + j;
+      const int src = (i < len && (j >= len || key_first(ks[a0 + i], rq[a0 + i], ks[c0 + j], rq[c0 + j]))) ? a0 + i : c0 + j;
       s_key[cur ^ 1][t] = ks[src];
       s_req[cur ^ 1][t] = s_req[cur][src];
     }

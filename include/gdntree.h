@@ -79,7 +79,9 @@ typedef struct {
  *
  *   lat_logp  f32 [B][P][K]  candidate log-probs per position, NON-INCREASING along K
  *                            (a sorted top-K); an unsorted row yields a valid tree that
- *                            may differ from the best-first one.  Must not hold NaN.
+ *                            may differ from the best-first one.  Must not hold NaN; -inf
+ *                            is allowed (such a candidate, and its subtree, comes after
+ *                            every finite one, and still counts toward N).
  *   lat_tok   i32 [B][P][K]  candidate token ids (distinct within a position)
  *   root_tok  i32 [B]        the pending last token of each request
  *   out                      every field written for slots < n_nodes[b]

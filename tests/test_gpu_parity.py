@@ -181,6 +181,21 @@ def test_k1_chain_and_exhausted_trie():
     H.check_all(_custom(P=2, K=3, N=64, B=3))       # 12-node trie, n = 13
 
 
+def test_minus_inf_log_probs():
+    """Masked (-inf) candidates, and finite log-probs whose fp64 sums round to -inf in fp32:
+    trees bit-exact against the oracle, per request and under batch budgets, then the whole
+    pipeline on them."""
+    w = _custom(P=3, K=4, N=64, B=3)  # tries of 84 nodes
+    rng = np.random.default_rng(5)
+    w.lat_logp[0, :, 2:] = -np.inf
+    w.lat_logp[1, 1, 1:] = -np.inf
+    w.lat_logp[2] = -np.sort(rng.uniform(1e38, 3.4e38, size=(3, 4)), axis=-1).astype(np.float32)
+    H.check_all(w)
+    for G in (20, 100, 180):
+        _say(f"-inf lattices under a budget of {G}")
+        H.check_all(w, shared=(G, None))
+
+
 def test_deep_chain_tau_17():
     """A peaked lattice and a target that always agrees with rank 0: depth 16, tau = 17."""
     w = _custom(P=16, K=16, N=64, B=2, H_=4)

@@ -4,6 +4,7 @@ Each check is fixed by the definition of best-first construction over a drafter 
 (SpecPilot summary, Prerequisites > draft-tree verification; Technical novelty) or by
 combinatorics, never by re-running the oracle's own code path.
 """
+import collections
 import itertools
 import math
 
@@ -171,3 +172,45 @@ def test_lazy_frontier_equals_full_frontier(seed):
         n = int(tree["n_nodes"][b])
         full = [(int(tree["parent"][b, i]), int(tree["rank"][b, i])) for i in range(1, n)]
         assert _lazy_build(logp[b], N) == full
+
+
+def test_minus_inf_log_probs_are_candidates():
+    """-inf log-probs (masked candidates) are candidates like any other: every finite trie
+    node comes first, in descending score order; then the -inf ones, all tied, in the tie order
+    (smaller parent slot, then smaller rank), which is breadth-first over the remaining
+    frontier: a queue, each new node's children joining at the back.  The tree is as large as
+    the budget or the trie allows."""
+    rng = np.random.default_rng(77)
+    P, K, N = 3, 4, 64                  # a trie of 84 nodes
+    logp, tok = _lattice(rng, 3, P, K)
+    logp[0, :, 2:] = -np.inf            # half of every position masked
+    logp[1, 1, 1:] = -np.inf            # position 1 masked but for rank 0
+    # finite log-probs whose sums fall below -FLT_MAX (-inf once rounded to fp32)
+    logp[2] = -np.sort(rng.uniform(1e38, 3.4e38, size=(P, K)), axis=-1).astype(np.float32)
+    tree = oracle.build_tree(logp, tok, np.arange(3), N)
+    for b in range(3):
+        allnodes = _all_trie_nodes(logp[b], P, K)
+        finite = sorted((x for x in allnodes if np.isfinite(x[1])), key=lambda x: -x[1])
+        got = _rank_paths(tree, b)[1:]
+        assert int(tree["n_nodes"][b]) == 1 + min(N, len(allnodes))
+        m = min(N, len(finite))
+        assert got[:m] == [p for p, _ in finite[:m]]
+        slot_path = {0: ()}
+        for i, path in enumerate(got[:m]):
+            slot_path[i + 1] = path
+        inserted = set(slot_path.values())
+        queue = collections.deque(sorted((sl, r) for sl, path in slot_path.items() if len(path) < P
+                                         for r in range(K) if path + (r,) not in inserted))
+        expect = []
+        while len(expect) < N - m and queue:
+            sl, r = queue.popleft()
+            path = slot_path[sl] + (r,)
+            slot = m + 1 + len(expect)
+            expect.append(path)
+            slot_path[slot] = path
+            if len(path) < P:
+                queue.extend((slot, rr) for rr in range(K))
+        assert got[m:] == expect
+        sc = tree["score"][b, 1:len(got) + 1]
+        assert np.all(np.isfinite(sc[:m])) and np.all(sc[m:] == -np.inf)
+        assert np.all(np.diff(sc[:m]) <= 0)
