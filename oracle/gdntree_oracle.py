@@ -17,6 +17,9 @@ Decoding", paper.rainbus.top/paper/2611.02501):
     (SpecPilot summary, Prerequisites > draft-tree verification).  The best-first tree
     scores edges by log p(child | parent) and may be wider than the drafter block
     (SpecPilot summary, Technical novelty).
+  * Parent-conditioned edge scores (a DSpark-style Markov head): the logit of candidate y
+    at position s is l_s(y) = bases(y) + <W1[x_{s-1}], W2[y]>, conditioned on the previous
+    token x_{s-1} (SpecPilot summary, Prerequisites > parallel drafters and lattices).
   * Gated DeltaNet: h_t = alpha_t (I - beta_t k_t k_t^T) h_{t-1} + beta_t k_t v_t^T,
     o_t = h_t^T q_t; tree verification recomputes states along root paths instead of
     snapshotting every node (SpecPilot summary, Prerequisites > hybrid recurrent
@@ -35,6 +38,10 @@ Readings where the pages leave a step open (each listed in the design notes):
     counted), N stays the per-request cap, and ties across requests go to the smaller
     request index.
   * Outputs carry no 1/sqrt(d_k) scale: o = h^T q exactly.
+  * Markov head: a position's candidate set stays the lattice's K tokens; only their scores
+    depend on the previous token, which is the parent node's token (the root token at
+    position 0).  bases(y) is the drafter's base logit of candidate y at that position.
+    The edge log-prob is the log-softmax of l_s over the position's K candidates.
 
 Every function is a direct transcription of the definition; nothing is blocked, fused or
 reordered.  This oracle keeps every per-node state of one (layer, request) while it
@@ -165,6 +172,92 @@ def build_tree_shared(lat_logp: np.ndarray, lat_tok: np.ndarray, root_tok: np.nd
         for name in ("parent", "depth", "rank", "token", "score"):
             out[name][b, :n] = t[name]
         out["anc"][b, :n] = np.array(t["anc"], dtype=np.uint64)
+        out["n_nodes"][b] = n
+    return out
+
+
+def markov_edge_logp(bases: np.ndarray, lat_tok: np.ndarray, root_tok: np.ndarray, W1: np.ndarray,
+                     W2: np.ndarray) -> np.ndarray:
+    """Parent-conditioned edge log-probs of a DSpark-style Markov head.
+
+    SpecPilot summary, Prerequisites > parallel drafters and lattices: the head scores
+    candidate y at position s as l_s(y) = bases(y) + <W1[x_{s-1}], W2[y]>, where x_{s-1} is
+    the previous token.  In a draft tree the previous token of a child at position s is its
+    parent's token: the root token for s = 0, otherwise the lattice candidate of the parent's
+    rank at position s-1.
+
+    bases: f32 [B][P][K] base logits of the lattice candidates; lat_tok: int [B][P][K];
+    root_tok: int [B]; W1, W2: [V][R] embeddings of the previous and of the candidate token.
+    Returns fp64 [B][P][K][K]: [b][s][pr][r] = l_s(lat_tok[b,s,r] | x) minus the
+    log-sum-exp of l_s over the position's K candidates, with x = root_tok[b] for s = 0
+    (every pr row the same) and x = lat_tok[b,s-1,pr] for s >= 1.
+    """
+    B, P, K = bases.shape
+    out = np.empty((B, P, K, K))
+    for b in range(B):
+        for s in range(P):
+            for pr in range(K):
+                x = int(root_tok[b]) if s == 0 else int(lat_tok[b, s - 1, pr])
+                w1 = np.asarray(W1[x], np.float64)
+                logits = np.array([float(bases[b, s, r]) + float(np.dot(w1, np.asarray(W2[int(lat_tok[b, s, r])],
+                                                                                     np.float64)))
+                                   for r in range(K)])
+                m = logits.max()
+                out[b, s, pr] = logits - (m + np.log(np.sum(np.exp(logits - m))))
+    return out
+
+
+def build_tree_cond(edge_logp: np.ndarray, lat_tok: np.ndarray, root_tok: np.ndarray, N: int) -> dict:
+    """Best-first draft tree whose edge log-probs depend on the parent (a Markov-head lattice).
+
+    SpecPilot summary, Technical novelty (edges scored by log p(child | parent)) and
+    Prerequisites > draft-tree verification (greedy addition by path log-prob up to N).
+    The same construction as build_tree, except that the log-prob of child rank r of node
+    p is edge_logp[b, depth(p), pr, r] with pr = rank(p) (the parent's candidate at its own
+    position), and pr = 0 for the root's children.
+
+    edge_logp: f32 [B][P][K][K]; lat_tok: int [B][P][K]; root_tok: int [B]; N: budget.
+    Ties: the smaller parent slot, then the smaller rank.  Returns the arrays of build_tree.
+    """
+    B, P, K = lat_tok.shape
+    out = {
+        "parent": np.full((B, N + 1), -1, np.int64),
+        "depth": np.full((B, N + 1), -1, np.int64),
+        "rank": np.full((B, N + 1), -1, np.int64),
+        "token": np.full((B, N + 1), -1, np.int64),
+        "score": np.full((B, N + 1), np.nan),
+        "anc": np.zeros((B, N + 1), np.uint64),
+        "n_nodes": np.zeros(B, np.int64),
+    }
+    for b in range(B):
+        parent, depth, rank, token, score, anc = [-1], [0], [-1], [int(root_tok[b])], [0.0], [0]
+        frontier = [(0, r) for r in range(K)] if P > 0 else []
+
+        def edge(p, r):
+            return float(np.float64(edge_logp[b, depth[p], rank[p] if depth[p] >= 1 else 0, r]))
+
+        while len(parent) - 1 < N and frontier:
+            best = min(frontier, key=lambda c: (-(score[c[0]] + edge(*c)), c[0], c[1]))
+            frontier.remove(best)
+            p, r = best
+            i = len(parent)
+            d = depth[p] + 1
+            s_new = score[p] + edge(p, r)
+            parent.append(p)
+            depth.append(d)
+            rank.append(r)
+            token.append(int(lat_tok[b, d - 1, r]))
+            score.append(s_new)
+            anc.append(anc[p] | (1 << (i - 1)))
+            if d < P:
+                frontier.extend((i, rr) for rr in range(K))
+        n = len(parent)
+        out["parent"][b, :n] = parent
+        out["depth"][b, :n] = depth
+        out["rank"][b, :n] = rank
+        out["token"][b, :n] = token
+        out["score"][b, :n] = score
+        out["anc"][b, :n] = np.array(anc, dtype=np.uint64)
         out["n_nodes"][b] = n
     return out
 

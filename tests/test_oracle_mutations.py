@@ -16,6 +16,7 @@ from oracle import gdntree_oracle as real
 
 from . import test_oracle_accept as T_acc
 from . import test_oracle_build as T_build
+from . import test_oracle_markov as T_markov
 from . import test_oracle_shared as T_shared
 from . import test_oracle_verify as T_ver
 
@@ -39,14 +40,27 @@ MUTATIONS = {
     "shared_budget_off_by_one": ("while total < G and frontier:", "while total <= G and frontier:"),
     "commit_skips_root": ("for i in acc_node[b, :int(acc_len[b])]:",
                           "for i in acc_node[b, 1:int(acc_len[b])]:"),
+    "markov_prev_same_position": ("x = int(root_tok[b]) if s == 0 else int(lat_tok[b, s - 1, pr])",
+                                  "x = int(root_tok[b]) if s == 0 else int(lat_tok[b, s, pr])"),
+    "markov_no_root": ("x = int(root_tok[b]) if s == 0 else int(lat_tok[b, s - 1, pr])",
+                       "x = int(lat_tok[b, 0, pr]) if s == 0 else int(lat_tok[b, s - 1, pr])"),
+    "markov_sign": ("float(bases[b, s, r]) + float(np.dot(", "float(bases[b, s, r]) - float(np.dot("),
+    "markov_no_normalise": ("out[b, s, pr] = logits - (m + np.log(np.sum(np.exp(logits - m))))",
+                            "out[b, s, pr] = logits - m"),
+    "cond_transposed": ("edge_logp[b, depth[p], rank[p] if depth[p] >= 1 else 0, r]",
+                        "edge_logp[b, depth[p], r, rank[p] if depth[p] >= 1 else 0]"),
+    "cond_unconditioned": ("edge_logp[b, depth[p], rank[p] if depth[p] >= 1 else 0, r]",
+                           "edge_logp[b, depth[p], 0, r]"),
+    "cond_tie_rank_desc": ("key=lambda c: (-(score[c[0]] + edge(*c)), c[0], c[1])",
+                           "key=lambda c: (-(score[c[0]] + edge(*c)), c[0], -c[1])"),
 }
 
-EXPORTS = ["build_tree", "build_tree_shared", "gdn_update", "gdn_readout", "gdn_step", "verify_request", "verify",
+EXPORTS = ["build_tree", "build_tree_shared", "build_tree_cond", "markov_edge_logp", "gdn_update", "gdn_readout", "gdn_step", "verify_request", "verify",
            "accept", "commit", "pipeline"]
 
 
 def _pins():
-    for mod in (T_build, T_shared, T_ver, T_acc):
+    for mod in (T_build, T_shared, T_ver, T_acc, T_markov):
         for name, fn in inspect.getmembers(mod, inspect.isfunction):
             if not name.startswith("test_") or fn.__module__ != mod.__name__:
                 continue
