@@ -9,6 +9,9 @@ target, as hand-written gfx950 (MI355X) HIP kernels behind a C ABI (include/gdnt
     tree = gdntree_build_shared(lat_logp, lat_tok, root_tok, N, G, positions)
     # the end of a step fused with the next step's build (optionally under a batch budget):
     acc  = gdntree_accept_commit_build(tree, target_argmax, k, v, alpha, beta, state, P, *next_lattice, N, next_tree)
+    # a Markov-head drafter (candidate scores conditioned on the previous token):
+    edge = gdntree_markov_edges(bases, lat_tok, root_tok, W1, W2)   # [B][P][K][K]
+    tree = gdntree_build_cond(edge, lat_tok, root_tok, N)
 
 Importing this package loads libgdntree.so and raises if it has not been built.
 """
@@ -16,5 +19,5 @@ from ._binding import (EXPORTED, GDNTREE_BF16, GDNTREE_ERR_ARG, GDNTREE_ERR_DEVI
                        GDNTREE_ERR_UNSUPPORTED, GDNTREE_F32, GDNTREE_OK, LIB, LIB_PATH, CTree,
                        GdnTreeError, Tree, gdntree_accept, gdntree_accept_commit,
                        gdntree_accept_commit_build, gdntree_accept_commit_build_shared, gdntree_build,
-                       gdntree_build_shared,
-                       gdntree_commit, gdntree_commit_build, gdntree_status_str, gdntree_verify)
+                       gdntree_build_cond, gdntree_build_shared, gdntree_commit, gdntree_commit_build,
+                       gdntree_markov_edges, gdntree_status_str, gdntree_verify)

@@ -20,7 +20,7 @@ GDNTREE_OK, GDNTREE_ERR_ARG, GDNTREE_ERR_UNSUPPORTED, GDNTREE_ERR_DEVICE = 0, 1,
 GDNTREE_F32, GDNTREE_BF16 = 0, 1
 EXPORTED = ("gdntree_build", "gdntree_build_shared", "gdntree_verify", "gdntree_accept_commit", "gdntree_accept", "gdntree_commit",
             "gdntree_commit_build", "gdntree_accept_commit_build", "gdntree_accept_commit_build_shared",
-            "gdntree_status_str")
+            "gdntree_build_cond", "gdntree_markov_edges", "gdntree_status_str")
 
 
 class GdnTreeError(RuntimeError):
@@ -44,6 +44,10 @@ def _load() -> ctypes.CDLL:
     lib.gdntree_build.restype = i
     lib.gdntree_build_shared.argtypes = [vp, vp, vp, vp, i, i, i, i, i, CTree, vp]
     lib.gdntree_build_shared.restype = i
+    lib.gdntree_build_cond.argtypes = [vp, vp, vp, i, i, i, i, CTree, vp]
+    lib.gdntree_build_cond.restype = i
+    lib.gdntree_markov_edges.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp]
+    lib.gdntree_markov_edges.restype = i
     lib.gdntree_verify.argtypes = [CTree, i, i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, i, vp, vp]
     lib.gdntree_verify.restype = i
     lib.gdntree_accept_commit.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp,
@@ -180,6 +184,40 @@ def gdntree_build(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch
         raise ValueError("output tree has the wrong shape")
     return _run(LIB.gdntree_build, (*args, B, P, K, N, out.c(), _stream(stream)), prepare, out,
                 (lat_logp, lat_tok, root_tok, out))
+
+
+def gdntree_build_cond(edge_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch.Tensor, N: int,
+                       out: Tree | None = None, stream=None, prepare: bool = False) -> Tree:
+    """Best-first tree over parent-conditioned edge log-probs [B][P][K][K]; see gdntree.h."""
+    B, P, K, K2 = edge_logp.shape
+    if K2 != K:
+        raise ValueError("edge_logp must be [B][P][K][K]")
+    out = out if out is not None else Tree.empty(B, N, edge_logp.device)
+    args = (_dev(edge_logp, "edge_logp", torch.float32, (B, P, K, K)),
+            _dev(lat_tok, "lat_tok", torch.int32, (B, P, K)),
+            _dev(root_tok, "root_tok", torch.int32, (B,)))
+    if out.B != B or out.N != N:
+        raise ValueError("output tree has the wrong shape")
+    return _run(LIB.gdntree_build_cond, (*args, B, P, K, N, out.c(), _stream(stream)), prepare, out,
+                (edge_logp, lat_tok, root_tok, out))
+
+
+def gdntree_markov_edges(bases: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch.Tensor, W1: torch.Tensor,
+                         W2: torch.Tensor, out: torch.Tensor | None = None, stream=None,
+                         prepare: bool = False) -> torch.Tensor:
+    """Markov-head edge log-probs [B][P][K][K] from base logits [B][P][K] and the head's [V][R]
+    embeddings (f32 or bf16, the same dtype); see gdntree.h."""
+    B, P, K = bases.shape
+    V, R = W1.shape
+    if W2.dtype != W1.dtype:
+        raise ValueError("W1 and W2 must share a dtype")
+    out = out if out is not None else torch.empty(B, P, K, K, dtype=torch.float32, device=bases.device)
+    args = (_dev(bases, "bases", torch.float32, (B, P, K)), _dev(lat_tok, "lat_tok", torch.int32, (B, P, K)),
+            _dev(root_tok, "root_tok", torch.int32, (B,)), _dev(W1, "W1", W1.dtype, (V, R)),
+            _dev(W2, "W2", W1.dtype, (V, R)))
+    return _run(LIB.gdntree_markov_edges, (*args, _code(W1.dtype), B, P, K, V, R,
+                                           _dev(out, "out", torch.float32, (B, P, K, K)), _stream(stream)),
+                prepare, out, (bases, lat_tok, root_tok, W1, W2, out))
 
 
 def gdntree_build_shared(lat_logp: torch.Tensor, lat_tok: torch.Tensor, root_tok: torch.Tensor, N: int,

@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libgdntree.so")
-SOURCES = ["gdntree_api.hip", "build_tree.hip", "verify_tree.hip", "accept_commit.hip", "commit_build.hip", "shared_budget.hip"]
+SOURCES = ["gdntree_api.hip", "build_tree.hip", "verify_tree.hip", "accept_commit.hip", "commit_build.hip",
+           "shared_budget.hip", "markov_edges.hip"]
 # the benchmark's streaming probe, in a library of its own (not part of the path's ABI)
 PROBE_SOURCES = ["stream_probe.hip"]
 PROBE_LIB = os.path.join(HERE, "libgdntree_probe.so")

@@ -15,6 +15,15 @@
 // is the only one offered).  This pops exactly the sequence of a full frontier ordered by
 // (score desc, parent asc, rank asc).  Only slots 0..63 can ever be parents (the 65th
 // node is the last insertion), so 64 lanes suffice.
+//
+// Parent-conditioned edges (a Markov-head lattice: the log-prob of child rank r at position s
+// depends on the parent's own rank pr at position s-1).  Each (s, pr) row of log-probs is
+// sorted once (descending, equal values by rank) with the permutation kept, and a node
+// offers its children in its own row's order: the same frontier argument holds row by row,
+// and the plain lattice is the special case of one row per position.  Row order is the
+// (sum desc, rank asc) order of the children as long as distinct log-probs give distinct
+// fp64 sums with the node's score; a node scored -inf, whose children all tie at -inf,
+// offers them in rank order instead (from the unsorted row).
 
 #pragma once
 
@@ -29,6 +38,8 @@ struct BuildParams {
   gdntree_tree out;
   // draft positions per request [B], clipped to [0, P]; null: all P for every request
   const int32_t *positions = nullptr;
+  // parent-conditioned edge log-probs [B][P][K][K] ([b][s][pr][r]); null: the plain lattice
+  const float *edge_logp = nullptr;
 };
 
 template <int CTRL, int ROWMASK>
@@ -98,26 +109,74 @@ __device__ __forceinline__ void stage_lattice(const BuildParams &bp, int b, int 
   }
 }
 
+// Threads t = 0..nth-1 stage request b's parent-conditioned rows: the raw rows to s_raw, then
+// (after a workgroup barrier) every row sorted by descending log-prob, equal values by rank,
+// to s_logp with the permutation (the candidate rank of each sorted entry) to s_perm; token
+// ids to s_ltok.  Ends with a workgroup barrier.  Every thread of the workgroup calls it.
+__device__ __forceinline__ void stage_lattice_cond(const BuildParams &bp, int b, int t, int nth, float *s_raw,
+                                                   float *s_logp, uint8_t *s_perm, int *s_ltok) {
+  const int K = bp.K, PK = bp.P * bp.K, PKK = PK * bp.K;
+  const float *e = bp.edge_logp + (size_t)b * PKK;
+  const int32_t *lt = bp.lat_tok + (size_t)b * PK;
+  for (int x = t; x < PKK; x += nth) s_raw[x] = e[x];
+  for (int x = t; x < PK; x += nth) s_ltok[x] = lt[x];
+  __syncthreads();
+  for (int x = t; x < PKK; x += nth) {
+    const int row = x / K, i = x - row * K;
+    const float v = s_raw[x];
+    int pos = 0;
+    for (int j = 0; j < K; ++j) {
+      const float w = s_raw[row * K + j];
+      pos += (w > v || (w == v && j < i)) ? 1 : 0;
+    }
+    s_logp[row * K + pos] = v;
+    s_perm[row * K + pos] = (uint8_t)i;
+  }
+  __syncthreads();
+}
+
 // Builds request b's tree.  Unless `staged` (the caller has staged the lattice with
 // stage_lattice and met a workgroup barrier since), every thread of the workgroup (tid < nth)
 // helps stage the lattice and meets the workgroup barrier; then the first wave alone runs the
-// pops and writes the tree.
+// pops and writes the tree.  COND: the rows are parent-conditioned and already staged with
+// stage_lattice_cond (s_logp sorted rows, s_perm their ranks).
+template <bool COND = false>
 __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int tid, int nth, float *s_logp,
-                                              int *s_ltok, bool staged = false) {
+                                              int *s_ltok, bool staged = false, const uint8_t *s_perm = nullptr) {
   const int P = bp.P, K = bp.K, N = bp.N;
   // children are offered only at depths below this request's own position count
   const int Pb = bp.positions ? min(max(bp.positions[b], 0), P) : P;
   const gdntree_tree &out = bp.out;
   const int PK = P * K;
-  if (!staged) {
+  if (!COND && !staged) {
     stage_lattice(bp, b, tid, nth, s_logp, s_ltok);
     __syncthreads();
   }
   if (tid >= 64) return;  // one wave builds
   const int lane = tid;
   const int root_token = bp.root_tok[b];  // loaded now, used after the pops
-  // first-child log-prob of a node at depth d (children sit at lattice position d): lane d
+  // first-child log-prob of a node at depth d (children sit at lattice position d): lane d.
+  // Conditioned: the first (sorted) entry and its rank of every row, row w in lane w % 64 of
+  // register w / 64 (at most 16 x 16 rows).
   const float lp_first = s_logp[min(lane, P - 1) * K];
+  float cf_lp[4];
+  int cf_rk[4];
+  if constexpr (COND) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = min(64 * j + lane, PK - 1);
+      cf_lp[j] = s_logp[row * K];
+      cf_rk[j] = s_perm[row * K];
+    }
+  }
+  // the first child of row `row` (uniform): its log-prob and rank
+  auto first_of = [&](int row, float &lp, int &rk) {
+    const int j = row >> 6, l = row & 63;
+    const float v = j == 0 ? cf_lp[0] : j == 1 ? cf_lp[1] : j == 2 ? cf_lp[2] : cf_lp[3];
+    const int k = j == 0 ? cf_rk[0] : j == 1 ? cf_rk[1] : j == 2 ? cf_rk[2] : cf_rk[3];
+    lp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+    rk = __builtin_amdgcn_readlane(k, l);
+  };
 
   // Lane l holds node l (its slot) and the one frontier candidate it offers (`has`): its
   // lowest unexpanded child rank `next`, that child's score `cand`, and, fetched ahead, the
@@ -128,16 +187,23 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
   int my_parent = -1, my_depth = 0, my_rank = -1, my_next = 0;
   double my_score = 0.0, cand = kNone;
   bool has = false;
+  // conditioned: the rank of the child on offer and, fetched ahead with `nlp`, of the next one;
+  // `byrank`: the node's children are offered in rank order (its score is -inf)
+  int my_crank = 0, ncr = 0;
+  bool byrank = false;
+  const float *s_raw = s_logp + (COND ? bp.P * K * K : 0);  // conditioned: the unsorted rows follow
   unsigned long long my_anc = 0ull;
   // LDS index of the fetched-ahead log-prob; every lane reloads its entry after each pop
   // (one unconditional read, so the value lands straight in its register)
   int nlp_at = 0;
   if (lane == 0) {  // the root (P >= 1 and K >= 1); no children when the request has no positions
     has = Pb > 0;
-    cand = 0.0 + (double)s_logp[0];
+    cand = 0.0 + (double)s_logp[0];  // row 0 for the conditioned rows too: position 0, the root
     nlp_at = min(1, K - 1);
+    if constexpr (COND) my_crank = s_perm[0];
   }
   float nlp = s_logp[nlp_at];
+  if constexpr (COND) ncr = s_perm[nlp_at];
   // The 65th slot (index 64) has no lane; it is the last insertion and is kept uniformly.
   int x_parent = -1, x_depth = 0, x_rank = -1;
   double x_score = 0.0;
@@ -163,19 +229,35 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
       hit = __ballot(top && cand == m);
     }
     const int p = __ffsll((long long)hit) - 1;                    // smallest parent slot
-    const int r = __builtin_amdgcn_readlane(my_next, p);
+    const int nx = __builtin_amdgcn_readlane(my_next, p);         // index in p's child order
+    const int r = COND ? __builtin_amdgcn_readlane(my_crank, p) : nx;  // the child's rank
     const int dp = __builtin_amdgcn_readlane(my_depth, p);
     const int d = dp + 1;
     const unsigned long long a = readlane_u64(my_anc, p) | (1ull << (n - 1));
-    const float first = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp_first), min(d, P - 1)));
+    // the new node's row of children and its first child
+    const int row_n = COND ? min(d, P - 1) * K + r : min(d, P - 1);
+    float first;
+    int first_rk = 0;
+    if constexpr (COND) {
+      if (m == kNone) {  // a node scored -inf: its children tie, rank order (uniform branch)
+        first = s_raw[row_n * K];
+        first_rk = 0;
+      } else {
+        first_of(row_n, first, first_rk);
+      }
+    } else {
+      first = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp_first), min(d, P - 1)));
+    }
 
     // (fetched-ahead entries are clamped, always valid: one standing past the last rank or
     // position is never used)
-    if (lane == p) {  // offer p's next child rank
-      my_next = r + 1;
-      has = r + 1 < K;
+    if (lane == p) {  // offer p's next child
+      my_next = nx + 1;
+      has = nx + 1 < K;
       cand = my_score + nlpd;
-      nlp_at = dp * K + min(r + 2, K - 1);
+      const int row_p = COND ? (dp == 0 ? 0 : dp * K + my_rank) : dp;
+      nlp_at = row_p * K + min(nx + 2, K - 1);
+      if constexpr (COND) my_crank = byrank ? nx + 1 : ncr;
     }
     if (n < 64) {
       if (lane == n) {
@@ -183,12 +265,21 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
         my_next = 0;
         has = d < Pb;
         cand = m + (double)first;
-        nlp_at = min(d, P - 1) * K + min(1, K - 1);
+        nlp_at = row_n * K + min(1, K - 1);
+        if constexpr (COND) {
+          my_crank = first_rk;
+          byrank = m == kNone;
+        }
       }
     } else {
       x_parent = p; x_depth = d; x_rank = r; x_score = m; x_anc = a;
     }
-    nlp = s_logp[nlp_at];
+    if constexpr (COND) {
+      nlp = byrank ? s_raw[nlp_at] : s_logp[nlp_at];
+      ncr = s_perm[nlp_at];
+    } else {
+      nlp = s_logp[nlp_at];
+    }
     ++n;
   }
 

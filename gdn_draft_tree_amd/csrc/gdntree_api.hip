@@ -48,6 +48,36 @@ GDNTREE_EXPORT gdntree_status gdntree_build(const float *lat_logp, const int32_t
   return GDNTREE_OK;
 }
 
+GDNTREE_EXPORT gdntree_status gdntree_build_cond(const float *edge_logp, const int32_t *lat_tok,
+                                                 const int32_t *root_tok, int B, int P, int K, int N,
+                                                 gdntree_tree out, hipStream_t stream) {
+  if (!edge_logp || !lat_tok || !root_tok || !out.parent || !out.depth || !out.rank ||
+      !out.token || !out.score || !out.anc || !out.n_nodes)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || P <= 0 || K <= 0 || N <= 0) return GDNTREE_ERR_ARG;
+  if (P > kMaxP || K > kCondMaxK || N > kMaxN || !grid_fits(B)) return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  if (launch_build_cond(edge_logp, lat_tok, root_tok, B, P, K, N, out, stream) != hipSuccess)
+    return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
+GDNTREE_EXPORT gdntree_status gdntree_markov_edges(const float *bases, const int32_t *lat_tok,
+                                                   const int32_t *root_tok, const void *W1, const void *W2,
+                                                   gdntree_dtype w_dtype, int B, int P, int K, int V, int R,
+                                                   float *edge_logp, hipStream_t stream) {
+  if (!bases || !lat_tok || !root_tok || !W1 || !W2 || !edge_logp) return GDNTREE_ERR_ARG;
+  if (B <= 0 || P <= 0 || K <= 0 || V <= 0 || R <= 0 || !dtype_ok(w_dtype)) return GDNTREE_ERR_ARG;
+  const long long wbytes = (long long)V * R * (w_dtype == GDNTREE_BF16 ? 2 : 4);
+  if (P > kMaxP || K > kMaxK || R > 64 || wbytes > 0x7fffffffLL || !grid_fits((long long)B * P))
+    return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  if (launch_markov_edges(bases, lat_tok, root_tok, W1, W2, w_dtype == GDNTREE_BF16, B, P, K, V, R, edge_logp,
+                          stream) != hipSuccess)
+    return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
 GDNTREE_EXPORT gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_tok,
                                                    const int32_t *root_tok, const int32_t *positions,
                                                    int B, int P, int K, int N, int G, gdntree_tree out,

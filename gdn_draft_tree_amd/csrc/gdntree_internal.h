@@ -13,6 +13,7 @@ constexpr int kMaxSlots = kMaxN + 1;
 constexpr int kMaxP = 16;          // positions, hence tree depth
 constexpr int kMaxK = 64;          // candidates per position
 constexpr int kMaxAnc = kMaxP + 1; // ancestors-or-self of a node (depth 0..16)
+constexpr int kCondMaxK = 16;      // candidates per position with parent-conditioned rows
 constexpr int kSharedMaxSlots = 4096;  // keys the budget cut holds: pow2(B) * min(N, G)
 constexpr int kSharedMaxB = 1024;      // requests of a build under a shared budget
 
@@ -39,6 +40,14 @@ __device__ __forceinline__ float load_elem(const float *p, size_t i) { return p[
 // Launchers (defined next to their kernels).  They assume validated arguments.
 hipError_t launch_build(const float *lat_logp, const int32_t *lat_tok, const int32_t *root_tok,
                         int B, int P, int K, int N, gdntree_tree out, hipStream_t stream);
+
+// best-first build over parent-conditioned edge log-probs [B][P][K][K] (K <= kCondMaxK)
+hipError_t launch_build_cond(const float *edge_logp, const int32_t *lat_tok, const int32_t *root_tok, int B,
+                             int P, int K, int N, gdntree_tree out, hipStream_t stream);
+// Markov-head edge log-probs [B][P][K][K] from base logits, token ids and the head's embeddings
+hipError_t launch_markov_edges(const float *bases, const int32_t *lat_tok, const int32_t *root_tok,
+                               const void *W1, const void *W2, bool w_bf16, int B, int P, int K, int V, int R,
+                               float *edge_logp, hipStream_t stream);
 
 struct VerifyParams {
   const int32_t *parent;

@@ -11,7 +11,9 @@
  * gdntree_accept_commit_build_shared fuses that build into the end of the previous step.
  * gdntree_accept_commit also comes as two calls, gdntree_accept then gdntree_commit, and
  * gdntree_commit_build / gdntree_accept_commit_build run a commit (with or without the
- * acceptance) together with the next step's tree build in one launch.
+ * acceptance) together with the next step's tree build in one launch.  For a drafter whose
+ * candidate scores depend on the previous token (a Markov head), gdntree_markov_edges forms
+ * the parent-conditioned edge log-probs and gdntree_build_cond builds the tree over them.
  *
  * Sources: the SpecPilot paper summary (paper.rainbus.top, "SpecPilot: Autonomous
  * Algorithm Discovery and Systems Optimization for Speculative Decoding"), sections
@@ -117,6 +119,51 @@ gdntree_status gdntree_build(const float *lat_logp, const int32_t *lat_tok,
 gdntree_status gdntree_build_shared(const float *lat_logp, const int32_t *lat_tok,
                                     const int32_t *root_tok, const int32_t *positions, int B,
                                     int P, int K, int N, int G, gdntree_tree out, hipStream_t stream);
+
+/*
+ * gdntree_markov_edges - parent-conditioned edge log-probs of a DSpark-style Markov head.
+ *
+ * The head scores candidate y at position s as l_s(y) = bases(y) + <W1[x_{s-1}], W2[y]>,
+ * x_{s-1} the previous token (SpecPilot summary, Prerequisites > parallel drafter).  A
+ * child's previous token is its parent's: the root token at position 0, else the parent's
+ * candidate at position s-1.  A position's candidates stay its K lattice tokens; only their
+ * scores depend on the parent.
+ *
+ *   bases     f32 [B][P][K]      base logits of the lattice candidates
+ *   lat_tok   i32 [B][P][K]      candidate token ids (in [0, V))
+ *   root_tok  i32 [B]            the pending last token of each request (in [0, V))
+ *   W1, W2    [V][R], w_dtype    previous-token and candidate embeddings (f32 or bf16)
+ *   edge_logp f32 [B][P][K][K]   out: [b][s][pr][r] = l_s(candidate r | the previous token of
+ *                                row pr) minus the log-sum-exp of l_s over the K candidates of
+ *                                position s; row pr's previous token is candidate pr of
+ *                                position s-1 (s >= 1) or the root token (s = 0, every row)
+ * Arithmetic in fp32 (the dot products in order over R, a max-shifted log-sum-exp).  A token
+ * id outside [0, V) reads an all-zero embedding row.  Limits: P <= 16, K <= 64, R <= 64,
+ * V * R * (element size) < 2^31 (else ERR_UNSUPPORTED).
+ */
+gdntree_status gdntree_markov_edges(const float *bases, const int32_t *lat_tok, const int32_t *root_tok,
+                                    const void *W1, const void *W2, gdntree_dtype w_dtype, int B, int P,
+                                    int K, int V, int R, float *edge_logp, hipStream_t stream);
+
+/*
+ * gdntree_build_cond - best-first draft tree over parent-conditioned edge log-probs.
+ *
+ * As gdntree_build, except that the log-prob of child rank r of node p is
+ * edge_logp[b][depth(p)][pr][r] with pr = rank(p), the parent's own candidate at its position
+ * (pr = 0 for the root's children): edges scored by log p(child | parent) (SpecPilot summary,
+ * Technical novelty).  Scores are fp64 sums of these fp32 log-probs root to leaf; ties go to
+ * the smaller parent slot, then the smaller rank.  The rows need not be sorted: each row is
+ * sorted once and a node offers its children in that order, which is the tie rule's order
+ * whenever distinct log-probs of a row give distinct fp64 sums with the node's score (rows of
+ * log-probabilities do for every score above -1e8); a node scored -inf offers its children,
+ * all tied at -inf, in rank order.
+ *
+ *   edge_logp f32 [B][P][K][K]   e.g. from gdntree_markov_edges; no NaN (-inf allowed)
+ *   lat_tok, root_tok, out       as for gdntree_build
+ * Limits: P <= 16, K <= 16, N <= 64 (else ERR_UNSUPPORTED).
+ */
+gdntree_status gdntree_build_cond(const float *edge_logp, const int32_t *lat_tok, const int32_t *root_tok,
+                                  int B, int P, int K, int N, gdntree_tree out, hipStream_t stream);
 
 /*
  * gdntree_verify - per-node gated delta rule over the tree, one or more layers.

@@ -24,8 +24,9 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_accept_commit_build",
-                           "gdntree_accept_commit_build_shared", "gdntree_build", "gdntree_build_shared", "gdntree_commit", "gdntree_commit_build", "gdntree_status_str",
-                           "gdntree_verify"]
+                           "gdntree_accept_commit_build_shared", "gdntree_build", "gdntree_build_cond",
+                           "gdntree_build_shared", "gdntree_commit", "gdntree_commit_build",
+                           "gdntree_markov_edges", "gdntree_status_str", "gdntree_verify"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -79,6 +80,52 @@ def test_build_rejects(case, expect):
     if case == "N65": args["N"] = 65
     st = g.LIB.gdntree_build(args["logp"], args["tok"], args["root"], args["B"], args["P"], args["K"],
                              args["N"], args["tree"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_edge", 1), ("null_tok", 1), ("null_tree_field", 1), ("B0", 1), ("K0", 1), ("N0", 1),
+    ("P17", 2), ("K17", 2), ("N65", 2),
+])
+def test_build_cond_rejects(case, expect):
+    """Conditioned rows are staged per request in LDS: K <= 16."""
+    g = _lib()
+    args = dict(edge=FAKE, tok=FAKE, root=FAKE, B=2, P=8, K=16, N=24, tree=_tree(g))
+    if case == "null_edge": args["edge"] = None
+    if case == "null_tok": args["tok"] = None
+    if case == "null_tree_field": args["tree"] = _tree(g, score=1)
+    if case == "B0": args["B"] = 0
+    if case == "K0": args["K"] = 0
+    if case == "N0": args["N"] = 0
+    if case == "P17": args["P"] = 17
+    if case == "K17": args["K"] = 17
+    if case == "N65": args["N"] = 65
+    st = g.LIB.gdntree_build_cond(args["edge"], args["tok"], args["root"], args["B"], args["P"], args["K"],
+                                  args["N"], args["tree"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_bases", 1), ("null_w2", 1), ("null_out", 1), ("B0", 1), ("V0", 1), ("R0", 1), ("dtype", 1),
+    ("P17", 2), ("K65", 2), ("R65", 2), ("Vbig", 2),
+])
+def test_markov_edges_rejects(case, expect):
+    g = _lib()
+    args = dict(bases=FAKE, tok=FAKE, root=FAKE, W1=FAKE, W2=FAKE, dt=g.GDNTREE_F32, B=2, P=8, K=16, V=1000,
+                R=32, out=FAKE)
+    if case == "null_bases": args["bases"] = None
+    if case == "null_w2": args["W2"] = None
+    if case == "null_out": args["out"] = None
+    if case == "B0": args["B"] = 0
+    if case == "V0": args["V"] = 0
+    if case == "R0": args["R"] = 0
+    if case == "dtype": args["dt"] = 7
+    if case == "P17": args["P"] = 17
+    if case == "K65": args["K"] = 65
+    if case == "R65": args["R"] = 65
+    if case == "Vbig": args["V"] = 1 << 25  # V * R * 4 bytes past 2^31
+    st = g.LIB.gdntree_markov_edges(args["bases"], args["tok"], args["root"], args["W1"], args["W2"], args["dt"],
+                                    args["B"], args["P"], args["K"], args["V"], args["R"], args["out"], None)
     assert st == expect
 
 

@@ -549,3 +549,105 @@ def test_accept_commit_build_shared_equals_the_two_calls(G, positions):
     H.assert_tree_equal(a["tree"], ref)
     H.assert_tree_equal(b["tree"], ref)
     _say(f"fused shared build G={G}: drafts {int(ref['n_nodes'].sum()) - 32}")
+
+
+# ---------------------------------------------------------------------------------------------
+# Markov-head lattices: parent-conditioned edge log-probs and the build over them
+# ---------------------------------------------------------------------------------------------
+def _markov(name, seed, R, wdtype, B=None):
+    """The config's lattice tokens and roots with seeded Markov-head inputs; the embeddings
+    cast to the kernel's dtype (bf16 by round-to-nearest-even on the CPU): both sides consume
+    the cast values."""
+    import workloads
+    cfg = CONFIGS[name] if B is None else replace(CONFIGS[name], B=B)
+    w = generate(cfg, seed=seed)
+    mh = workloads.markov_head(cfg, seed=seed, R=R)
+    dt = torch.bfloat16 if wdtype == "bf16" else torch.float32
+    W1 = torch.from_numpy(mh.W1).to(dt)
+    W2 = torch.from_numpy(mh.W2).to(dt)
+    return w, mh.bases, W1, W2
+
+
+@pytest.mark.parametrize("name,R,wdtype", [("batched", 32, "f32"), ("ragged", 32, "bf16"), ("ragged", 64, "f32"),
+                                           ("deep", 16, "bf16")])
+def test_markov_edges_against_oracle(name, R, wdtype):
+    """Edge log-probs of the Markov head against the oracle's fp64 values.  The kernel works in
+    fp32 (an R-term dot product, a max-shifted log-sum-exp over K): the bar is 5e-5 absolute on
+    log-probs of magnitude <= ~30, far above fp32 rounding (~1e-6) and far below any real error
+    (a wrong previous token or candidate shifts entries by ~1)."""
+    import oracle
+    import gdn_draft_tree_amd as g
+    w, bases, W1, W2 = _markov(name, 4, R, wdtype, B=1 if name == "deep" else 8)
+    tok, root = w.lat_tok, w.root_tok
+    gpu = g.gdntree_markov_edges(torch.from_numpy(bases).cuda(), torch.from_numpy(tok).cuda(),
+                                 torch.from_numpy(root).cuda(), W1.cuda(), W2.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.markov_edge_logp(bases, tok, root, W1.to(torch.float64).numpy(), W2.to(torch.float64).numpy())
+    err = np.abs(gpu.cpu().numpy().astype(np.float64) - ref)
+    _say(f"markov edges {name} R={R} {wdtype}: max |err| {err.max():.2e}, |value| <= {np.abs(ref).max():.1f}")
+    assert np.all(np.isfinite(gpu.cpu().numpy()))
+    assert err.max() <= 5e-5
+
+
+def test_markov_edges_out_of_range_tokens():
+    """A token id outside [0, V) reads an all-zero embedding row (on both the previous-token and
+    the candidate side): the oracle over embeddings padded with zero rows at those ids agrees."""
+    import oracle
+    import gdn_draft_tree_amd as g
+    w, bases, W1, W2 = _markov("batched", 1, 16, "f32", B=3)
+    tok, root = w.lat_tok.copy(), w.root_tok.copy()
+    V = W1.shape[0]
+    tok[0, 2, 5] = V + 3     # a candidate, and the previous token of row 5 at position 3
+    tok[1, 0, 0] = -7        # negative
+    root[2] = V + 1          # the root
+    gpu = g.gdntree_markov_edges(torch.from_numpy(bases).cuda(), torch.from_numpy(tok).cuda(),
+                                 torch.from_numpy(root).cuda(), W1.cuda(), W2.cuda())
+    torch.cuda.synchronize()
+    pad = np.zeros((8, W1.shape[1]))
+    W1p = np.concatenate([W1.double().numpy(), pad])   # ids V .. V+7 read zeros
+    W2p = np.concatenate([W2.double().numpy(), pad])
+    tok_o = tok.copy()
+    tok_o[1, 0, 0] = V + 7   # the negative id, mapped to a zero row on the oracle side
+    ref = oracle.markov_edge_logp(bases, tok_o, root, W1p, W2p)
+    assert np.abs(gpu.cpu().numpy() - ref).max() <= 5e-5
+
+
+def _check_build_cond(edge, tok, root, N):
+    import oracle
+    import gdn_draft_tree_amd as g
+    tree = g.gdntree_build_cond(torch.from_numpy(edge).cuda(), torch.from_numpy(tok).cuda(),
+                                torch.from_numpy(root).cuda(), N)
+    torch.cuda.synchronize()
+    got = {f: getattr(tree, f).cpu().numpy() for f in ("parent", "depth", "rank", "token", "score", "anc", "n_nodes")}
+    H.assert_tree_equal(got, oracle.build_tree_cond(edge, tok, root, N))
+    return got
+
+
+@pytest.mark.parametrize("name,N", [("ragged", 64), ("batched", 24), ("deep", 64), ("ragged", 17)])
+def test_build_cond_markov_rows(name, N):
+    """Trees over Markov-head edge log-probs (the oracle's values, cast to fp32: the input both
+    sides build from) bit-exact against the oracle: topology, tokens, scores, masks."""
+    import oracle
+    w, bases, W1, W2 = _markov(name, 6, 32, "f32", B=1 if name == "deep" else 12)
+    edge = oracle.markov_edge_logp(bases, w.lat_tok, w.root_tok, W1.double().numpy(),
+                                   W2.double().numpy()).astype(np.float32)
+    got = _check_build_cond(edge, w.lat_tok, w.root_tok, N)
+    _say(f"build_cond {name} N={N}: nodes {got['n_nodes'].min()}..{got['n_nodes'].max()}, "
+         f"max depth {got['depth'].max()}")
+
+
+def test_build_cond_unsorted_ties_and_minus_inf():
+    """Rows in no order (the kernel sorts each (position, parent rank) row), rows of equal
+    values (the tie rule alone), -inf entries (candidates like any other) and a trie smaller
+    than the budget."""
+    rng = np.random.default_rng(11)
+    B, P, K, N = 4, 5, 6, 64
+    logits = rng.normal(0, 2, size=(B, P, K, K))
+    edge = (logits - np.log(np.exp(logits).sum(-1, keepdims=True))).astype(np.float32)
+    edge[1] = np.float32(-math.log(K))                 # every edge tied
+    edge[2, :, :, 3:] = -np.inf                        # half of every row masked
+    edge[3, 2, 1:, :] = -np.inf                        # rows of position 2 masked but for parent rank 0
+    tok = rng.integers(0, 5000, size=(B, P, K)).astype(np.int32)
+    root = rng.integers(0, 5000, size=B).astype(np.int32)
+    _check_build_cond(edge, tok, root, N)
+    _check_build_cond(edge[:, :2, :, :].copy(), tok[:, :2].copy(), root, N)  # 6 + 36 = 42 nodes < 64

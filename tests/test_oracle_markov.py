@@ -159,3 +159,40 @@ def test_ties_go_to_the_smaller_parent_then_rank():
     for i in range(1, n):
         paths[i] = paths[int(tree["parent"][0, i])] + (int(tree["rank"][0, i]),)
     assert [paths[i] for i in range(n)] == bfs[:n]
+
+
+def test_minus_inf_edges_are_candidates():
+    """-inf edge log-probs in conditioned rows: every finite trie node first, by descending
+    path score; then the -inf ones, all tied, breadth-first over the remaining frontier in
+    (parent slot, rank) order (a queue, each new node's children joining at the back)."""
+    import collections
+    rng = np.random.default_rng(21)
+    P, K, N = 3, 4, 64
+    edge, tok = _lattice_cond(rng, 2, P, K)
+    edge[0, :, :, 2:] = -np.inf         # half of every row masked
+    edge[1, 1, 1:, :] = -np.inf         # position 1 masked under every parent but rank 0
+    tree = oracle.build_tree_cond(edge, tok, np.arange(2), N)
+    for b in range(2):
+        allp = _all_paths(edge[b], P, K)
+        finite = sorted((x for x in allp if np.isfinite(x[1])), key=lambda x: -x[1])
+        n = int(tree["n_nodes"][b])
+        assert n == 1 + min(N, len(allp))
+        paths = {0: ()}
+        for i in range(1, n):
+            paths[i] = paths[int(tree["parent"][b, i])] + (int(tree["rank"][b, i]),)
+        got = [paths[i] for i in range(1, n)]
+        m = min(N, len(finite))
+        assert got[:m] == [p for p, _ in finite[:m]]
+        slot_path = {i: paths[i] for i in range(m + 1)}
+        inserted = set(slot_path.values())
+        queue = collections.deque(sorted((sl, r) for sl, path in slot_path.items() if len(path) < P
+                                         for r in range(K) if path + (r,) not in inserted))
+        expect = []
+        while len(expect) < N - m and queue:
+            sl, r = queue.popleft()
+            path = slot_path[sl] + (r,)
+            slot_path[m + 1 + len(expect)] = path
+            if len(path) < P:
+                queue.extend((m + 1 + len(expect), rr) for rr in range(K))
+            expect.append(path)
+        assert got[m:] == expect

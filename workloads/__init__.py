@@ -6,4 +6,4 @@ tree building, no recurrence, no acceptance) and imports neither the oracle nor 
 HIP library, so both sides of every parity test can consume the same arrays.
 """
 from .configs import CONFIGS, Config  # noqa: F401
-from .generate import Workload, generate, resolve_target  # noqa: F401
+from .generate import MarkovHead, Workload, generate, markov_head, resolve_target  # noqa: F401

@@ -20,6 +20,13 @@ q, k, v, alpha and beta are then cast to the config dtype (bf16 by round-to-near
 through torch on the CPU, or fp32).  The cast tensors are what both the oracle (widened
 exactly to fp64) and the GPU consume.
 
+Markov-head inputs (``markov_head``, for the parent-conditioned lattices), from
+``numpy.random.SeedSequence([seed, 0x4D48])`` in three named child streams: base logits
+~ N(0, std 2) [B][P][K] sorted descending along K (rank 0 is the selector's top candidate),
+then W1 and W2 ~ N(0, std 1/sqrt(R)) [V][R] in fp32, so that <W1[x], W2[y]> has unit std.
+They pair with a workload's lattice tokens and root tokens; random matrices stand in for a
+trained head.
+
 The synthetic target argmax of tree slot i (the token the target model predicts after the
 node in slot i) is the lattice candidate of rank c_i at the node's child position when the
 slot's choice c_i is a rank and the node is above the last position, else the slot's
@@ -156,3 +163,23 @@ def resolve_target(depth: np.ndarray, n_nodes: np.ndarray, lat_tok: np.ndarray,
             if c < K and d < P:
                 out[b, i] = lat_tok[b, d, c]
     return out.astype(np.int32)
+
+
+@dataclass
+class MarkovHead:
+    bases: np.ndarray  # f32 [B][P][K], sorted descending along K
+    W1: np.ndarray     # f32 [V][R], previous-token embeddings
+    W2: np.ndarray     # f32 [V][R], candidate embeddings
+
+
+def markov_head(cfg: Config | str, seed: int = 0, R: int = 32, *, B: int | None = None) -> MarkovHead:
+    """Seeded stand-ins for a Markov head over the config's lattice shape (see the recipe)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    Bn = cfg.B if B is None else B
+    bases_s, w1_s, w2_s = (np.random.Generator(np.random.PCG64(c))
+                           for c in np.random.SeedSequence([seed, 0x4D48]).spawn(3))
+    bases = -np.sort(-bases_s.normal(0.0, 2.0, size=(Bn, cfg.P, cfg.K)), axis=-1).astype(np.float32)
+    W1 = w1_s.normal(0.0, 1.0 / np.sqrt(R), size=(cfg.V, R)).astype(np.float32)
+    W2 = w2_s.normal(0.0, 1.0 / np.sqrt(R), size=(cfg.V, R)).astype(np.float32)
+    return MarkovHead(bases, W1, W2)
