@@ -18,7 +18,7 @@ __global__ __launch_bounds__(64) void accept_kernel(CommitParams p) {
 }
 
 template <int D, bool BF16IN, int PATH>
-__global__ __launch_bounds__(256) void commit_kernel(CommitParams p) {
+__global__ __launch_bounds__(256, kCommitWavesPerEU) void commit_kernel(CommitParams p) {
   __shared__ CommitSmem<D> sm;
   commit_unit<D, BF16IN, PATH>(p, blockIdx.x, threadIdx.x, sm);
 }

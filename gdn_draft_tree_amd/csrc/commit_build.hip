@@ -15,7 +15,7 @@ namespace gdntree {
 namespace {
 
 template <int D, bool BF16IN>
-__global__ __launch_bounds__(256) void commit_build_kernel(CommitParams p, BuildParams bp, int nb) {
+__global__ __launch_bounds__(256, kCommitWavesPerEU) void commit_build_kernel(CommitParams p, BuildParams bp, int nb) {
   __shared__ CommitSmem<D> sm;
   __shared__ float s_logp[kMaxP * kMaxK];
   __shared__ int s_ltok[kMaxP * kMaxK];
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void commit_build_kernel(CommitParams p, Build
 // each request's next build starts once its own acceptance is known.  The commit workgroups
 // walk their request's tree themselves.
 template <int D, bool BF16IN>
-__global__ __launch_bounds__(256) void accept_commit_build_kernel(CommitParams p, BuildParams bp, int nb, int na) {
+__global__ __launch_bounds__(256, kCommitWavesPerEU) void accept_commit_build_kernel(CommitParams p, BuildParams bp, int nb, int na) {
   __shared__ CommitSmem<D> sm;
   __shared__ float s_logp[kMaxP * kMaxK];
   __shared__ int s_ltok[kMaxP * kMaxK];

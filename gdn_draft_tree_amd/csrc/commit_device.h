@@ -69,6 +69,11 @@ __device__ __forceinline__ void write_acceptance(const CommitParams &p, int b, i
   p.acc_tok[ab + t] = t < len - 1 ? s_tok[s_path[t + 1]] : (t == len - 1 ? bonus : -1);
 }
 
+// Register budget of the commit kernels: four waves per SIMD, so that four workgroups fit a
+// CU and a batch of 32 requests x 32 heads is resident at once (a few spilled registers cost
+// less than a second round of workgroups).
+constexpr int kCommitWavesPerEU = 4;
+
 template <int D>
 struct CommitSmem {
   float k[kMaxAnc][D];
