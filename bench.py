@@ -268,6 +268,58 @@ def tau_curve(name: str, seeds: int, budgets=(4, 8, 16, 24, 32, 48, 64)) -> None
                       "data": "synthetic lattices and targets (seeded); build and acceptance on the GPU"}))
 
 
+def markov_timing(name: str, seeds: int, launches: int, R: int = 32) -> None:
+    """The Markov-head path alone: parent-conditioned edge log-probs from the head
+    (gdntree_markov_edges) and the best-first build over them (gdntree_build_cond), each as
+    `launches` launches back to back over `seeds` seeded batches of the workload's shape, timed
+    with two events around each batch of launches (medians over five batches).  Prints one JSON
+    line."""
+    import numpy as np
+    import torch
+
+    import gdn_draft_tree_amd as g
+    from workloads import CONFIGS, generate, markov_head
+
+    cfg = CONFIGS[name]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sets = []
+    for s in range(seeds):
+        w, mh = generate(cfg, seed=s), markov_head(cfg, seed=s, R=R)
+        d = dict(bases=torch.from_numpy(mh.bases).to(dev), lat_tok=torch.from_numpy(w.lat_tok).to(dev),
+                 root_tok=torch.from_numpy(w.root_tok).to(dev), W1=torch.from_numpy(mh.W1).to(dev),
+                 W2=torch.from_numpy(mh.W2).to(dev))
+        d["edge"] = g.gdntree_markov_edges(d["bases"], d["lat_tok"], d["root_tok"], d["W1"], d["W2"])
+        d["tree"] = g.gdntree_build_cond(d["edge"], d["lat_tok"], d["root_tok"], cfg.N)
+        d["p_edges"] = g.gdntree_markov_edges(d["bases"], d["lat_tok"], d["root_tok"], d["W1"], d["W2"],
+                                              out=d["edge"], stream=stream, prepare=True)
+        d["p_build"] = g.gdntree_build_cond(d["edge"], d["lat_tok"], d["root_tok"], cfg.N, out=d["tree"],
+                                            stream=stream, prepare=True)
+        sets.append(d)
+    torch.cuda.synchronize()
+    n_nodes = torch.cat([d["tree"].n_nodes for d in sets]).cpu().numpy()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for what in ("p_edges", "p_build"):
+        for i in range(2 * seeds):  # warm
+            sets[i % seeds][what]()
+        med = []
+        for _ in range(5):
+            e0.record(stream)
+            for i in range(launches):
+                sets[i % seeds][what]()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            med.append(e0.elapsed_time(e1) * 1e3 / launches)
+        out[what] = float(np.median(med))
+    print(json.dumps({"metric": "Markov-head edge log-probs and the conditioned best-first build: us per launch",
+                      "workload": f"{cfg.name}: {cfg.notes}", "B": cfg.B, "P": cfg.P, "K": cfg.K, "N": cfg.N,
+                      "V": cfg.V, "R": R, "head_dtype": "f32", "seeds": seeds, "launches": launches,
+                      "markov_edges_us": out["p_edges"], "build_cond_us": out["p_build"],
+                      "mean_nodes": float(n_nodes.mean()),
+                      "data": "synthetic head (seeded bases, W1, W2) over the workload's lattice tokens"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +344,9 @@ def main():
                     help="verify (and commit) launches timed one by one for the medians (>= 100)")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the streaming probe that measures what this part streams for the verify's bytes")
+    ap.add_argument("--markov-only", type=int, default=0, metavar="K",
+                    help="instead of the step benchmark: time the Markov-head edge kernel and the "
+                         "conditioned build, K launches back to back each, then exit")
     ap.add_argument("--verify-only", type=int, default=0, metavar="K",
                     help="instead of the step benchmark: K verify launches back to back over the input "
                          "sets, then exit (a short, single-kernel program for profiler runs)")
@@ -304,6 +359,9 @@ def main():
 
     if args.tau_curve:
         tau_curve(args.workload, args.tau_seeds)
+        return
+    if args.markov_only:
+        markov_timing(args.workload, 4, args.markov_only)
         return
 
     cpu = None
