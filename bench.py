@@ -433,6 +433,16 @@ def main():
         d["p_commit"] = g.gdntree_commit(d["tree"], d["acc"][0], d["acc"][2], d["k"], d["v"], d["alpha"], d["beta"],
                                          d["state"], cfg.P, stream=stream, prepare=True)
         if cfg.G is None:
+            # the commit deferred into the next verify: acceptance + next build, then the
+            # acceptance + commit of this set's tree inside the verify of the next set's tree
+            # (committed into the next set's state: every set carries its own state, so the
+            # state buffers rotate with the rows; the work per step is that of a decode loop)
+            d["p_accept_build"] = g.gdntree_accept_build(d["tree"], d["target"], cfg.P, dn["lat_logp"], dn["lat_tok"],
+                                                         dn["root_tok"], cfg.N, dn["tree"], acc=d["acc"],
+                                                         stream=stream, prepare=True)
+            d["p_accept_commit_verify"] = g.gdntree_accept_commit_verify(
+                d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], cfg.P, dn["tree"], dn["q"], dn["k"],
+                dn["v"], dn["alpha"], dn["beta"], dn["state"], o=dn["o"], stream=stream, prepare=True)
             d["p_accept_commit_build"] = g.gdntree_accept_commit_build(
                 d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
                 dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, dn["tree"], acc=d["acc"], stream=stream,
@@ -477,9 +487,24 @@ def main():
             d["p_verify"]()
             (d["p_accept_commit_build"] if i + 1 < i0 + k else d["p_accept_commit"])()
 
+    # Deferred commit: build(i0) -> verify(i0) -> [accept(i), then per request build(i+1); one
+    # launch] -> [accept + commit of step i inside the verify of step i+1; one launch] -> ...;
+    # the last step's acceptance and commit on their own.  The same builds, verifies,
+    # acceptances and commits as run_pipelined, with the state read once per step.
+    def run_deferred(i0, k):
+        sets[i0 % nsets]["p_build"]()
+        sets[i0 % nsets]["p_verify"]()
+        for i in range(i0, i0 + k - 1):
+            d = sets[i % nsets]
+            d["p_accept_build"]()
+            d["p_accept_commit_verify"]()
+        sets[(i0 + k - 1) % nsets]["p_accept_commit"]()
+
     for i in range(args.warmup):
         step(i)
     run_pipelined(0, args.warmup)
+    if cfg.G is None:
+        run_deferred(0, args.warmup)
     torch.cuda.synchronize()
     if args.copy_calibration:
         calibration_kernels(dev)
@@ -496,6 +521,12 @@ def main():
         step(args.warmup + i)
     torch.cuda.synchronize()
     elapsed_seq = time.perf_counter() - t0
+    elapsed_def = None
+    if cfg.G is None:
+        t0 = time.perf_counter()
+        run_deferred(args.warmup, args.steps)
+        torch.cuda.synchronize()
+        elapsed_def = time.perf_counter() - t0
 
     # per-kernel durations with HIP events on the launch stream
     for i in range(args.steps):
@@ -601,6 +632,11 @@ def main():
                        "verify_back_to_back": t_verify},
         "sequential": {"ms_per_step": ms_seq, "value": nodes_per_step / (ms_seq * 1e-3),
                        "order": "build -> verify -> accept_commit, each step after the previous one"},
+        "deferred_commit": None if elapsed_def is None else {
+            "ms_per_step": elapsed_def / args.steps * 1e3,
+            "value": nodes_per_step / (elapsed_def / args.steps),
+            "order": ("build -> verify(i0) -> [accept(i), then per request build(i+1); one launch] -> "
+                      "[accept(i) + commit(i) + verify(i+1); one launch] -> ...; one stream")},
         "pipelining": ("build -> verify(i) -> [accept(i), then per request build(i+1); commit(i) beside "
                        "them; one launch] -> verify(i+1) ...; one stream") if cfg.G is None else
                       "build_shared -> verify(i) -> [accept(i), then per request build(i+1); commit(i) "

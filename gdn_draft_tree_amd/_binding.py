@@ -20,7 +20,8 @@ GDNTREE_OK, GDNTREE_ERR_ARG, GDNTREE_ERR_UNSUPPORTED, GDNTREE_ERR_DEVICE = 0, 1,
 GDNTREE_F32, GDNTREE_BF16 = 0, 1
 EXPORTED = ("gdntree_build", "gdntree_build_shared", "gdntree_verify", "gdntree_accept_commit", "gdntree_accept", "gdntree_commit",
             "gdntree_commit_build", "gdntree_accept_commit_build", "gdntree_accept_commit_build_shared",
-            "gdntree_build_cond", "gdntree_markov_edges", "gdntree_status_str")
+            "gdntree_build_cond", "gdntree_markov_edges", "gdntree_accept_build", "gdntree_accept_commit_verify",
+            "gdntree_status_str")
 
 
 class GdnTreeError(RuntimeError):
@@ -66,6 +67,11 @@ def _load() -> ctypes.CDLL:
     lib.gdntree_accept_commit_build_shared.argtypes = [CTree, i, i, i, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp,
                                                        vp, vp, vp, vp, vp, vp, i, i, i, i, i, CTree, vp]
     lib.gdntree_accept_commit_build_shared.restype = i
+    lib.gdntree_accept_build.argtypes = [CTree, i, i, i, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, CTree, vp]
+    lib.gdntree_accept_build.restype = i
+    lib.gdntree_accept_commit_verify.argtypes = [CTree, i, i, vp, vp, vp, vp, vp, vp, vp, vp, CTree, i, i, i, i, i,
+                                                 i, i, vp, vp, vp, vp, vp, vp, i, vp, vp]
+    lib.gdntree_accept_commit_verify.restype = i
     lib.gdntree_status_str.argtypes = [i]
     lib.gdntree_status_str.restype = ctypes.c_char_p
     return lib
@@ -391,6 +397,60 @@ def gdntree_accept_commit_build(tree: Tree, target_argmax, k, v, alpha, beta, st
                 prepare, (acc_len, acc_tok, acc_node),
                 (tree, target_argmax, k, v, alpha, beta, state, acc_len, acc_tok, acc_node, next_lat_logp,
                  next_lat_tok, next_root_tok, next_out))
+
+
+def gdntree_accept_build(tree: Tree, target_argmax, P: int, next_lat_logp, next_lat_tok, next_root_tok,
+                         next_N: int, next_out: Tree, acc=None, stream=None, prepare: bool = False):
+    """gdntree_accept of this step and gdntree_build of the next step's tree into `next_out`, in
+    one launch (no state touched).  Returns (acc_len, acc_tok, acc_node)."""
+    B, R = tree.B, tree.N + 1
+    acc_len, acc_tok, acc_node = _acc_buffers(B, P, target_argmax.device, acc)
+    tp = _dev(target_argmax, "target_argmax", torch.int32, (B, R))
+    ap = (_dev(acc_len, "acc_len", torch.int32, (B,)),
+          _dev(acc_tok, "acc_tok", torch.int32, (B, P + 1)),
+          _dev(acc_node, "acc_node", torch.int32, (B, P + 1)))
+    nxt = _next_lattice(next_lat_logp, next_lat_tok, next_root_tok, next_N, next_out)
+    return _run(LIB.gdntree_accept_build, (tree.c(), B, R - 1, P, tp, *ap, *nxt, _stream(stream)),
+                prepare, (acc_len, acc_tok, acc_node),
+                (tree, target_argmax, acc_len, acc_tok, acc_node, next_lat_logp, next_lat_tok, next_root_tok,
+                 next_out))
+
+
+def gdntree_accept_commit_verify(prev_tree: Tree, prev_target_argmax, prev_k, prev_v, prev_alpha, prev_beta,
+                                 prev_P: int, tree: Tree, q, k, v, alpha, beta, state, o=None, acc=None,
+                                 out_dtype=None, stream=None, prepare: bool = False):
+    """The previous step's acceptance and commit deferred into this step's verify, one launch:
+    state <- the previous accepted node's state (in place), then o = the verify of `tree` on
+    it.  `acc`: optional (acc_len, acc_tok, acc_node) buffers for the previous step's
+    acceptance.  Returns o."""
+    L, B, R, H, D = q.shape
+    dt = q.dtype
+    Rp = prev_tree.N + 1
+    out_dtype = out_dtype or dt
+    if o is None:
+        o = torch.empty(L, B, R, H, D, dtype=out_dtype, device=q.device)
+    if prev_tree.B != B:
+        raise ValueError("previous tree has the wrong batch size")
+    pp = [_dev(prev_target_argmax, "prev_target_argmax", torch.int32, (B, Rp))]
+    pp += [_dev(x, nm, dt, (L, B, Rp, H, D)) for x, nm in ((prev_k, "prev_k"), (prev_v, "prev_v"))]
+    pp += [_dev(x, nm, dt, (L, B, Rp, H)) for x, nm in ((prev_alpha, "prev_alpha"), (prev_beta, "prev_beta"))]
+    if acc is None:
+        ap = (None, None, None)
+    else:
+        ap = (_dev(acc[0], "acc_len", torch.int32, (B,)),
+              _dev(acc[1], "acc_tok", torch.int32, (B, prev_P + 1)),
+              _dev(acc[2], "acc_node", torch.int32, (B, prev_P + 1)))
+    ptrs = [_dev(x, nm, dt, (L, B, R, H, D)) for x, nm in ((q, "q"), (k, "k"), (v, "v"))]
+    ptrs += [_dev(x, nm, dt, (L, B, R, H)) for x, nm in ((alpha, "alpha"), (beta, "beta"))]
+    sp = _dev(state, "state", torch.float32, (L, B, H, D, D))
+    op = _dev(o, "o", out_dtype, (L, B, R, H, D))
+    if tree.B != B or tree.N != R - 1:
+        raise ValueError("tree shape does not match the rows")
+    return _run(LIB.gdntree_accept_commit_verify,
+                (prev_tree.c(), Rp - 1, prev_P, *pp, *ap, tree.c(), B, R - 1, L, H, D, D, _code(dt), *ptrs, sp,
+                 _code(out_dtype), op, _stream(stream)), prepare, o,
+                (prev_tree, prev_target_argmax, prev_k, prev_v, prev_alpha, prev_beta, acc, tree, q, k, v, alpha,
+                 beta, state, o))
 
 
 def gdntree_accept_commit_build_shared(tree: Tree, target_argmax, k, v, alpha, beta, state, P: int,

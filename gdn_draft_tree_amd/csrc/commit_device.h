@@ -27,25 +27,37 @@
 
 namespace gdntree {
 
-// The acceptance walk of request b by one wave: s_path[0..len) = the accepted slots from
-// the root, s_tok = the tokens of the used slots, *s_len = tau (0 for a node count outside
-// [1, R]), *s_bonus = the target's argmax at the last accepted node.  Lane 0 writes them.
-__device__ __forceinline__ void accept_walk(const CommitParams &p, int b, int lane, int *s_path,
-                                            int *s_tok, int *s_len, int *s_bonus) {
-  const int n = p.n_nodes[b];
-  const bool n_ok = n >= 1 && n <= p.R;
-  const size_t tb = (size_t)b * p.R;
-  int par0 = -1, tok0 = 0, tgt0 = 0, par1 = -1, tok1 = 0, tgt1 = 0;
-  if (n_ok && lane < n) { par0 = p.parent[tb + lane]; tok0 = p.token[tb + lane]; tgt0 = p.target[tb + lane]; }
-  if (n_ok && lane + 64 < n) { par1 = p.parent[tb + lane + 64]; tok1 = p.token[tb + lane + 64]; tgt1 = p.target[tb + lane + 64]; }
-  if (n_ok && lane < n) s_tok[lane] = tok0;
-  if (n_ok && lane + 64 < n) s_tok[lane + 64] = tok1;
+// What one wave holds of a request's tree for the acceptance walk: lane l has slots l and
+// l + 64 (parent, token, target argmax), loaded for every slot below R.
+struct WalkRegs {
+  int n, par0, tok0, tgt0, par1, tok1, tgt1;
+};
+
+__device__ __forceinline__ WalkRegs walk_load(const int32_t *parent, const int32_t *token, const int32_t *target,
+                                              const int32_t *n_nodes, int R, int b, int lane) {
+  WalkRegs w{n_nodes[b], -1, 0, 0, -1, 0, 0};
+  const size_t tb = (size_t)b * R;
+  if (lane < R) { w.par0 = parent[tb + lane]; w.tok0 = token[tb + lane]; w.tgt0 = target[tb + lane]; }
+  if (lane + 64 < R) { w.par1 = parent[tb + lane + 64]; w.tok1 = token[tb + lane + 64]; w.tgt1 = target[tb + lane + 64]; }
+  return w;
+}
+
+// The acceptance walk of one request by one wave, from the values walk_load fetched:
+// s_path[0..len) = the accepted slots from the root, s_tok = the tokens of the used slots,
+// *s_len = tau (0 for a node count outside [1, R]), *s_bonus = the target's argmax at the last
+// accepted node.  Lane 0 writes the scalars and the path.
+__device__ __forceinline__ void walk_run(const WalkRegs &w, int R, int P, int lane, int *s_path, int *s_tok,
+                                         int *s_len, int *s_bonus) {
+  const int n = w.n;
+  const bool n_ok = n >= 1 && n <= R;
+  if (n_ok && lane < n) s_tok[lane] = w.tok0;
+  if (n_ok && lane + 64 < n) s_tok[lane + 64] = w.tok1;
   int u = 0, len = 1;
   if (lane == 0) s_path[0] = 0;
-  while (n_ok && len <= p.P) {
-    const int tu = (u < 64) ? __builtin_amdgcn_readlane(tgt0, u) : __builtin_amdgcn_readlane(tgt1, u - 64);
-    const unsigned long long m0 = __ballot(lane >= 1 && lane < n && par0 == u && tok0 == tu);
-    const unsigned long long m1 = __ballot(lane + 64 < n && par1 == u && tok1 == tu);
+  while (n_ok && len <= P) {
+    const int tu = (u < 64) ? __builtin_amdgcn_readlane(w.tgt0, u) : __builtin_amdgcn_readlane(w.tgt1, u - 64);
+    const unsigned long long m0 = __ballot(lane >= 1 && lane < n && w.par0 == u && w.tok0 == tu);
+    const unsigned long long m1 = __ballot(lane + 64 < n && w.par1 == u && w.tok1 == tu);
     int cnode;
     if (m0) cnode = __ffsll((long long)m0) - 1;
     else if (m1) cnode = 64 + __ffsll((long long)m1) - 1;
@@ -56,8 +68,15 @@ __device__ __forceinline__ void accept_walk(const CommitParams &p, int b, int la
   }
   if (lane == 0) {
     *s_len = n_ok ? len : 0;
-    *s_bonus = (u < 64) ? __builtin_amdgcn_readlane(tgt0, u) : __builtin_amdgcn_readlane(tgt1, u - 64);
+    *s_bonus = (u < 64) ? __builtin_amdgcn_readlane(w.tgt0, u) : __builtin_amdgcn_readlane(w.tgt1, u - 64);
   }
+}
+
+// The acceptance walk of request b by one wave (walk_load, then walk_run).
+__device__ __forceinline__ void accept_walk(const CommitParams &p, int b, int lane, int *s_path,
+                                            int *s_tok, int *s_len, int *s_bonus) {
+  const WalkRegs w = walk_load(p.parent, p.token, p.target, p.n_nodes, p.R, b, lane);
+  walk_run(w, p.R, p.P, lane, s_path, s_tok, s_len, s_bonus);
 }
 
 // Lanes t = 0..P write request b's acceptance result.

@@ -296,6 +296,75 @@ GDNTREE_EXPORT gdntree_status gdntree_accept_commit_build_shared(
                                   next_positions, next_B, next_P, next_K, next_N, next_G, next_tree, stream);
 }
 
+GDNTREE_EXPORT gdntree_status gdntree_accept_build(gdntree_tree tree, int B, int N, int P,
+                                                   const int32_t *target_argmax, int32_t *acc_len,
+                                                   int32_t *acc_tok, int32_t *acc_node,
+                                                   const float *next_lat_logp, const int32_t *next_lat_tok,
+                                                   const int32_t *next_root_tok, int next_B, int next_P,
+                                                   int next_K, int next_N, gdntree_tree next_tree,
+                                                   hipStream_t stream) {
+  if (!tree.parent || !tree.token || !tree.n_nodes || !target_argmax || !acc_len || !acc_tok || !acc_node)
+    return GDNTREE_ERR_ARG;
+  if (!next_lat_logp || !next_lat_tok || !next_root_tok || !next_tree.parent || !next_tree.depth ||
+      !next_tree.rank || !next_tree.token || !next_tree.score || !next_tree.anc || !next_tree.n_nodes)
+    return GDNTREE_ERR_ARG;
+  // the acceptance reads the current tree while the build writes the next one
+  if (next_tree.parent == tree.parent || next_tree.n_nodes == tree.n_nodes || next_tree.token == tree.token)
+    return GDNTREE_ERR_ARG;
+  if (B <= 0 || N <= 0 || P <= 0 || next_B <= 0 || next_P <= 0 || next_K <= 0 || next_N <= 0)
+    return GDNTREE_ERR_ARG;
+  if (N > kMaxN || P > kMaxP || next_P > kMaxP || next_K > kMaxK || next_N > kMaxN ||
+      !grid_fits(next_B > B ? next_B : B))
+    return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  CommitParams p{};  // no commit workgroups (L = 0)
+  p.parent = tree.parent; p.token = tree.token; p.n_nodes = tree.n_nodes; p.target = target_argmax;
+  p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
+  p.B = B; p.R = N + 1; p.P = P; p.L = 0; p.H = 1; p.D = 128; p.in_bf16 = 1;
+  const BuildParams bp{next_lat_logp, next_lat_tok, next_root_tok, next_P, next_K, next_N, next_tree, nullptr};
+  if (launch_accept_commit_build(p, bp, next_B, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
+GDNTREE_EXPORT gdntree_status gdntree_accept_commit_verify(
+    gdntree_tree prev_tree, int prev_N, int prev_P, const int32_t *prev_target_argmax,
+    const void *prev_k, const void *prev_v, const void *prev_alpha, const void *prev_beta,
+    int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node, gdntree_tree tree, int B, int N, int L,
+    int H, int dk, int dv, gdntree_dtype in_dtype, const void *q, const void *k, const void *v,
+    const void *alpha, const void *beta, float *state, gdntree_dtype out_dtype, void *o,
+    hipStream_t stream) {
+  if (!prev_tree.parent || !prev_tree.token || !prev_tree.n_nodes || !prev_target_argmax || !prev_k ||
+      !prev_v || !prev_alpha || !prev_beta)
+    return GDNTREE_ERR_ARG;
+  if (!tree.parent || !tree.anc || !tree.n_nodes || !q || !k || !v || !alpha || !beta || !state || !o)
+    return GDNTREE_ERR_ARG;
+  const int nacc = (acc_len != nullptr) + (acc_tok != nullptr) + (acc_node != nullptr);
+  if (nacc != 0 && nacc != 3) return GDNTREE_ERR_ARG;  // all three acceptance outputs, or none
+  if (B <= 0 || N <= 0 || L <= 0 || H <= 0 || prev_N <= 0 || prev_P <= 0) return GDNTREE_ERR_ARG;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return GDNTREE_ERR_ARG;
+  if (gdntree_status st = head_dims(dk, dv); st != GDNTREE_OK) return st;
+  if (N > kMaxN || prev_N > kMaxN || prev_P > kMaxP || !grid_fits((long long)L * B * H))
+    return GDNTREE_ERR_UNSUPPORTED;
+  if (gdntree_status st = device_ok(); st != GDNTREE_OK) return st;
+  VerifyParams p;
+  p.parent = tree.parent;
+  p.anc = reinterpret_cast<const unsigned long long *>(tree.anc);
+  p.n_nodes = tree.n_nodes;
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha; p.beta = beta;
+  p.state = state;
+  p.o = o;
+  p.B = B; p.R = N + 1; p.L = L; p.H = H; p.D = dk;
+  p.in_bf16 = in_dtype == GDNTREE_BF16;
+  p.out_bf16 = out_dtype == GDNTREE_BF16;
+  p.pv_parent = prev_tree.parent; p.pv_token = prev_tree.token; p.pv_n_nodes = prev_tree.n_nodes;
+  p.pv_target = prev_target_argmax;
+  p.pv_k = prev_k; p.pv_v = prev_v; p.pv_alpha = prev_alpha; p.pv_beta = prev_beta;
+  p.acc_len = acc_len; p.acc_tok = acc_tok; p.acc_node = acc_node;
+  p.pv_R = prev_N + 1; p.pv_P = prev_P;
+  if (launch_verify(p, stream) != hipSuccess) return GDNTREE_ERR_DEVICE;
+  return GDNTREE_OK;
+}
+
 GDNTREE_EXPORT const char *gdntree_status_str(gdntree_status status) {
   switch (status) {
     case GDNTREE_OK: return "ok";

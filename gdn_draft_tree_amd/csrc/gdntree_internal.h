@@ -58,6 +58,14 @@ struct VerifyParams {
   void *o;
   int B, R, L, H, D;   // R = N + 1 slots
   int in_bf16, out_bf16;
+  // The previous step's acceptance and commit, done by the same launch before the verify
+  // (pv_parent == nullptr: none).  The previous tree, its target argmax and its rows (same
+  // layer, request, head and dtype layout, pv_R = previous N + 1 slots); the state is then
+  // written in place through `state`.  acc_*: the acceptance, written when non-null.
+  const int32_t *pv_parent = nullptr, *pv_token = nullptr, *pv_n_nodes = nullptr, *pv_target = nullptr;
+  const void *pv_k = nullptr, *pv_v = nullptr, *pv_alpha = nullptr, *pv_beta = nullptr;
+  int32_t *acc_len = nullptr, *acc_tok = nullptr, *acc_node = nullptr;
+  int pv_R = 0, pv_P = 0;
 };
 hipError_t launch_verify(const VerifyParams &p, hipStream_t stream);
 

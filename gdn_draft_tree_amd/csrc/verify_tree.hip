@@ -54,6 +54,7 @@
 
 #include <type_traits>
 
+#include "commit_device.h"
 #include "gdntree_internal.h"
 
 namespace gdntree {
@@ -86,9 +87,10 @@ struct VerifyGeom {
   static constexpr int NTH = 64 * WAVES;
 };
 
-template <int D, bool BF16IN, int NT, bool X65>
+template <int D, bool BF16IN, int NT, bool X65, bool CM>
 struct VerifySmem {
   typedef VerifyGeom<D, BF16IN, NT, X65> G;
+  typedef typename G::T T;
   // q rows | k rows; once they are dead, the dense W1 rows as three bf16 parts (when they fit):
   // W1[t][s] for t < PR, s < SPD, zero off t's ancestors-or-self.  Within a 32-slot block,
   // slot 16 h + 4 g + i sits at 8 g + 4 h + i, so that one lane's operand fragment is one
@@ -106,12 +108,19 @@ struct VerifySmem {
   float cwl[kMaxAnc][64];                  // W1 weights b_{anc e} g_t / g_{anc e}, per depth and lane
   int bad;
   int sync;                                // tree-wave phase counter
+  // The previous step's commit: its accepted path's k rows (rows 0..16) and v rows (rows
+  // 17..33), the path's slots, the previous tree's tokens, tau, the bonus token, and a counter
+  // of the product waves whose path rows have landed.
+  alignas(16) unsigned char cpath[CM ? 2 * kMaxAnc * D * (int)sizeof(T) : 16];
+  int cslot[kMaxAnc];
+  int ctok[CM ? kMaxSlots : 1];
+  int ctau, cbonus, csync;
 };
 
-template <int D, bool BF16IN, int NT, bool X65>
+template <int D, bool BF16IN, int NT, bool X65, bool CM>
 struct VerifyShape {
   typedef VerifyGeom<D, BF16IN, NT, X65> G;
-  static constexpr int LDS = (int)sizeof(VerifySmem<D, BF16IN, NT, X65>);
+  static constexpr int LDS = (int)sizeof(VerifySmem<D, BF16IN, NT, X65, CM>);
   static_assert(LDS <= kLdsBytes, "a workgroup's LDS fits a CU");
   static constexpr int WG_PER_CU = kLdsBytes / LDS < 2 ? 1 : 2;
   // A workgroup's waves are dealt over the CU's four SIMDs, so the register budget must let
@@ -245,11 +254,11 @@ __device__ __forceinline__ void tree_sync(int *cnt, int *bad, int target, int la
   }
 }
 
-template <int D, bool BF16IN, int NT, bool X65>
-__global__ __launch_bounds__((VerifyGeom<D, BF16IN, NT, X65>::NTH), (VerifyShape<D, BF16IN, NT, X65>::WPEU))
+template <int D, bool BF16IN, int NT, bool X65, bool CM>
+__global__ __launch_bounds__((VerifyGeom<D, BF16IN, NT, X65>::NTH), (VerifyShape<D, BF16IN, NT, X65, CM>::WPEU))
 void verify_kernel(VerifyParams p) {
   typedef VerifyGeom<D, BF16IN, NT, X65> G;
-  typedef VerifySmem<D, BF16IN, NT, X65> SM;
+  typedef VerifySmem<D, BF16IN, NT, X65, CM> SM;
   typedef typename G::T T;
   constexpr int RM = G::RM, ROWB = G::ROWB, NTH = G::NTH;
   constexpr int CH = 16 / (int)sizeof(T), CPR = D / CH;
@@ -366,7 +375,7 @@ void verify_kernel(VerifyParams p) {
       }
     }
     wg_barrier();  // (0)
-    if (!valid) {
+    if (!CM && !valid) {  // (with a commit, the commit is done first)
       __builtin_amdgcn_s_waitcnt(0);  // loads into this workgroup's LDS land before it ends
       return;
     }
@@ -374,8 +383,10 @@ void verify_kernel(VerifyParams p) {
     // State fragments in the [d_k][d_v] layout: lane (g, c) gathers S0[32 ks + 8 g + e][j],
     // 16 consecutive channels (64 bytes) per row and instruction.  The fragment of the next
     // k-step is in flight while the current one is split and multiplied (register budget of
-    // two resident workgroups per CU).
+    // two resident workgroups per CU).  With a commit first, the wave holds all its fragments
+    // (the previous committed state), updates them and then multiplies them as they are.
     constexpr int KW = 1;
+    constexpr int KG = CM ? KS : KW;  // fragments gathered before barrier (1)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(p.state) + (size_t)u * D * D, 0, D * D * 4, 0x00020000);
     const int voff = (8 * g4 * D + j) * 4;
@@ -386,12 +397,114 @@ void verify_kernel(VerifyParams p) {
         raw[ks][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, voff, (32 * ks + e) * D * 4, 0));
     };
 #pragma unroll
-    for (int ks = 0; ks < KW; ++ks) gather(ks);
-    // vmcnt(8 KW): this wave's row loads have landed (loads complete in order; the state loads
+    for (int ks = 0; ks < KG; ++ks) gather(ks);
+    // vmcnt(8 KG): this wave's row loads have landed (loads complete in order; the state loads
     // just issued may still be in flight)
-    static_assert(8 * KW < 16, "the wait count fits");
-    __builtin_amdgcn_s_waitcnt((8 * KW) | (7 << 4) | (15 << 8));
-    wg_barrier();  // (1) the q, k, v rows and the per-node data are in LDS
+    static_assert(8 * KG < 64, "the wait count fits");
+    __builtin_amdgcn_s_waitcnt(((8 * KG) & 15) | ((8 * KG) >> 4 << 14) | (7 << 4) | (15 << 8));
+    wg_barrier();  // (1) the q, k, v rows and the per-node data are in LDS (and the accepted path)
+
+    if constexpr (CM) {
+      // ---- the previous step's commit along its accepted path (tau rows, root first): for
+      // each row, S <- a (S - b k (k . S)) + b k v^T = a S + k (b (v - a k . S))^T, in fp32, on
+      // this wave's fragments; the path's k and v rows are fetched into LDS by the product
+      // waves together, the gates into registers (lane x: path row x) ----------------------
+      const int tau = __builtin_amdgcn_readfirstlane(s.ctau);
+      if (tau > 0) {
+        constexpr int RB = D * (int)sizeof(T), CPRW = RB / 16;
+        constexpr int PROUNDS = (kMaxAnc * CPRW + 64 * NPW - 1) / (64 * NPW);
+        const size_t pvoff = ((size_t)lb * p.pv_R * p.H + h) * D;
+        const int pnb = (int)(((p.pv_R - 1) * rstride + D) * sizeof(T));
+        const __amdgpu_buffer_rsrc_t pk = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const T *>(p.pv_k) + pvoff), 0, pnb, 0x00020000);
+        const __amdgpu_buffer_rsrc_t pv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const T *>(p.pv_v) + pvoff), 0, pnb, 0x00020000);
+#pragma unroll
+        for (int x = 0; x < PROUNDS; ++x) {
+          const int c = 64 * (wave + NPW * x) + lane;  // 16-byte chunk c of the path's rows
+          if (c < tau * CPRW) {
+            const int r = c / CPRW, cc = c - r * CPRW;
+            const unsigned off = (unsigned)((s.cslot[r] * (int)rstride + cc * CH) * (int)sizeof(T));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(pk, (lds_void_t *)(s.cpath + 1024 * (wave + NPW * x)), 16, off,
+                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                pv, (lds_void_t *)(s.cpath + kMaxAnc * RB + 1024 * (wave + NPW * x)), 16, off, 0, 0, 0);
+          }
+        }
+        float pa = 0.f, pb = 0.f;
+        if (lane < tau) {
+          const size_t gi = ((size_t)lb * p.pv_R + s.cslot[lane]) * p.H + h;
+          pa = load_elem(static_cast<const T *>(p.pv_alpha), gi);
+          pb = load_elem(static_cast<const T *>(p.pv_beta), gi);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // the state fragments, path rows and gates have landed
+        if (lane == 0) __hip_atomic_fetch_add(&s.csync, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        int spins = 0;
+        bool met = true;
+        while (__hip_atomic_load(&s.csync, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < NPW) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > (1 << 22)) {
+            met = false;
+            break;
+          }
+        }
+        if (!met) {
+          s.bad = 1;  // the state stays as it was; the outputs of this unit are NaN
+        } else {
+          const unsigned char *kb = s.cpath;
+          const T *vb = reinterpret_cast<const T *>(s.cpath + kMaxAnc * RB);
+          auto kfrag = [&](int r, int ks, float (&kv)[8]) {
+            if constexpr (BF16IN) {
+              const uint4 x = *reinterpret_cast<const uint4 *>(kb + r * RB + (32 * ks + 8 * g4) * 2);
+              const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                kv[2 * i] = __uint_as_float(w[i] << 16);
+                kv[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+              }
+            } else {
+              const float4 x0 = *reinterpret_cast<const float4 *>(kb + r * RB + (32 * ks + 8 * g4) * 4);
+              const float4 x1 = *reinterpret_cast<const float4 *>(kb + r * RB + (32 * ks + 8 * g4 + 4) * 4);
+              kv[0] = x0.x; kv[1] = x0.y; kv[2] = x0.z; kv[3] = x0.w;
+              kv[4] = x1.x; kv[5] = x1.y; kv[6] = x1.z; kv[7] = x1.w;
+            }
+          };
+          for (int r = 0; r < tau; ++r) {
+            const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pa), r));
+            const float bb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pb), r));
+            float dot4[4] = {0.f, 0.f, 0.f, 0.f};  // k . S over this lane's key rows, one sum per k-step
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+              float kv[8];
+              kfrag(r, ks, kv);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) dot4[ks & 3] = fmaf(kv[e], raw[ks][e], dot4[ks & 3]);
+            }
+            float dot = (dot4[0] + dot4[1]) + (dot4[2] + dot4[3]);
+            dot += __shfl_xor(dot, 16);  // the four lanes of channel j hold its 4 x 32 key rows
+            dot += __shfl_xor(dot, 32);
+            const float coef = bb * (to_f32(vb[r * D + j]) - a * dot);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {  // k read again rather than held across the exchange
+              float kv[8];
+              kfrag(r, ks, kv);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) raw[ks][e] = fmaf(kv[e], coef, a * raw[ks][e]);
+            }
+          }
+          // the committed state, in place
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(raw[ks][e]), rs, voff, (32 * ks + e) * D * 4, 0);
+        }
+      }
+      if (!valid) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+      }
+    }
 
     // The rest of a product wave's work, as straight-line code for each count of row tiles in
     // use (a runtime loop bound over the tiles would keep every accumulator live everywhere).
@@ -421,7 +534,7 @@ void verify_kernel(VerifyParams p) {
         bf16x8 sh, sm, sl;
         split3(raw[ks], sh, sm, sl);
         asm volatile("" : "+v"(sh), "+v"(sm), "+v"(sl)::"memory");
-        if (ks + KW < KS) gather(ks + KW);
+        if (!CM && ks + KW < KS) gather(ks + KW);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mt = 0; mt < NTU; ++mt) {
@@ -581,11 +694,14 @@ void verify_kernel(VerifyParams p) {
   unsigned long long w_mask = 0ull, my_mask = 0ull;
   int w_par = 0;
   uint32_t w_a0 = 0u, w_b0 = 0u, w_a1 = 0u, w_b1 = 0u;  // gate bits
+  WalkRegs wr{};  // the previous tree, for the acceptance walk before a commit
   if (tw == 0) {
     if (lane == 0) {
       s.sync = 0;
       s.bad = 0;
+      if constexpr (CM) s.csync = 0;
     }
+    if constexpr (CM) wr = walk_load(p.pv_parent, p.pv_token, p.pv_target, p.pv_n_nodes, p.pv_R, b, lane);
     w_mask = p.anc[tb + tn];
     w_par = p.parent[tb + tn];
     my_mask = p.anc[tb + ts];
@@ -615,7 +731,28 @@ void verify_kernel(VerifyParams p) {
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the counter and the clears are written
   __builtin_amdgcn_sched_barrier(0);
   wg_barrier();  // (0) the product waves may queue their state loads
+  // Before a commit, tree wave 0 walks the previous step's acceptance: the accepted slots and
+  // tau for the product waves (and, when asked, the acceptance itself, by the layer-0, head-0
+  // workgroup of each request).
+  auto cm_walk = [&]() {
+    asm volatile("" : "+v"(wr.par0), "+v"(wr.tok0), "+v"(wr.tgt0), "+v"(wr.par1), "+v"(wr.tok1), "+v"(wr.tgt1));
+    walk_run(wr, p.pv_R, p.pv_P, lane, s.cslot, s.ctok, &s.ctau, &s.cbonus);
+    if (p.acc_len && h == 0 && lb < p.B) {
+      const int len = s.ctau;
+      if (len > 0 && lane <= p.pv_P) {
+        const size_t ab = (size_t)b * (p.pv_P + 1);
+        if (lane == 0) p.acc_len[b] = len;
+        p.acc_node[ab + lane] = lane < len ? s.cslot[lane] : -1;
+        p.acc_tok[ab + lane] = lane < len - 1 ? s.ctok[s.cslot[lane + 1]] : (lane == len - 1 ? s.cbonus : -1);
+      }
+    }
+  };
   if (!valid) {
+    if constexpr (CM) {  // no verify output, but the commit still happens
+      if (tw == 0) cm_walk();
+      __builtin_amdgcn_s_waitcnt(0);
+      wg_barrier();  // (1)
+    }
     __builtin_amdgcn_s_waitcnt(0);  // the per-node loads complete before the wave ends
     return;
   }
@@ -678,6 +815,9 @@ void verify_kernel(VerifyParams p) {
       s.gamma[0] = alp[0];
       s.beta[0] = bet[0];
     }
+  }
+  if constexpr (CM) {
+    if (tw == 0) cm_walk();
   }
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) lgkmcnt(0): rows landed, prologue written
   wg_barrier();   // (1) rows, masks, gates and cleared regions are in LDS
@@ -833,8 +973,12 @@ void verify_kernel(VerifyParams p) {
 template <int D, bool BF16IN, int NT, bool X65>
 hipError_t launch_one(const VerifyParams &p, hipStream_t stream) {
   const unsigned units = (unsigned)(p.L * p.B * p.H);
-  hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, X65>), dim3(units), dim3(VerifyGeom<D, BF16IN, NT, X65>::NTH),
-                     0, stream, p);
+  if (p.pv_parent)
+    hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, X65, true>), dim3(units),
+                       dim3(VerifyGeom<D, BF16IN, NT, X65>::NTH), 0, stream, p);
+  else
+    hipLaunchKernelGGL((verify_kernel<D, BF16IN, NT, X65, false>), dim3(units),
+                       dim3(VerifyGeom<D, BF16IN, NT, X65>::NTH), 0, stream, p);
   return hipGetLastError();
 }
 

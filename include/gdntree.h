@@ -11,7 +11,9 @@
  * gdntree_accept_commit_build_shared fuses that build into the end of the previous step.
  * gdntree_accept_commit also comes as two calls, gdntree_accept then gdntree_commit, and
  * gdntree_commit_build / gdntree_accept_commit_build run a commit (with or without the
- * acceptance) together with the next step's tree build in one launch.  For a drafter whose
+ * acceptance) together with the next step's tree build in one launch.  Alternatively the
+ * commit is deferred into the next step's verify: gdntree_accept_build (acceptance + next
+ * build), then gdntree_accept_commit_verify (acceptance + commit + verify of the next tree).  For a drafter whose
  * candidate scores depend on the previous token (a Markov head), gdntree_markov_edges forms
  * the parent-conditioned edge log-probs and gdntree_build_cond builds the tree over them.
  *
@@ -323,6 +325,61 @@ gdntree_status gdntree_accept_commit_build_shared(
     const float *next_lat_logp, const int32_t *next_lat_tok, const int32_t *next_root_tok,
     const int32_t *next_positions, int next_B, int next_P, int next_K, int next_N, int next_G,
     gdntree_tree next_tree, hipStream_t stream);
+
+/*
+ * gdntree_accept_build - gdntree_accept for this step and gdntree_build for the next step's
+ * lattices in ONE launch: request b's next tree is built by the workgroup that has just
+ * walked request b's acceptance, and no state is touched.  It pairs with
+ * gdntree_accept_commit_verify, which commits this step's states inside the next step's
+ * verify.  Results are exactly those of gdntree_accept followed by gdntree_build.
+ *
+ *   tree ... acc_node      as for gdntree_accept (this step)
+ *   next_lat_logp ... next_N, next_tree   as for gdntree_build (the next step)
+ * next_tree must not share memory with tree; equal parent, token or n_nodes pointers give
+ * ERR_ARG.  Every check of the two calls applies; on any error nothing is enqueued.
+ */
+gdntree_status gdntree_accept_build(gdntree_tree tree, int B, int N, int P,
+                                    const int32_t *target_argmax, int32_t *acc_len, int32_t *acc_tok,
+                                    int32_t *acc_node, const float *next_lat_logp,
+                                    const int32_t *next_lat_tok, const int32_t *next_root_tok,
+                                    int next_B, int next_P, int next_K, int next_N,
+                                    gdntree_tree next_tree, hipStream_t stream);
+
+/*
+ * gdntree_accept_commit_verify - the previous step's acceptance and commit, deferred into
+ * this step's verify: ONE launch in which every (layer, request, head) workgroup first walks
+ * its request's acceptance of the previous tree (as gdntree_accept), recomputes the accepted
+ * node's state from the committed state along the accepted path (as gdntree_commit: fp32,
+ * the gated delta rule row by row) and writes it in place, then verifies this step's tree
+ * on that state (as gdntree_verify).  The state is read once and written once per step,
+ * instead of read by the commit, written, and read again by the next verify (SpecPilot
+ * summary, Technical novelty: states recomputed along root paths, not snapshotted).
+ * Results are those of gdntree_accept_commit on the previous step followed by
+ * gdntree_verify on this one (the state to fp32 rounding of a different summation order).
+ *
+ *   prev_tree, prev_N, prev_P       the previous step's tree, its node budget and positions
+ *   prev_target_argmax i32 [B][prev_N+1]   the target's argmax after each previous slot
+ *   prev_k, prev_v     in_dtype [L][B][prev_N+1][H][d]   the previous step's rows
+ *   prev_alpha, prev_beta  in_dtype [L][B][prev_N+1][H]
+ *   acc_len, acc_tok, acc_node   the previous step's acceptance, as gdntree_accept writes
+ *                    it ([B], [B][prev_P+1], [B][prev_P+1]); all three NULL to skip, else
+ *                    all three non-NULL (a mix gives ERR_ARG)
+ *   tree ... o       as for gdntree_verify (this step); state is read, committed in place,
+ *                    and the verify runs on the committed state
+ * A request whose previous n_nodes lies outside [1, prev_N+1] keeps its state (and gets no
+ * acceptance output); a request whose current tree is malformed gets the NaN / no-output
+ * treatment of gdntree_verify, and its state is still committed.  The previous step's
+ * arrays are only read; the acceptance outputs must not overlap any input.  Reads
+ * prev_tree.parent, prev_tree.token, prev_tree.n_nodes, tree.parent, tree.anc and
+ * tree.n_nodes.  Limits: those of gdntree_verify, and prev_N <= 64, prev_P <= 16.
+ */
+gdntree_status gdntree_accept_commit_verify(
+    gdntree_tree prev_tree, int prev_N, int prev_P, const int32_t *prev_target_argmax,
+    const void *prev_k, const void *prev_v, const void *prev_alpha, const void *prev_beta,
+    int32_t *acc_len, int32_t *acc_tok, int32_t *acc_node, gdntree_tree tree, int B, int N, int L,
+    int H, int dk, int dv, gdntree_dtype in_dtype, const void *q, const void *k, const void *v,
+    const void *alpha, const void *beta, float *state, gdntree_dtype out_dtype, void *o,
+    hipStream_t stream);
 
 /* Human-readable name of a status code ("unknown status" for other values). */
 const char *gdntree_status_str(gdntree_status status);

@@ -23,8 +23,9 @@ def _declared():
 
 
 def test_header_declares_the_boundary():
-    assert _declared() == ["gdntree_accept", "gdntree_accept_commit", "gdntree_accept_commit_build",
-                           "gdntree_accept_commit_build_shared", "gdntree_build", "gdntree_build_cond",
+    assert _declared() == ["gdntree_accept", "gdntree_accept_build", "gdntree_accept_commit",
+                           "gdntree_accept_commit_build", "gdntree_accept_commit_build_shared",
+                           "gdntree_accept_commit_verify", "gdntree_build", "gdntree_build_cond",
                            "gdntree_build_shared", "gdntree_commit", "gdntree_commit_build",
                            "gdntree_markov_edges", "gdntree_status_str", "gdntree_verify"]
 
@@ -126,6 +127,65 @@ def test_markov_edges_rejects(case, expect):
     if case == "Vbig": args["V"] = 1 << 25  # V * R * 4 bytes past 2^31
     st = g.LIB.gdntree_markov_edges(args["bases"], args["tok"], args["root"], args["W1"], args["W2"], args["dt"],
                                     args["B"], args["P"], args["K"], args["V"], args["R"], args["out"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_target", 1), ("null_acc", 1), ("null_next_tree_field", 1), ("same_tree", 1), ("B0", 1),
+    ("next_K0", 1), ("N65", 2), ("P17", 2), ("next_P17", 2), ("next_K65", 2), ("next_N65", 2),
+])
+def test_accept_build_rejects(case, expect):
+    g = _lib()
+    tree, nxt = _tree(g), g.CTree(**{f: 0x2000 for f, _ in g.CTree._fields_})
+    a = dict(tree=tree, B=2, N=24, P=8, tgt=FAKE, acc=(FAKE, FAKE, FAKE), lp=FAKE, lt=FAKE, rt=FAKE, nB=2, nP=8,
+             nK=16, nN=24, nxt=nxt)
+    if case == "null_target": a["tgt"] = None
+    if case == "null_acc": a["acc"] = (FAKE, None, FAKE)
+    if case == "null_next_tree_field": a["nxt"] = g.CTree(**{**{f: 0x2000 for f, _ in g.CTree._fields_}, "rank": None})
+    if case == "same_tree": a["nxt"] = tree
+    if case == "B0": a["B"] = 0
+    if case == "next_K0": a["nK"] = 0
+    if case == "N65": a["N"] = 65
+    if case == "P17": a["P"] = 17
+    if case == "next_P17": a["nP"] = 17
+    if case == "next_K65": a["nK"] = 65
+    if case == "next_N65": a["nN"] = 65
+    st = g.LIB.gdntree_accept_build(a["tree"], a["B"], a["N"], a["P"], a["tgt"], *a["acc"], a["lp"], a["lt"], a["rt"],
+                                    a["nB"], a["nP"], a["nK"], a["nN"], a["nxt"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_prev_token", 1), ("null_prev_target", 1), ("null_prev_k", 1), ("null_q", 1), ("null_state", 1),
+    ("acc_mixed", 1), ("prevN0", 1), ("prevP0", 1), ("H0", 1), ("in_dtype", 1), ("out_dtype", 1), ("dk0", 1),
+    ("dk96", 2), ("dk_ne_dv", 2), ("N65", 2), ("prevN65", 2), ("prevP17", 2),
+])
+def test_accept_commit_verify_rejects(case, expect):
+    g = _lib()
+    a = dict(prev=_tree(g), pN=24, pP=8, ptgt=FAKE, pk=FAKE, pv=FAKE, pa=FAKE, pb=FAKE, acc=(None, None, None),
+             tree=_tree(g), B=2, N=24, L=1, H=4, dk=128, dv=128, dt=g.GDNTREE_BF16, q=FAKE, k=FAKE, v=FAKE,
+             al=FAKE, be=FAKE, st=FAKE, odt=g.GDNTREE_BF16, o=FAKE)
+    if case == "null_prev_token": a["prev"] = _tree(g, token=1)
+    if case == "null_prev_target": a["ptgt"] = None
+    if case == "null_prev_k": a["pk"] = None
+    if case == "null_q": a["q"] = None
+    if case == "null_state": a["st"] = None
+    if case == "acc_mixed": a["acc"] = (FAKE, FAKE, None)
+    if case == "prevN0": a["pN"] = 0
+    if case == "prevP0": a["pP"] = 0
+    if case == "H0": a["H"] = 0
+    if case == "in_dtype": a["dt"] = 5
+    if case == "out_dtype": a["odt"] = 5
+    if case == "dk0": a["dk"] = 0
+    if case == "dk96": a["dk"] = a["dv"] = 96
+    if case == "dk_ne_dv": a["dv"] = 64
+    if case == "N65": a["N"] = 65
+    if case == "prevN65": a["pN"] = 65
+    if case == "prevP17": a["pP"] = 17
+    st = g.LIB.gdntree_accept_commit_verify(a["prev"], a["pN"], a["pP"], a["ptgt"], a["pk"], a["pv"], a["pa"], a["pb"],
+                                            *a["acc"], a["tree"], a["B"], a["N"], a["L"], a["H"], a["dk"], a["dv"],
+                                            a["dt"], a["q"], a["k"], a["v"], a["al"], a["be"], a["st"], a["odt"],
+                                            a["o"], None)
     assert st == expect
 
 
