@@ -344,6 +344,10 @@ def main():
                     help="verify (and commit) launches timed one by one for the medians (>= 100)")
     ap.add_argument("--no-stream-ceiling", action="store_true",
                     help="skip the streaming probe that measures what this part streams for the verify's bytes")
+    ap.add_argument("--deferred-only", type=int, default=0, metavar="K",
+                    help="instead of the step benchmark: K launches of the verify with the previous "
+                         "step's commit deferred into it (gdntree_accept_commit_verify), back to back over "
+                         "the input sets, then exit (a short program for profiler runs)")
     ap.add_argument("--markov-only", type=int, default=0, metavar="K",
                     help="instead of the step benchmark: time the Markov-head edge kernel and the "
                          "conditioned build, K launches back to back each, then exit")
@@ -452,6 +456,17 @@ def main():
                 d["tree"], d["target"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], cfg.P,
                 dn["lat_logp"], dn["lat_tok"], dn["root_tok"], cfg.N, cfg.G, dn["tree"],
                 next_positions=dn["positions"], acc=d["acc"], stream=stream, prepare=True)
+
+    if args.deferred_only:
+        if cfg.G is not None:
+            sys.exit("--deferred-only runs without a shared budget")
+        for i in range(args.deferred_only):
+            sets[i % nsets]["p_accept_commit_verify"]()
+        torch.cuda.synchronize()
+        if args.copy_calibration:
+            calibration_kernels(dev)
+        print(json.dumps({"deferred_only": args.deferred_only, "workload": args.workload, "sets": nsets}))
+        return
 
     if args.verify_only:
         for i in range(args.verify_only):

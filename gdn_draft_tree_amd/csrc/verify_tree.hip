@@ -382,10 +382,11 @@ void verify_kernel(VerifyParams p) {
     const int j = 16 * wave + l16;  // this lane's value channel (K pass and the 65th row)
     // State fragments in the [d_k][d_v] layout: lane (g, c) gathers S0[32 ks + 8 g + e][j],
     // 16 consecutive channels (64 bytes) per row and instruction.  The fragment of the next
-    // k-step is in flight while the current one is split and multiplied (register budget of
-    // two resident workgroups per CU).  With a commit first, the wave holds all its fragments
-    // (the previous committed state), updates them and then multiplies them as they are.
-    constexpr int KW = 1;
+    // k-step (two with at most three row tiles, where the registers allow it) is in flight while
+    // the current one is split and multiplied (register budget of two resident workgroups per
+    // CU).  With a commit first, the wave holds all its fragments (the previous committed
+    // state), updates them, writes them back and multiplies them as they are.
+    constexpr int KW = NT <= 3 ? 2 : 1;
     constexpr int KG = CM ? KS : KW;  // fragments gathered before barrier (1)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(p.state) + (size_t)u * D * D, 0, D * D * 4, 0x00020000);
@@ -504,6 +505,8 @@ void verify_kernel(VerifyParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         return;
       }
+      // the products below take the committed state from these registers (streaming it back
+      // from the caches instead measured slower: part of it had left L2 and was read again)
     }
 
     // The rest of a product wave's work, as straight-line code for each count of row tiles in
