@@ -178,36 +178,42 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
     rk = __builtin_amdgcn_readlane(k, l);
   };
 
-  // Lane l holds node l (its slot) and the one frontier candidate it offers (`has`): its
-  // lowest unexpanded child rank `next`, that child's score `cand`, and, fetched ahead, the
-  // log-prob `nlp` of the rank after it, so no LDS read sits between two pops.  Whether a
-  // lane offers a candidate is a flag of its own: a candidate's score may be -inf (a log-prob
-  // of -inf, or a finite fp64 sum that rounds to -inf in fp32) and is still a candidate.
+  // Lane l holds node l (its slot) and the one frontier candidate it offers: its lowest
+  // unexpanded child rank `next`, that child's score `cand`, and, fetched ahead, the log-prob
+  // `nlp` of the rank after it, so no LDS read sits between two pops.  Which lanes offer a
+  // candidate is a wave mask of its own (`offer`): a candidate's score may be -inf (a log-prob
+  // of -inf, or a finite fp64 sum that rounds to -inf in fp32) and is still a candidate.  `key`
+  // is the candidate's score rounded to fp32 (-inf for a lane that offers none).  The pops are
+  // branch-free: every lane evaluates both updates and keeps the one for its role.
   const double kNone = -__builtin_inf();
+  const float kNoneF = -__builtin_inff();
   int my_parent = -1, my_depth = 0, my_rank = -1, my_next = 0;
   double my_score = 0.0, cand = kNone;
-  bool has = false;
+  float key = kNoneF;
+  unsigned long long offer = 0ull;  // uniform: lanes that offer a candidate
   // conditioned: the rank of the child on offer and, fetched ahead with `nlp`, of the next one;
   // `byrank`: the node's children are offered in rank order (its score is -inf)
   int my_crank = 0, ncr = 0;
   bool byrank = false;
   const float *s_raw = s_logp + (COND ? bp.P * K * K : 0);  // conditioned: the unsorted rows follow
-  unsigned long long my_anc = 0ull;
   // LDS index of the fetched-ahead log-prob; every lane reloads its entry after each pop
   // (one unconditional read, so the value lands straight in its register)
   int nlp_at = 0;
   if (lane == 0) {  // the root (P >= 1 and K >= 1); no children when the request has no positions
-    has = Pb > 0;
     cand = 0.0 + (double)s_logp[0];  // row 0 for the conditioned rows too: position 0, the root
+    key = (float)cand;
     nlp_at = min(1, K - 1);
     if constexpr (COND) my_crank = s_perm[0];
   }
+  if (Pb > 0) offer = 1ull;
   float nlp = s_logp[nlp_at];
   if constexpr (COND) ncr = s_perm[nlp_at];
+  // next, depth and (conditioned) the offered rank of every lane, packed for one lane read
+  auto pack = [&]() { return my_next | (my_depth << 8) | (my_crank << 16); };
+  int my_pk = pack();
   // The 65th slot (index 64) has no lane; it is the last insertion and is kept uniformly.
   int x_parent = -1, x_depth = 0, x_rank = -1;
   double x_score = 0.0;
-  unsigned long long x_anc = 0ull;
 
   int n = 1;
   while (n <= N) {
@@ -216,24 +222,23 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
     // lanes whose rounded score equals the fp32 maximum; when that lane is unique it is the
     // winner, otherwise the exact fp64 maximum is taken over those lanes (ties to the lowest
     // lane, which holds the smallest parent slot).
-    if (__ballot(has) == 0ull) break;                             // the trie is exhausted
-    const float c32 = (float)cand;
-    const float m32 = wave_max_f32(has ? c32 : -__builtin_inff());
-    const bool top = has && c32 == m32;
-    unsigned long long hit = __ballot(top);
+    const float m32 = wave_max_f32(key);
+    unsigned long long hit = offer & __builtin_amdgcn_fcmpf(key, m32, 1 /* ordered equal */);
+    if (hit == 0ull) break;  // the trie is exhausted
     double m;
     if (__popcll(hit) == 1) {
       m = __longlong_as_double(readlane_u64((unsigned long long)__double_as_longlong(cand), __ffsll((long long)hit) - 1));
     } else {
+      const bool top = (hit >> lane) & 1ull;
       m = wave_max_f64(top ? cand : kNone);
-      hit = __ballot(top && cand == m);
+      hit &= __builtin_amdgcn_fcmp(cand, m, 1 /* ordered equal; -inf equals -inf */);
     }
     const int p = __ffsll((long long)hit) - 1;                    // smallest parent slot
-    const int nx = __builtin_amdgcn_readlane(my_next, p);         // index in p's child order
-    const int r = COND ? __builtin_amdgcn_readlane(my_crank, p) : nx;  // the child's rank
-    const int dp = __builtin_amdgcn_readlane(my_depth, p);
+    const int pk = __builtin_amdgcn_readlane(my_pk, p);
+    const int nx = pk & 0xff;                                     // index in p's child order
+    const int dp = (pk >> 8) & 0xff;
+    const int r = COND ? (pk >> 16) : nx;                         // the child's rank
     const int d = dp + 1;
-    const unsigned long long a = readlane_u64(my_anc, p) | (1ull << (n - 1));
     // the new node's row of children and its first child
     const int row_n = COND ? min(d, P - 1) * K + r : min(d, P - 1);
     float first;
@@ -249,31 +254,35 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
       first = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lp_first), min(d, P - 1)));
     }
 
-    // (fetched-ahead entries are clamped, always valid: one standing past the last rank or
-    // position is never used)
-    if (lane == p) {  // offer p's next child
-      my_next = nx + 1;
-      has = nx + 1 < K;
-      cand = my_score + nlpd;
-      const int row_p = COND ? (dp == 0 ? 0 : dp * K + my_rank) : dp;
-      nlp_at = row_p * K + min(nx + 2, K - 1);
-      if constexpr (COND) my_crank = byrank ? nx + 1 : ncr;
-    }
+    // p offers its next child; the new node n (a lane below 64) offers its first child.
+    // (Fetched-ahead entries are clamped, always valid: one standing past the last rank or
+    // position is never used.)
+    const bool is_p = lane == p, is_n = lane == n;
+    const bool p_more = nx + 1 < K, n_more = d < Pb;
+    const double cand_p = my_score + nlpd;          // lane p's own score and log-prob
+    const double cand_n = m + (double)first;
+    const int row_p = COND ? (dp == 0 ? 0 : dp * K + my_rank) : dp;
+    const int at_p = row_p * K + min(nx + 2, K - 1), at_n = row_n * K + min(1, K - 1);
     if (n < 64) {
-      if (lane == n) {
-        my_parent = p; my_depth = d; my_rank = r; my_score = m; my_anc = a;
-        my_next = 0;
-        has = d < Pb;
-        cand = m + (double)first;
-        nlp_at = row_n * K + min(1, K - 1);
-        if constexpr (COND) {
-          my_crank = first_rk;
-          byrank = m == kNone;
-        }
-      }
+      my_parent = is_n ? p : my_parent;
+      my_depth = is_n ? d : my_depth;
+      my_rank = is_n ? r : my_rank;
+      my_score = is_n ? m : my_score;
     } else {
-      x_parent = p; x_depth = d; x_rank = r; x_score = m; x_anc = a;
+      x_parent = p; x_depth = d; x_rank = r; x_score = m;
     }
+    const bool up_n = is_n && n < 64;
+    cand = is_p ? cand_p : (up_n ? cand_n : cand);
+    key = is_p ? (p_more ? (float)cand_p : kNoneF) : (up_n ? (n_more ? (float)cand_n : kNoneF) : key);
+    my_next = is_p ? nx + 1 : (up_n ? 0 : my_next);
+    nlp_at = is_p ? at_p : (up_n ? at_n : nlp_at);
+    if constexpr (COND) {
+      my_crank = is_p ? (byrank ? nx + 1 : ncr) : (up_n ? first_rk : my_crank);
+      byrank = up_n ? (m == kNone) : byrank;
+    }
+    offer = p_more ? offer : (offer & ~(1ull << p));
+    if (n < 64 && n_more) offer |= 1ull << n;
+    my_pk = pack();
     if constexpr (COND) {
       nlp = byrank ? s_raw[nlp_at] : s_logp[nlp_at];
       ncr = s_perm[nlp_at];
@@ -282,6 +291,19 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
     }
     ++n;
   }
+
+  // Ancestor masks after the build, by pointer jumping over the parent links: bit t-1 of node
+  // t, then each round ORs in the mask of the node 2^i links up (depth <= 16: five rounds).
+  unsigned long long my_anc = (lane >= 1 && lane < n) ? (1ull << (lane - 1)) : 0ull;
+  int up = (lane >= 1 && lane < n) ? my_parent : 0;
+#pragma unroll
+  for (int it = 0; it < 5; ++it) {
+    const unsigned lo = (unsigned)__builtin_amdgcn_ds_bpermute(up << 2, (int)(unsigned)my_anc);
+    const unsigned hi = (unsigned)__builtin_amdgcn_ds_bpermute(up << 2, (int)(unsigned)(my_anc >> 32));
+    my_anc |= ((unsigned long long)hi << 32) | lo;
+    up = __builtin_amdgcn_ds_bpermute(up << 2, up);
+  }
+  const unsigned long long x_anc = n == 65 ? (readlane_u64(my_anc, x_parent) | (1ull << 63)) : 0ull;
 
   // tokens, after the build: the candidate of the node's rank at its lattice position
   const int *lt = s_ltok;
