@@ -46,6 +46,14 @@
 // Rows 0..63 go through 16-row MFMA tiles; a 65th row (a tree of 64 drafts) rides in one
 // extra tile of its own, and its W1 row is summed on VALU.
 //
+// With the previous step's commit first (CM), the same workgroup first recomputes the state of
+// the previous step's accepted node (same page, Prerequisites > speculative decoding and >
+// hybrid recurrent architecture: greedy acceptance, then the accepted path's state): tree wave
+// 0 walks the previous tree's acceptance, the product waves hold their whole state slice in
+// registers, fetch the accepted path's k and v rows into LDS, apply the path's rows in order
+// (S <- a S + k (b (v - a k . S))^T, fp32), write the slice back in place and go on to the
+// products with it.  The state is then read once and written once per step.
+//
 // MFMA operand registers are refilled only after the products that read them have completed:
 // every chain of products is fenced off from the code that refills its operands, and before a
 // wave overwrites registers that earlier products read, it reads each accumulator those
