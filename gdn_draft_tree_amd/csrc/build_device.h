@@ -118,19 +118,32 @@ __device__ __forceinline__ void stage_lattice_cond(const BuildParams &bp, int b,
   const int K = bp.K, PK = bp.P * bp.K, PKK = PK * bp.K;
   const float *e = bp.edge_logp + (size_t)b * PKK;
   const int32_t *lt = bp.lat_tok + (size_t)b * PK;
-  for (int x = t; x < PKK; x += nth) s_raw[x] = e[x];
+  if ((PKK & 3) == 0 && (reinterpret_cast<uintptr_t>(e) & 15) == 0) {  // whole 16-byte pieces
+    const float4 *e4 = reinterpret_cast<const float4 *>(e);
+    float4 *r4 = reinterpret_cast<float4 *>(s_raw);
+    for (int x = t; x < PKK / 4; x += nth) r4[x] = e4[x];
+  } else {
+    for (int x = t; x < PKK; x += nth) s_raw[x] = e[x];
+  }
   for (int x = t; x < PK; x += nth) s_ltok[x] = lt[x];
   __syncthreads();
-  for (int x = t; x < PKK; x += nth) {
-    const int row = x / K, i = x - row * K;
-    const float v = s_raw[x];
-    int pos = 0;
-    for (int j = 0; j < K; ++j) {
-      const float w = s_raw[row * K + j];
-      pos += (w > v || (w == v && j < i)) ? 1 : 0;
+  // one row per thread, held in registers: each entry's place is the number of entries of the
+  // row that come before it (larger, or equal with a smaller rank)
+  for (int row = t; row < PK; row += nth) {
+    float v[kCondMaxK];
+#pragma unroll
+    for (int i = 0; i < kCondMaxK; ++i) v[i] = i < K ? s_raw[row * K + i] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kCondMaxK; ++i) {
+      if (i < K) {
+        int pos = 0;
+#pragma unroll
+        for (int j = 0; j < kCondMaxK; ++j)
+          pos += (j < K && (v[j] > v[i] || (v[j] == v[i] && j < i))) ? 1 : 0;
+        s_logp[row * K + pos] = v[i];
+        s_perm[row * K + pos] = (uint8_t)i;
+      }
     }
-    s_logp[row * K + pos] = v;
-    s_perm[row * K + pos] = (uint8_t)i;
   }
   __syncthreads();
 }
@@ -284,7 +297,7 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
     if (n < 64 && n_more) offer |= 1ull << n;
     my_pk = pack();
     if constexpr (COND) {
-      nlp = byrank ? s_raw[nlp_at] : s_logp[nlp_at];
+      nlp = (byrank ? s_raw : s_logp)[nlp_at];
       ncr = s_perm[nlp_at];
     } else {
       nlp = s_logp[nlp_at];

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(64) void build_tree_kernel(BuildParams bp) {
 // wave builds.
 __global__ __launch_bounds__(256) void build_cond_kernel(BuildParams bp) {
   // the sorted rows, then the unsorted ones (P * K * K entries each, at the request's P and K)
-  __shared__ float s_rows[2 * kMaxP * kCondMaxK * kCondMaxK];
+  __shared__ alignas(16) float s_rows[2 * kMaxP * kCondMaxK * kCondMaxK];
   __shared__ uint8_t s_perm[kMaxP * kCondMaxK * kCondMaxK];
   __shared__ int s_ltok[kMaxP * kCondMaxK];
   float *s_logp = s_rows, *s_raw = s_rows + bp.P * bp.K * bp.K;
