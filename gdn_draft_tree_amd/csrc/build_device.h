@@ -183,12 +183,19 @@ __device__ __forceinline__ void build_request(const BuildParams &bp, int b, int 
     }
   }
   // the first child of row `row` (uniform): its log-prob and rank
+  // (all four registers are read and the pick is made on scalars: no branch on j)
   auto first_of = [&](int row, float &lp, int &rk) {
     const int j = row >> 6, l = row & 63;
-    const float v = j == 0 ? cf_lp[0] : j == 1 ? cf_lp[1] : j == 2 ? cf_lp[2] : cf_lp[3];
-    const int k = j == 0 ? cf_rk[0] : j == 1 ? cf_rk[1] : j == 2 ? cf_rk[2] : cf_rk[3];
-    lp = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-    rk = __builtin_amdgcn_readlane(k, l);
+    int v[4], k[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      v[x] = __builtin_amdgcn_readlane(__float_as_int(cf_lp[x]), l);
+      k[x] = __builtin_amdgcn_readlane(cf_rk[x], l);
+    }
+    const int v01 = j & 1 ? v[1] : v[0], v23 = j & 1 ? v[3] : v[2];
+    const int k01 = j & 1 ? k[1] : k[0], k23 = j & 1 ? k[3] : k[2];
+    lp = __int_as_float(j & 2 ? v23 : v01);
+    rk = j & 2 ? k23 : k01;
   };
 
   // Lane l holds node l (its slot) and the one frontier candidate it offers: its lowest
