@@ -574,6 +574,9 @@ void verify_kernel(VerifyParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      // From here to the stores this wave is on the launch's critical path (the tree waves are
+      // done with their chain): it takes precedence over them on its SIMD.
+      __builtin_amdgcn_s_setprio(2);
       // ---- o[t] = g_t A_q[t] + sum_s W1[t][s] U[s] on MFMA, U[s] = v[s] - g_s A_k[s] ---------
       // U takes A_k's place in this lane's registers (rows >= n zero) while the tree waves finish
       // the path solves (the gates and the v rows are in LDS since barrier (1)).
@@ -695,7 +698,7 @@ void verify_kernel(VerifyParams p) {
   }
 
   // ================================== tree waves =====================================
-  __builtin_amdgcn_s_setprio(3);
+  __builtin_amdgcn_s_setprio(3);  // the tree chain runs beside the state passes: it goes first
   const int tw = wave - NPW;  // 0: per-node tree work and the path solves; 1..3: clears
   const size_t tb = (size_t)b * p.R;
   // tw 0 issues the small per-node loads; tw 1..3 clear the compact Gram rows.
@@ -947,6 +950,7 @@ void verify_kernel(VerifyParams p) {
     if (lane == 0) s.cw[0] = s.beta[0] * z_root;  // the root: W1[0, 0] = b_0 (q_0 . k_0)
   }
   tree_sync(&s.sync, &s.bad, 2 * kTreeWaves, lane);  // the compact W1 rows are written
+  __builtin_amdgcn_s_setprio(1);  // the chain is done; the product waves' U and W1 U go first
   const int tt = tid - 64 * NPW;
   bf16x8 fh[PXN], fm[PXN], fl[PXN];
 #pragma unroll
