@@ -18,6 +18,15 @@
 // most 17 ballot steps over 65 slots), so that acceptance and commit are one launch, or the
 // workgroup takes the accepted path that the acceptance kernel (one wave per request) wrote
 // before.
+//
+// The tau rank-1 updates S_x = a_x S_{x-1} + k_x c_x^T, c_x = b_x (v_x - a_x S_{x-1}^T k_x), are
+// applied in the unrolled (WY) form: with G_x the product of the gates a_0..a_x and
+// R(x, y) = G_x / G_y the product of a_{y+1}..a_x,
+//     S_{x-1}^T k_x = G_{x-1} S_0^T k_x + sum_{y < x} R(x-1, y) (k_x . k_y) c_y,
+//     S_tau-1 = G_{tau-1} S_0 + sum_y R(tau-1, y) k_y c_y^T,
+// so the tau dot products with the committed state are independent (no step waits on the
+// previous one's update), the Gram entries k_x . k_y are shared by the workgroup, and only a
+// scalar recurrence over the c_x of each column is sequential.
 
 #pragma once
 
@@ -98,6 +107,7 @@ struct CommitSmem {
   float k[kMaxAnc][D];
   float v[kMaxAnc][D];
   float a[kMaxAnc], b[kMaxAnc];
+  float kk[kMaxAnc][kMaxAnc];  // Gram entries k_x . k_y of the path rows, y < x
   int path[kMaxAnc];
   int tok[kMaxSlots];
   int len, bonus, bad;
@@ -184,27 +194,79 @@ __device__ __forceinline__ void commit_unit(const CommitParams &p, int hh, int t
     s_b[x] = load_elem(gb, gi);
   }
   __syncthreads();
+  // the Gram entries of the path rows, y < x, by every thread (fp32, summed in order)
+  for (int e = tid; e < kMaxAnc * kMaxAnc; e += 256) {
+    const int x = e / kMaxAnc, y = e % kMaxAnc;
+    if (y < x && x < len) {
+      float g = 0.f;
+#pragma unroll 8
+      for (int i = 0; i < D; ++i) g = fmaf(s_k[x][i], s_k[y][i], g);
+      sm.kk[x][y] = g;
+    }
+  }
+  __syncthreads();
   if (!act) return;
 
-  for (int x = 0; x < len; ++x) {
-    float dot = 0.f;
+  // d_x = k_x . S_0[:, j] for every path row: this lane's half, then the other half
+  float d[kMaxAnc];
 #pragma unroll
-    for (int m = 0; m < EPL; m += 4) {
-      const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][i0 + m]);
-      dot += kk.x * st[m] + kk.y * st[m + 1] + kk.z * st[m + 2] + kk.w * st[m + 3];
+  for (int x = 0; x < kMaxAnc; ++x) {
+    d[x] = 0.f;
+    if (x < len) {
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < EPL; m += 4) {
+        const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][i0 + m]);
+        d4[0] = fmaf(kk.x, st[m], d4[0]);
+        d4[1] = fmaf(kk.y, st[m + 1], d4[1]);
+        d4[2] = fmaf(kk.z, st[m + 2], d4[2]);
+        d4[3] = fmaf(kk.w, st[m + 3], d4[3]);
+      }
+      d[x] = (d4[0] + d4[1]) + (d4[2] + d4[3]);
     }
-    dot += __shfl_xor(dot, 32);  // the other half of column j
-    // read k again below instead of keeping d/2 values of it in registers across the exchange
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    const float a = s_a[x];
-    const float coef = s_b[x] * (s_v[x][j] - a * dot);  // S <- a S + k (b (v - a k.S))
+  }
 #pragma unroll
-    for (int m = 0; m < EPL; m += 4) {
-      const float4 kk = *reinterpret_cast<const float4 *>(&s_k[x][i0 + m]);
-      st[m] = a * st[m] + kk.x * coef;
-      st[m + 1] = a * st[m + 1] + kk.y * coef;
-      st[m + 2] = a * st[m + 2] + kk.z * coef;
-      st[m + 3] = a * st[m + 3] + kk.w * coef;
+  for (int x = 0; x < kMaxAnc; ++x)
+    if (x < len) d[x] += __shfl_xor(d[x], 32);  // the other half of column j
+  // c_x, in path order; G = G_{x-1}
+  float c[kMaxAnc];
+  float G = 1.f;
+#pragma unroll
+  for (int x = 0; x < kMaxAnc; ++x) {
+    c[x] = 0.f;
+    if (x < len) {
+      float ks = G * d[x];  // S_{x-1}^T k_x, channel j
+      float r = 1.f;        // R(x-1, y), y from x-1 down
+#pragma unroll
+      for (int y = kMaxAnc - 1; y >= 0; --y) {
+        if (y < x) {
+          ks = fmaf(r * sm.kk[x][y], c[y], ks);
+          r *= s_a[y];
+        }
+      }
+      const float a = s_a[x];
+      c[x] = s_b[x] * (s_v[x][j] - a * ks);
+      G *= a;
+    }
+  }
+  // S_tau-1[:, j] = G_{tau-1} S_0[:, j] + sum_y R(tau-1, y) k_y c_y; the coefficients from the last
+  // row back, R(tau-1, tau-1) = 1
+  float r = 1.f;
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) st[m] *= G;
+#pragma unroll
+  for (int y = kMaxAnc - 1; y >= 0; --y) {
+    if (y < len) {
+      const float coef = r * c[y];
+#pragma unroll
+      for (int m = 0; m < EPL; m += 4) {
+        const float4 kk = *reinterpret_cast<const float4 *>(&s_k[y][i0 + m]);
+        st[m] = fmaf(kk.x, coef, st[m]);
+        st[m + 1] = fmaf(kk.y, coef, st[m + 1]);
+        st[m + 2] = fmaf(kk.z, coef, st[m + 2]);
+        st[m + 3] = fmaf(kk.w, coef, st[m + 3]);
+      }
+      r *= s_a[y];
     }
   }
   // Non-temporal stores: the committed state is next read by the following step's verify, long
