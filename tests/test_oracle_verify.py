@@ -240,6 +240,41 @@ def test_commit_equals_node_state():
     np.testing.assert_allclose(new, kept, rtol=1e-12, atol=1e-13)
 
 
+def _commit_unrolled(k, v, alpha, beta, h0):
+    """The accepted path's updates in unrolled form (the form the commit kernels evaluate):
+    with G_x the product of alpha_0..alpha_x and R(x, y) = alpha_{y+1} ... alpha_x,
+    S_{x-1}^T k_x = G_{x-1} h0^T k_x + sum_{y<x} R(x-1, y) (k_x . k_y) c_y,
+    c_x = beta_x (v_x - alpha_x S_{x-1}^T k_x), and the final state is
+    G h0 + sum_y R(tau-1, y) k_y c_y^T.  k, v: [tau][d]; alpha, beta: [tau]; h0: [dk][dv]."""
+    tau = len(alpha)
+    R = lambda x, y: float(np.prod(alpha[y + 1:x + 1]))  # empty product = 1
+    d = k @ h0                      # [tau][dv]: k_x . h0[:, j]
+    gram = k @ k.T
+    c = np.zeros_like(v)
+    G = 1.0
+    for x in range(tau):
+        ks = G * d[x] + sum(R(x - 1, y) * gram[x, y] * c[y] for y in range(x))
+        c[x] = beta[x] * (v[x] - alpha[x] * ks)
+        G *= alpha[x]
+    return G * h0 + sum(R(tau - 1, y) * np.outer(k[y], c[y]) for y in range(tau))
+
+
+@pytest.mark.parametrize("tau,d", [(1, 4), (2, 6), (5, 8), (17, 16)])
+def test_commit_unrolled_form(tau, d):
+    """The unrolled form equals the oracle's row-by-row commit along the same path, for unit
+    and for unnormalised keys (the identity does not need |k| = 1)."""
+    rng = np.random.default_rng(100 + tau)
+    for unit_k in (True, False):
+        n = tau
+        _, k, v, alpha, beta, h0 = _data(rng, n, 1, d, d, unit_k=unit_k)
+        acc_node = np.arange(tau)[None, :]
+        acc_len = np.array([tau])
+        ref = oracle.commit(acc_node, acc_len, k[None, None], v[None, None], alpha[None, None],
+                            beta[None, None], h0[None, None])[0, 0, 0]
+        got = _commit_unrolled(k[:, 0], v[:, 0], alpha[:, 0], beta[:, 0], h0[0])
+        np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
 def _stock_chain(rows_q, rows_k, rows_v, rows_a, rows_b, h0_head):
     """The stock sequential recurrence over a row sequence of one head, written out here on its
     own (expanded form: h <- a h - a b k (k^T h) + b k v^T, then o = h^T q), independent of the
