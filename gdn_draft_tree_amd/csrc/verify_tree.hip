@@ -317,11 +317,14 @@ void verify_kernel(VerifyParams p) {
     const uint32_t wb = (uint32_t)(aset >> (32 * mb));
     const int below = mb ? __popc((uint32_t)aset) : 0;
     float xv[8];
+    // (each entry read unconditionally, at a clamped index, then selected, so that the eight
+    // reads are in flight together rather than one conditional read and wait each)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int q = 16 * (e >> 2) + 4 * g + (e & 3);            // slot 32 mb + q
       const int d = below + __popc(wb & ((2u << q) - 1u)) - 1;  // its depth on t's path
-      xv[e] = ((wb >> q) & 1u) ? s.cw[t * kAR + imin(max(d, 0), kAR - 1)] : 0.f;
+      const float x = s.cw[imin(t, RM - 1) * kAR + imin(max(d, 0), kAR - 1)];
+      xv[e] = ((wb >> q) & 1u) ? x : 0.f;
     }
     split3(xv, xh, xm, xl);
   };
